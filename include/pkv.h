@@ -1,0 +1,252 @@
+/*
+ * pkv.h -- C ABI of libpkv: decode-phase attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources. Three web pages describe the method:
+ *   [SLS]  "Scaling LLM serving" (jayaprakash.net), sections "The KV cache",
+ *          "Managing the cache: PagedAttention", "Reuse shared prefixes".
+ *   [M23]  "Module 23: Serving" (Transformers & Math), section 23.1 "The Memory
+ *          Wall" (KV-size equation), 23.2 "Prefill and Decode", 23.4 "Paged
+ *          Attention", and the closing Exercises.
+ *   [DSS]  "Designing an LLM serving system" (clio.skatech.org), sections
+ *          "What it must do, and at what size", "The KV cache", "Continuous
+ *          batching" (scheduler flowchart) and "Paged attention".
+ *
+ * Everything here is plain C: pointers, sizes, status codes. No C++ or torch
+ * type crosses the boundary. Device pointers are HIP device addresses on the
+ * current device; `stream` is a hipStream_t passed as void* (NULL = the
+ * legacy default stream). All device entry points only enqueue work: they
+ * return after the launch, with no implicit synchronisation.
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout (one K pool and one V pool per layer; the block tables are
+ * one per sequence and shared by all layers)
+ *
+ *   PKV_BLOCK_TOKENS = 16 tokens per block ([M23] 23.4 gives "say 16 tokens").
+ *
+ *   k_pool  bf16  [num_blocks][n_kv_heads][16][head_dim]        (token-major)
+ *           element (blk, h, t, i) at  ((blk*n_kv_heads + h)*16 + t)*head_dim + i
+ *   v_pool  bf16  [num_blocks][n_kv_heads][head_dim][16]        (dim-major)
+ *           element (blk, h, t, i) at  ((blk*n_kv_heads + h)*head_dim + i)*16 + t
+ *
+ *   So one (block, head) tile of K and of V is 16*head_dim*2 bytes of
+ *   contiguous memory each (4 KiB at head_dim 128). V is stored dim-major so
+ *   that the 16 tokens of one head dimension are adjacent: that is the
+ *   operand order the matrix cores need for the probability-times-V product.
+ *   All offsets are computed in 64-bit arithmetic.
+ *
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entry (s, b) is the
+ *                 physical block holding positions 16b .. 16b+15 of sequence
+ *                 s ([M23] 23.4: a per-sequence table maps positions to
+ *                 blocks; [DSS] "Paged attention": the blocks need not be
+ *                 contiguous). Entries at b >= ceil(ctx_s/16) are ignored.
+ *   context_lens  int32 [num_seqs]; ctx_s counts every cached token of
+ *                 sequence s INCLUDING the one appended in this step, which
+ *                 sits at position ctx_s - 1. Valid range 1 .. max_context_len.
+ *
+ *   q      bf16  [num_seqs][n_q_heads][head_dim]
+ *   k_new  bf16  [num_seqs][n_kv_heads][head_dim]   (same for v_new)
+ *   out    fp32  [num_seqs][n_q_heads][head_dim]
+ *
+ *   Grouped-query attention ([SLS] "The KV cache": a few KV heads, each
+ *   shared by a group of query heads): G = n_q_heads / n_kv_heads, and query
+ *   head j reads KV head j / G (consecutive groups). G = 1 is multi-head
+ *   attention, n_kv_heads = 1 is multi-query attention.
+ *
+ * What the decode computes, for each sequence s and query head j with
+ * h = j / G (softmax attention of the one new query token over the whole
+ * cached context, [M23] 23.2: decode reads the whole KV cache for one token
+ * per sequence):
+ *
+ *   z_t       = scale * sum_i q[s,j,i] * K(bt[s][t/16], h, t%16, i),  0 <= t < ctx_s
+ *   out[s,j,:] = sum_t softmax(z)_t * V(bt[s][t/16], h, t%16, :)
+ *
+ * Arithmetic: bf16 inputs widened exactly to fp32; scores, the online
+ * softmax and the accumulation in fp32; output fp32.
+ *
+ * ---------------------------------------------------------------------------
+ * Errors
+ *
+ *   Every entry point returns PKV_OK (0) or a negative PKV_E* code. Host-side
+ *   checks happen before any launch; on an error nothing is enqueued.
+ *   Device-side checks (values that live in device memory: block ids,
+ *   context lengths) cannot return a status: the kernel ORs a PKV_DEVERR_*
+ *   bit into *err_flag (an int32 in device memory the caller zeroes; NULL
+ *   disables reporting), never reads or writes out of bounds, and writes NaN
+ *   to the outputs that depended on the bad value.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_TOKENS 16
+#define PKV_DEFAULT_PARTITION_TOKENS 0 /* pass 0 to let the library choose */
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* null pointer, negative size, inconsistent shape */
+  PKV_EUNSUPPORTED = -2,  /* head_dim not in {64, 128} */
+  PKV_ENOMEM = -3,        /* allocator: no free block */
+  PKV_EWORKSPACE = -4,    /* workspace smaller than pkv_decode_workspace_bytes */
+  PKV_EHIP = -5           /* the HIP runtime reported a launch error */
+};
+
+/* Device error bits, ORed into *err_flag by the kernels. */
+#define PKV_DEVERR_BLOCK_ID 1   /* a needed block-table entry outside [0, num_blocks) */
+#define PKV_DEVERR_CONTEXT 2    /* a context length outside [1, max_context_len] */
+#define PKV_DEVERR_COPY_PAIR 4  /* a copy_blocks id outside [0, num_blocks) */
+
+/* Static string for a status code; never NULL. */
+const char* pkv_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * KV-cache size closed form ([M23] 23.1, the KV-memory equation; [SLS] "The
+ * KV cache" gives the same product per token).
+ *   bytes per token = 2 * n_layers * n_kv_heads * head_dim * bytes_per_value
+ *   bytes           = bytes per token * context_len * batch
+ * Pure host arithmetic, exact in 64 bits. Returns 0 if any argument is < 0. */
+uint64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t bytes_per_value);
+uint64_t pkv_kv_cache_bytes(int32_t n_layers, int32_t n_kv_heads,
+                            int32_t head_dim, int64_t context_len,
+                            int64_t batch, int32_t bytes_per_value);
+/* Bytes of ONE pool (K or V) of one layer in the layout above:
+ * num_blocks * n_kv_heads * 16 * head_dim * 2. */
+uint64_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim);
+
+/* ------------------------------------------------------------------------
+ * kv_append: scatter this step's new key and value of every sequence into
+ * its pool slot ([M23] 23.4 and [DSS] "Paged attention": positions reach
+ * physical blocks through the per-sequence table; blocks are allocated as
+ * the sequence grows, so the caller has already made bt[s][(ctx_s-1)/16]
+ * valid and private, e.g. with pkv_seq_grow).
+ *
+ * For each s: p = ctx_s - 1, blk = bt[s][p/16], slot = p % 16, and for every
+ * KV head h and dimension i the 16-bit patterns k_new[s,h,i] / v_new[s,h,i]
+ * are stored at K/V element (blk, h, slot, i). Pure bit copy: bit-exact.
+ *
+ * k_pool, v_pool : device, bf16 pools of one layer, num_blocks blocks.
+ * k_new, v_new   : device, bf16 [num_seqs][n_kv_heads][head_dim].
+ * block_tables, context_lens : device int32, as above.
+ * Device errors: bt entry outside [0, num_blocks) or ctx_s outside
+ * [1, 16*max_blocks_per_seq] -> the sequence is skipped and the matching
+ * PKV_DEVERR bit set. num_seqs == 0 is a no-op. */
+int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
+                  const void* v_new, const int32_t* block_tables,
+                  const int32_t* context_lens, int32_t num_seqs,
+                  int32_t max_blocks_per_seq, int32_t num_blocks,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t* err_flag,
+                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attn_decode: the attention above, for every sequence and query head.
+ *
+ * The context of each sequence is cut into partitions of partition_tokens
+ * tokens (a multiple of 16; 0 = library default). One wavefront handles one
+ * (sequence, KV head, partition) and serves all G query heads of that KV
+ * head from the same K/V tiles, so each KV byte is read once. If more than
+ * one partition is needed (max_context_len > partition_tokens) a second
+ * kernel merges the partial (max, sum, accumulator) triples; the workspace
+ * holds them. Exactly ceil(max_context_len/partition_tokens) partitions are
+ * provisioned per (sequence, head).
+ *
+ * out        : device fp32 [num_seqs][n_q_heads][head_dim], written fully.
+ * q          : device bf16 [num_seqs][n_q_heads][head_dim].
+ * k_pool, v_pool, block_tables, context_lens : as above.
+ * n_q_heads % n_kv_heads must be 0. head_dim in {64, 128}.
+ * scale      : multiplies the q.k dot product (1/sqrt(head_dim) usually).
+ * max_context_len : host-side upper bound of every ctx_s, at most
+ *              16*max_blocks_per_seq; sizes the grid and the workspace.
+ * workspace  : device scratch of at least pkv_decode_workspace_bytes(...)
+ *              bytes (may be NULL when that is 0); caller-owned.
+ * Device errors: ctx_s outside [1, max_context_len], or a needed table
+ * entry outside [0, num_blocks): out[s,:,:] becomes NaN for that sequence
+ * and the PKV_DEVERR bit is set. num_seqs == 0 is a no-op. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
+                                  int32_t head_dim, int32_t max_context_len,
+                                  int32_t partition_tokens);
+int pkv_paged_attn_decode(float* out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, float scale,
+                          int32_t max_context_len, int32_t partition_tokens,
+                          void* workspace, size_t workspace_bytes,
+                          int32_t* err_flag, void* stream);
+/* The partition size the library uses when partition_tokens == 0. */
+int32_t pkv_default_partition_tokens(int32_t head_dim, int32_t max_context_len);
+
+/* ------------------------------------------------------------------------
+ * copy_blocks: copy-on-write support ([DSS] "Paged attention": when
+ * sequences that share blocks diverge, the shared block is copied on write).
+ * For each pair p: the whole K and V block src[p] (all heads, all 16 slots)
+ * is copied to block dst[p] of the given layer's pools. src/dst are device
+ * int32 arrays of n_pairs entries; the dst blocks must be distinct and must
+ * not be any src block. Device errors: an id outside [0, num_blocks) skips
+ * the pair and sets PKV_DEVERR_COPY_PAIR. */
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
+                    const int32_t* dst, int32_t n_pairs, int32_t num_blocks,
+                    int32_t n_kv_heads, int32_t head_dim, int32_t* err_flag,
+                    void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator with reference counts ([SLS] "Managing the cache":
+ * blocks allocated as the sequence grows, requests can share blocks; [DSS]
+ * "Paged attention": shared prefix blocks, copy on write at divergence;
+ * [DSS] "Continuous batching": a finished sequence releases its blocks;
+ * [DSS] "Autoscaling": cache occupancy is the capacity signal).
+ *
+ * Host memory only, no device calls, not thread-safe (one scheduler thread
+ * owns it). Free blocks form a LIFO stack: a freed block is the next one
+ * handed out; a new allocator hands out 0, 1, 2, ... in order. Block ids are
+ * otherwise opaque: results never depend on which ids are used.
+ *
+ * Tables passed to the seq functions are host int32 arrays of capacity
+ * max_blocks entries, n_blocks of which are in use. */
+typedef struct pkv_allocator pkv_allocator;
+
+int pkv_allocator_create(int32_t num_blocks, pkv_allocator** out); /* num_blocks >= 1 */
+void pkv_allocator_destroy(pkv_allocator* a);                      /* NULL ok */
+int pkv_block_alloc(pkv_allocator* a, int32_t* id); /* refcount 1; PKV_ENOMEM if none */
+int pkv_block_incref(pkv_allocator* a, int32_t id); /* EINVAL if id free/out of range */
+int pkv_block_decref(pkv_allocator* a, int32_t id); /* at 0 the block is freed */
+int32_t pkv_block_refcount(const pkv_allocator* a, int32_t id); /* -1 if out of range */
+int32_t pkv_num_free(const pkv_allocator* a);
+int32_t pkv_num_blocks(const pkv_allocator* a);
+
+/* Make the table ready for writing position new_context_len - 1:
+ *  1. allocate blocks until n_blocks >= ceil(new_context_len / 16), so a
+ *     sequence holds exactly the blocks its context needs and at most one
+ *     partly filled block ([M23] Exercises: the waste is at most one partly
+ *     filled block per request);
+ *  2. if the block holding position new_context_len - 1 has refcount > 1,
+ *     copy on write: allocate a fresh block, decref the shared one, put the
+ *     fresh one in the table and report the pair in (*cow_src, *cow_dst);
+ *     otherwise both are set to -1. The caller must then run
+ *     pkv_copy_blocks(src, dst) on every layer before the next kv_append.
+ * new_context_len in [1, 16*max_blocks]. On PKV_ENOMEM the blocks already
+ * added stay in the table (n_blocks says how many) and no copy-on-write was
+ * done; the state is consistent and the call can be retried after a
+ * release. */
+int pkv_seq_grow(pkv_allocator* a, int32_t* table, int32_t* n_blocks,
+                 int32_t max_blocks, int32_t new_context_len,
+                 int32_t* cow_src, int32_t* cow_dst);
+/* Share the first n_blocks entries of table with a new sequence: increfs
+ * each (the caller copies those entries into the new sequence's table).
+ * All-or-nothing: on an invalid id nothing is changed. */
+int pkv_seq_fork(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
+/* A finished sequence: decref each of its n_blocks blocks.
+ * All-or-nothing: on an invalid id nothing is changed. */
+int pkv_seq_release(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

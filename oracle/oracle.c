@@ -1,0 +1,207 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU model of paged decode
+ * attention. TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark call it; the product path never does.
+ * It shares no code, header or table with the GPU library: the layout and
+ * the arithmetic below are written out again from their definitions.
+ *
+ * Single-threaded. Floating point in double precision (the pages fix no
+ * precision for the attention itself, so the oracle computes the definition
+ * as exactly as a double allows). Built with -O2 -ffp-contract=off and no
+ * fast-math, so every operation is the one written here.
+ *
+ * Sources (page title, then section):
+ *   [SLS] "Scaling LLM serving" -- "The KV cache" (per-token size product,
+ *         grouped-query heads), "Managing the cache: PagedAttention".
+ *   [M23] "Module 23: Serving" -- 23.1 "The Memory Wall" (the KV-memory
+ *         equation), 23.2 "Prefill and Decode" (decode reads the whole KV
+ *         cache for one new token per sequence), 23.4 "Paged Attention"
+ *         (16-token blocks, per-sequence table from positions to blocks).
+ *   [DSS] "Designing an LLM serving system" -- "What it must do, and at what
+ *         size", "Paged attention" (indirection, non-contiguous blocks,
+ *         sharing, copy on write).
+ *
+ * Layout, restated from the library's documented contract:
+ *   block = 16 tokens; position p of sequence s lives in physical block
+ *   table[s][p / 16], slot p % 16.
+ *   K pool element (blk, h, t, i): ((blk * n_kv + h) * 16 + t) * d + i
+ *   V pool element (blk, h, t, i): ((blk * n_kv + h) * d + i) * 16 + t
+ *   Query head j uses KV head j / (n_q / n_kv).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BLOCK 16
+
+/* A bf16 value is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_value(uint16_t bits) {
+  uint32_t word = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &word, sizeof f);
+  return (double)f;
+}
+
+static size_t k_index(int64_t blk, int h, int t, int i, int n_kv, int d) {
+  return (size_t)((((int64_t)blk * n_kv + h) * ORACLE_BLOCK + t) * d + i);
+}
+
+static size_t v_index(int64_t blk, int h, int t, int i, int n_kv, int d) {
+  return (size_t)((((int64_t)blk * n_kv + h) * d + i) * ORACLE_BLOCK + t);
+}
+
+/* ------------------------------------------------------------------------
+ * KV-cache bytes ([M23] 23.1: 2 x layers x kv_heads x d_head x L x B x
+ * bytes). Exact in 64-bit integers. */
+uint64_t oracle_kv_bytes(int64_t n_layers, int64_t n_kv_heads, int64_t d_head,
+                         int64_t context_len, int64_t batch,
+                         int64_t bytes_per_value) {
+  return (uint64_t)2 * (uint64_t)n_layers * (uint64_t)n_kv_heads *
+         (uint64_t)d_head * (uint64_t)context_len * (uint64_t)batch *
+         (uint64_t)bytes_per_value;
+}
+
+/* ------------------------------------------------------------------------
+ * Append: the token at position ctx_s - 1 of each sequence goes to slot
+ * (table[s][(ctx_s - 1) / 16], (ctx_s - 1) % 16). Bit copy.
+ * Returns 0, or -1 (nothing written for that sequence) on an invalid
+ * context length or block id; the other sequences are still written. */
+int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
+                     const uint16_t* v_new, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs,
+                     int max_blocks_per_seq, int num_blocks, int n_kv, int d) {
+  int status = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    int ctx = context_lens[s];
+    if (ctx < 1 || ctx > ORACLE_BLOCK * max_blocks_per_seq) {
+      status = -1;
+      continue;
+    }
+    int pos = ctx - 1;
+    int32_t blk = block_tables[(size_t)s * max_blocks_per_seq + pos / ORACLE_BLOCK];
+    if (blk < 0 || blk >= num_blocks) {
+      status = -1;
+      continue;
+    }
+    int slot = pos % ORACLE_BLOCK;
+    for (int h = 0; h < n_kv; ++h) {
+      for (int i = 0; i < d; ++i) {
+        size_t src = ((size_t)s * n_kv + h) * d + i;
+        k_pool[k_index(blk, h, slot, i, n_kv, d)] = k_new[src];
+        v_pool[v_index(blk, h, slot, i, n_kv, d)] = v_new[src];
+      }
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------
+ * Copy on write ([DSS] "Paged attention"): block dst[p] becomes a copy of
+ * block src[p], K and V, every head and slot. */
+int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src,
+                       const int32_t* dst, int n_pairs, int num_blocks,
+                       int n_kv, int d) {
+  int status = 0;
+  size_t per_block = (size_t)n_kv * ORACLE_BLOCK * d;
+  for (int p = 0; p < n_pairs; ++p) {
+    if (src[p] < 0 || src[p] >= num_blocks || dst[p] < 0 || dst[p] >= num_blocks) {
+      status = -1;
+      continue;
+    }
+    for (size_t e = 0; e < per_block; ++e) {
+      k_pool[(size_t)dst[p] * per_block + e] = k_pool[(size_t)src[p] * per_block + e];
+      v_pool[(size_t)dst[p] * per_block + e] = v_pool[(size_t)src[p] * per_block + e];
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------
+ * One output row: the attention of query row q_row (d values, bf16 bits)
+ * over the ctx cached tokens of one sequence, reached through its table,
+ * for KV head h. Softmax written as its definition with the maximum
+ * subtracted first (the shift leaves the ratios unchanged and keeps exp()
+ * finite):
+ *   z_t = scale * sum_i q_i k_{t,i}
+ *   w_t = exp(z_t - max_u z_u),   out_i = (sum_t w_t v_{t,i}) / (sum_t w_t)
+ * Returns 0, or -1 with NaN written on an invalid block id or ctx < 1. */
+int oracle_decode_row(double* out_row, const uint16_t* q_row,
+                      const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* table_row, int ctx, int num_blocks,
+                      int n_kv, int h, int d, double scale) {
+  if (ctx < 1) {
+    for (int i = 0; i < d; ++i) out_row[i] = NAN;
+    return -1;
+  }
+  for (int b = 0; b < (ctx + ORACLE_BLOCK - 1) / ORACLE_BLOCK; ++b) {
+    if (table_row[b] < 0 || table_row[b] >= num_blocks) {
+      for (int i = 0; i < d; ++i) out_row[i] = NAN;
+      return -1;
+    }
+  }
+  double* z = (double*)malloc(sizeof(double) * (size_t)ctx);
+  if (!z) return -2;
+
+  for (int t = 0; t < ctx; ++t) {
+    int32_t blk = table_row[t / ORACLE_BLOCK];
+    int slot = t % ORACLE_BLOCK;
+    double dot = 0.0;
+    for (int i = 0; i < d; ++i)
+      dot += bf16_value(q_row[i]) * bf16_value(k_pool[k_index(blk, h, slot, i, n_kv, d)]);
+    z[t] = scale * dot;
+  }
+
+  double zmax = z[0];
+  for (int t = 1; t < ctx; ++t)
+    if (z[t] > zmax) zmax = z[t];
+
+  double denom = 0.0;
+  for (int t = 0; t < ctx; ++t) {
+    z[t] = exp(z[t] - zmax); /* z now holds the unnormalised weights */
+    denom += z[t];
+  }
+
+  for (int i = 0; i < d; ++i) {
+    double num = 0.0;
+    for (int t = 0; t < ctx; ++t) {
+      int32_t blk = table_row[t / ORACLE_BLOCK];
+      num += z[t] * bf16_value(v_pool[v_index(blk, h, t % ORACLE_BLOCK, i, n_kv, d)]);
+    }
+    out_row[i] = num / denom;
+  }
+  free(z);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * The whole decode step of one layer: every sequence s, every query head j
+ * (KV head j / G). out is double [num_seqs][n_q][d]. Returns 0, or -1 if any
+ * sequence was invalid (its rows are NaN). */
+int oracle_decode(double* out, const uint16_t* q, const uint16_t* k_pool,
+                  const uint16_t* v_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, int num_seqs,
+                  int max_blocks_per_seq, int num_blocks, int n_q, int n_kv,
+                  int d, double scale) {
+  if (n_kv <= 0 || n_q % n_kv != 0) return -3;
+  int group = n_q / n_kv;
+  int status = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    int ctx = context_lens[s];
+    int bad_ctx = ctx > ORACLE_BLOCK * max_blocks_per_seq;
+    for (int j = 0; j < n_q; ++j) {
+      double* row = out + ((size_t)s * n_q + j) * d;
+      if (bad_ctx) {
+        for (int i = 0; i < d; ++i) row[i] = NAN;
+        status = -1;
+        continue;
+      }
+      int rc = oracle_decode_row(row, q + ((size_t)s * n_q + j) * d, k_pool,
+                                 v_pool, block_tables + (size_t)s * max_blocks_per_seq,
+                                 ctx, num_blocks, n_kv, j / group, d, scale);
+      if (rc == -2) return -2;
+      if (rc != 0) status = -1;
+    }
+  }
+  return status;
+}

@@ -1,0 +1,56 @@
+"""Every plausible mistake in the oracle must fail at least one pin.
+
+Each mutant is a one-line textual change to a temporary copy of
+oracle/oracle.c (a dropped term, a wrong sign, index or layout, a missing
+normalisation), compiled with the same flags; the pin checks of
+tests/oracle_pins.py then run against it. Nothing here touches the real
+oracle build or the GPU.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from oracle.build import SRC, build
+from oracle_pins import ALL_CHECKS
+
+MUTANTS = {
+    "kv_head_modulo": ("j / group", "j % n_kv"),
+    "dropped_scale": ("z[t] = scale * dot;", "z[t] = dot;"),
+    "exp_sign": ("z[t] = exp(z[t] - zmax);", "z[t] = exp(zmax - z[t]);"),
+    "max_not_subtracted": ("z[t] = exp(z[t] - zmax);", "z[t] = exp(z[t]);"),
+    "v_layout_token_major": ("* d + i) * ORACLE_BLOCK + t);", "* ORACLE_BLOCK + t) * d + i);"),
+    "v_slot_from_block_index": ("v_index(blk, h, t % ORACLE_BLOCK, i, n_kv, d)",
+                                "v_index(blk, h, t / ORACLE_BLOCK, i, n_kv, d)"),
+    "k_dim_slot_swapped": ("bf16_value(k_pool[k_index(blk, h, slot, i, n_kv, d)])",
+                           "bf16_value(k_pool[k_index(blk, h, i % ORACLE_BLOCK, slot, n_kv, d)])"),
+    "context_off_by_one": ("for (int t = 0; t < ctx; ++t) {\n    int32_t blk",
+                           "for (int t = 0; t < ctx - 1; ++t) {\n    int32_t blk"),
+    "no_normalisation": ("out_row[i] = num / denom;", "out_row[i] = num;"),
+    "append_slot_shift": ("int slot = pos % ORACLE_BLOCK;", "int slot = (pos + 1) % ORACLE_BLOCK;"),
+    "append_table_entry": ("+ pos / ORACLE_BLOCK];", "+ ctx / ORACLE_BLOCK];"),
+    "copy_k_only": ("      v_pool[(size_t)dst[p] * per_block + e] = v_pool[(size_t)src[p] * per_block + e];\n", ""),
+    "kv_bytes_no_two": ("return (uint64_t)2 * (uint64_t)n_layers", "return (uint64_t)n_layers"),
+    "kv_bytes_no_precision": (" *\n         (uint64_t)bytes_per_value;", ";"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    build(src=str(src), lib=str(lib))
+    mutant = oracle.Oracle(str(lib))
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(mutant)
+        except Exception as e:  # noqa: BLE001 -- any failure counts as caught
+            failed.append((check.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
