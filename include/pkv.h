@@ -22,7 +22,7 @@
  * Memory layout (one K pool and one V pool per layer; the block tables are
  * one per sequence and shared by all layers)
  *
- *   PKV_BLOCK_TOKENS = 16 tokens per block ([M23] 23.4 gives "say 16 tokens").
+ *   PKV_BLOCK_TOKENS = 16 tokens per block (the block size [M23] 23.4 uses as its example).
  *
  *   k_pool  bf16  [num_blocks][n_kv_heads][16][head_dim]        (token-major)
  *           element (blk, h, t, i) at  ((blk*n_kv_heads + h)*16 + t)*head_dim + i
@@ -148,9 +148,10 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  * paged_attn_decode: the attention above, for every sequence and query head.
  *
  * The context of each sequence is cut into partitions of partition_tokens
- * tokens (a multiple of 16; 0 = library default). One wavefront handles one
- * (sequence, KV head, partition) and serves all G query heads of that KV
- * head from the same K/V tiles, so each KV byte is read once. If more than
+ * tokens (a multiple of 16 in [16, 1024]; 0 = library default). One
+ * wavefront handles one (sequence, KV head, partition) and serves up to 16
+ * query heads of that KV head from the same K/V tiles, so each KV byte is
+ * read once for G <= 16 (larger groups take ceil(G/16) passes). If more than
  * one partition is needed (max_context_len > partition_tokens) a second
  * kernel merges the partial (max, sum, accumulator) triples; the workspace
  * holds them. Exactly ceil(max_context_len/partition_tokens) partitions are
@@ -169,7 +170,8 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  * entry outside [0, num_blocks): out[s,:,:] becomes NaN for that sequence
  * and the PKV_DEVERR bit is set. num_seqs == 0 is a no-op. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
-                                  int32_t head_dim, int32_t max_context_len,
+                                  int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len,
                                   int32_t partition_tokens);
 int pkv_paged_attn_decode(float* out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables,
@@ -180,8 +182,37 @@ int pkv_paged_attn_decode(float* out, const void* q, const void* k_pool,
                           int32_t max_context_len, int32_t partition_tokens,
                           void* workspace, size_t workspace_bytes,
                           int32_t* err_flag, void* stream);
-/* The partition size the library uses when partition_tokens == 0. */
-int32_t pkv_default_partition_tokens(int32_t head_dim, int32_t max_context_len);
+/* The two kernels of pkv_paged_attn_decode as separate calls, with the
+ * same arguments and checks; calling partition then merge on one stream is
+ * exactly pkv_paged_attn_decode. pkv_paged_attn_partition writes out
+ * directly when one partition covers max_context_len, else the partial
+ * (max, sum, accumulator) triples into the workspace; pkv_paged_attn_merge
+ * combines them into out and is a no-op in the single-partition case.
+ * Separate calls let a caller time or overlap the two kernels. */
+int pkv_paged_attn_partition(float* out, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_tables,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, int32_t num_blocks,
+                             int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float scale,
+                             int32_t max_context_len, int32_t partition_tokens,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t* err_flag, void* stream);
+int pkv_paged_attn_merge(float* out, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float scale,
+                         int32_t max_context_len, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes,
+                         int32_t* err_flag, void* stream);
+/* The partition size the library uses when partition_tokens == 0: the
+ * largest of 512, 256, 128, 64 tokens that still gives at least 8192
+ * wavefronts for num_seqs * n_kv_heads * ceil(G/16) * ceil(max_ctx / P). */
+int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim,
+                                     int32_t max_context_len);
 
 /* ------------------------------------------------------------------------
  * copy_blocks: copy-on-write support ([DSS] "Paged attention": when

@@ -1,0 +1,332 @@
+"""paged_kv_cache_468_amd -- paged decode attention on AMD MI355X (gfx950).
+
+A thin ctypes binding of libpkv.so (the C ABI in include/pkv.h). Every
+function here only marshals arguments: checks that tensors have the
+documented dtype, shape, device and contiguity, and passes their device
+pointers, sizes and torch's current HIP stream to the library. All compute
+runs in the library's HIP kernels; there is no fallback. If libpkv.so is
+missing the import fails with an error that says how to build it.
+
+Functions keep the C names (pkv_*). Tensors:
+  k_pool  torch.bfloat16 [num_blocks, n_kv, 16, head_dim]   (token-major)
+  v_pool  torch.bfloat16 [num_blocks, n_kv, head_dim, 16]   (dim-major)
+  q       torch.bfloat16 [num_seqs, n_q, head_dim]
+  k_new / v_new torch.bfloat16 [num_seqs, n_kv, head_dim]
+  out     torch.float32 [num_seqs, n_q, head_dim]
+  block_tables torch.int32 [num_seqs, max_blocks]; context_lens torch.int32 [num_seqs]
+  err_flag torch.int32 [1] or None
+The allocator works on host numpy int32 tables.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4, -5
+PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT, PKV_DEVERR_COPY_PAIR = 1, 2, 4
+BLOCK_TOKENS = 16
+
+# every symbol include/pkv.h declares, with its ctypes signature
+_vp, _i32, _i64, _u64, _sz, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_uint64, ctypes.c_size_t, ctypes.c_float)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+SIGNATURES = {
+    "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_kv_bytes_per_token": (_u64, [_i32, _i32, _i32, _i32]),
+    "pkv_kv_cache_bytes": (_u64, [_i32, _i32, _i32, _i64, _i64, _i32]),
+    "pkv_pool_bytes": (_u64, [_i32, _i32, _i32]),
+    "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                     _vp, _vp]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_attn_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp,
+                                                _vp]),
+    "pkv_paged_attn_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_default_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
+    "pkv_allocator_destroy": (None, [_vp]),
+    "pkv_block_alloc": (ctypes.c_int, [_vp, _i32p]),
+    "pkv_block_incref": (ctypes.c_int, [_vp, _i32]),
+    "pkv_block_decref": (ctypes.c_int, [_vp, _i32]),
+    "pkv_block_refcount": (_i32, [_vp, _i32]),
+    "pkv_num_free": (_i32, [_vp]),
+    "pkv_num_blocks": (_i32, [_vp]),
+    "pkv_seq_grow": (ctypes.c_int, [_vp, _i32p, _i32p, _i32, _i32, _i32p, _i32p]),
+    "pkv_seq_fork": (ctypes.c_int, [_vp, _i32p, _i32]),
+    "pkv_seq_release": (ctypes.c_int, [_vp, _i32p, _i32]),
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+
+
+def _load():
+    # torch first: libpkv.so then binds to the HIP runtime torch already
+    # loaded (same soname), so torch's device pointers and stream handles are
+    # valid in the library. Loaded the other way round, the process would
+    # hold two HIP runtimes and torch's streams would be foreign handles.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python paged_kv_cache_468_amd/build.py` (hipcc, gfx950). There is no fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.pkv_strerror(int(status)).decode()
+
+
+def _check(status, where):
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _flag(err_flag):
+    if err_flag is None:
+        return None
+    return _dev(err_flag, "err_flag", _torch().int32)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _pool_dims(k_pool, v_pool):
+    torch = _torch()
+    _dev(k_pool, "k_pool", torch.bfloat16, 4)
+    _dev(v_pool, "v_pool", torch.bfloat16, 4)
+    nb, n_kv, bt, d = k_pool.shape
+    if bt != BLOCK_TOKENS or tuple(v_pool.shape) != (nb, n_kv, d, BLOCK_TOKENS):
+        raise ValueError(f"pools: expected K [nb, n_kv, 16, d] and V [nb, n_kv, d, 16], got "
+                         f"{tuple(k_pool.shape)} and {tuple(v_pool.shape)}")
+    return nb, n_kv, d
+
+
+# ---------------------------------------------------------------------------
+# C ABI, same names
+
+def pkv_kv_bytes_per_token(n_layers, n_kv_heads, head_dim, bytes_per_value=2):
+    return int(lib.pkv_kv_bytes_per_token(n_layers, n_kv_heads, head_dim, bytes_per_value))
+
+
+def pkv_kv_cache_bytes(n_layers, n_kv_heads, head_dim, context_len, batch, bytes_per_value=2):
+    return int(lib.pkv_kv_cache_bytes(n_layers, n_kv_heads, head_dim, context_len, batch,
+                                      bytes_per_value))
+
+
+def pkv_pool_bytes(num_blocks, n_kv_heads, head_dim):
+    return int(lib.pkv_pool_bytes(num_blocks, n_kv_heads, head_dim))
+
+
+def pkv_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, err_flag=None,
+                  stream=None):
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(k_new, "k_new", torch.bfloat16, 3)
+    _dev(v_new, "v_new", torch.bfloat16, 3)
+    num_seqs = k_new.shape[0]
+    if tuple(k_new.shape) != (num_seqs, n_kv, d) or tuple(v_new.shape) != (num_seqs, n_kv, d):
+        raise ValueError("k_new / v_new: expected [num_seqs, n_kv, head_dim]")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens: first dim must be num_seqs")
+    _check(lib.pkv_kv_append(_dev(k_pool, "k_pool", torch.bfloat16),
+                             _dev(v_pool, "v_pool", torch.bfloat16),
+                             _dev(k_new, "k_new", torch.bfloat16),
+                             _dev(v_new, "v_new", torch.bfloat16), bt, cl, num_seqs,
+                             block_tables.shape[1], nb, n_kv, d, _flag(err_flag),
+                             _stream(stream)), "pkv_kv_append")
+
+
+def pkv_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
+                               partition_tokens=0):
+    return int(lib.pkv_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim,
+                                              max_context_len, partition_tokens))
+
+
+def pkv_default_partition_tokens(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len):
+    return int(lib.pkv_default_partition_tokens(num_seqs, n_q_heads, n_kv_heads, head_dim,
+                                                max_context_len))
+
+
+def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                 partition_tokens, workspace, err_flag, stream):
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16, 3)
+    num_seqs, n_q, dq = q.shape
+    if dq != d:
+        raise ValueError("q: head_dim differs from the pools'")
+    _dev(out, "out", torch.float32, 3)
+    if tuple(out.shape) != (num_seqs, n_q, d):
+        raise ValueError("out: expected [num_seqs, n_q, head_dim] float32")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens: first dim must be num_seqs")
+    need = pkv_decode_workspace_bytes(num_seqs, n_q, n_kv, d, max_context_len, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    return (_dev(out, "out", torch.float32), _dev(q, "q", torch.bfloat16),
+            _dev(k_pool, "k_pool", torch.bfloat16), _dev(v_pool, "v_pool", torch.bfloat16), bt, cl,
+            num_seqs, block_tables.shape[1], nb, n_q, n_kv, d, float(scale), int(max_context_len),
+            int(partition_tokens), ws_ptr, ws_bytes, _flag(err_flag), _stream(stream)), workspace
+
+
+def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                          stream=None):
+    """out <- attention of q over the paged cache. workspace: a torch uint8
+    CUDA tensor of at least pkv_decode_workspace_bytes(...) bytes, or None
+    to have one allocated here (by torch's caching allocator)."""
+    args, _ = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                           max_context_len, partition_tokens, workspace, err_flag, stream)
+    _check(lib.pkv_paged_attn_decode(*args), "pkv_paged_attn_decode")
+
+
+def pkv_paged_attn_partition(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                             max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                             stream=None):
+    """First kernel of the decode; returns the workspace it used (pass the
+    same one to pkv_paged_attn_merge)."""
+    args, ws = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                            max_context_len, partition_tokens, workspace, err_flag, stream)
+    _check(lib.pkv_paged_attn_partition(*args), "pkv_paged_attn_partition")
+    return ws
+
+
+def pkv_paged_attn_merge(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                         max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                         stream=None):
+    args, _ = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                           max_context_len, partition_tokens, workspace, err_flag, stream)
+    _check(lib.pkv_paged_attn_merge(*args), "pkv_paged_attn_merge")
+
+
+def pkv_copy_blocks(k_pool, v_pool, src, dst, err_flag=None, stream=None):
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    s = _dev(src, "src", torch.int32, 1)
+    t = _dev(dst, "dst", torch.int32, 1)
+    if src.shape != dst.shape:
+        raise ValueError("src / dst: same length required")
+    _check(lib.pkv_copy_blocks(_dev(k_pool, "k_pool", torch.bfloat16),
+                               _dev(v_pool, "v_pool", torch.bfloat16), s, t, src.shape[0], nb,
+                               n_kv, d, _flag(err_flag), _stream(stream)), "pkv_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+
+def _i32_host(a, name):
+    if not isinstance(a, np.ndarray) or a.dtype != np.int32 or not a.flags.c_contiguous:
+        raise TypeError(f"{name}: expected a contiguous numpy int32 array")
+    return a.ctypes.data_as(_i32p)
+
+
+class Allocator:
+    """Owner of a pkv_allocator handle (host memory, one thread)."""
+
+    def __init__(self, num_blocks: int):
+        h = ctypes.c_void_p()
+        _check(lib.pkv_allocator_create(num_blocks, ctypes.byref(h)), "pkv_allocator_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pkv_block_alloc(self) -> int:
+        out = ctypes.c_int32()
+        _check(lib.pkv_block_alloc(self._h, ctypes.byref(out)), "pkv_block_alloc")
+        return out.value
+
+    def pkv_block_incref(self, b):
+        _check(lib.pkv_block_incref(self._h, int(b)), "pkv_block_incref")
+
+    def pkv_block_decref(self, b):
+        _check(lib.pkv_block_decref(self._h, int(b)), "pkv_block_decref")
+
+    def pkv_block_refcount(self, b) -> int:
+        return int(lib.pkv_block_refcount(self._h, int(b)))
+
+    def pkv_num_free(self) -> int:
+        return int(lib.pkv_num_free(self._h))
+
+    def pkv_num_blocks(self) -> int:
+        return int(lib.pkv_num_blocks(self._h))
+
+    def pkv_seq_grow(self, table: np.ndarray, n_blocks: int, new_context_len: int):
+        """Returns (status, n_blocks, cow_src, cow_dst); status is PKV_OK or
+        PKV_ENOMEM (other codes raise)."""
+        nb = ctypes.c_int32(n_blocks)
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        st = lib.pkv_seq_grow(self._h, _i32_host(table, "table"), ctypes.byref(nb),
+                              table.shape[0], int(new_context_len), ctypes.byref(src),
+                              ctypes.byref(dst))
+        if st not in (PKV_OK, PKV_ENOMEM):
+            raise PkvError(st, "pkv_seq_grow")
+        return st, nb.value, src.value, dst.value
+
+    def pkv_seq_fork(self, table: np.ndarray, n_blocks: int):
+        _check(lib.pkv_seq_fork(self._h, _i32_host(table, "table"), int(n_blocks)), "pkv_seq_fork")
+
+    def pkv_seq_release(self, table: np.ndarray, n_blocks: int):
+        _check(lib.pkv_seq_release(self._h, _i32_host(table, "table"), int(n_blocks)),
+               "pkv_seq_release")

@@ -1,0 +1,105 @@
+"""The C ABI library loads and exports every symbol include/pkv.h declares;
+host-only entry points and host-side argument checks work without a GPU
+(nothing here launches a kernel)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    import paged_kv_cache_468_amd as pkv
+    syms = declared_symbols()
+    assert len(syms) >= 20
+    for name in syms:
+        assert hasattr(pkv.lib, name), name
+        assert name in pkv.SIGNATURES, f"binding lacks a signature for {name}"
+    assert sorted(pkv.SIGNATURES) == syms
+
+
+def test_library_is_in_tree():
+    import paged_kv_cache_468_amd as pkv
+    assert os.path.dirname(pkv.LIB_PATH) == os.path.join(ROOT, "paged_kv_cache_468_amd")
+
+
+def test_kv_bytes_against_printed_values():
+    """The library's closed form against the same printed values the oracle
+    is pinned to (tests/golden/kv_sizes.json)."""
+    import paged_kv_cache_468_amd as pkv
+    doc = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_sizes.json")))
+    for c in doc["cases"]:
+        got = pkv.pkv_kv_cache_bytes(c["layers"], c["kv_heads"], c["d"], c["L"], c["B"], c["bytes"])
+        assert got == pkv.pkv_kv_bytes_per_token(c["layers"], c["kv_heads"], c["d"], c["bytes"]) * c["L"] * c["B"]
+        if "exact_bytes" in c:
+            assert got == c["exact_bytes"], c["cite"]
+        elif "rounds_to" in c:
+            scale = 1e9 if c["unit"].endswith("GB") else 1e6
+            assert round(got / scale, c["decimals"]) == c["rounds_to"], c["cite"]
+        else:
+            scale = 2**30 if c["unit"] == "GiB" else 1.0
+            assert abs(got / scale - c["approx"]) <= c["tol"], c["cite"]
+    assert pkv.pkv_pool_bytes(10, 8, 128) == 10 * 8 * 16 * 128 * 2
+    # one pool per layer holds exactly kv_bytes_per_token(1 layer)/2 per slot
+    assert pkv.pkv_pool_bytes(1, 4, 64) * 2 == pkv.pkv_kv_bytes_per_token(1, 4, 64) * 16
+
+
+def test_strerror():
+    import paged_kv_cache_468_amd as pkv
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(pkv.strerror(code), str) and pkv.strerror(code)
+
+
+def _decode_raw(**over):
+    import paged_kv_cache_468_amd as pkv
+    a = dict(out=None, q=None, k=None, v=None, bt=None, cl=None, num_seqs=4, max_blocks=16,
+             num_blocks=64, n_q=8, n_kv=2, d=128, scale=0.1, max_ctx=256, part=0, ws=None,
+             ws_bytes=0, err=None, stream=None)
+    a.update(over)
+    dummy = ctypes.c_void_p(0x1000)   # never dereferenced: host checks reject first
+    ptr = lambda x: dummy if x is None else x
+    return pkv.lib.pkv_paged_attn_decode(ptr(a["out"]), ptr(a["q"]), ptr(a["k"]), ptr(a["v"]),
+                                         ptr(a["bt"]), ptr(a["cl"]), a["num_seqs"], a["max_blocks"],
+                                         a["num_blocks"], a["n_q"], a["n_kv"], a["d"], a["scale"],
+                                         a["max_ctx"], a["part"], a["ws"], a["ws_bytes"], a["err"],
+                                         a["stream"])
+
+
+def test_host_side_argument_checks():
+    import paged_kv_cache_468_amd as pkv
+    assert _decode_raw(d=96) == pkv.PKV_EUNSUPPORTED
+    assert _decode_raw(n_q=9, n_kv=2) == pkv.PKV_EINVAL
+    assert _decode_raw(max_ctx=16 * 16 + 1) == pkv.PKV_EINVAL
+    assert _decode_raw(part=24) == pkv.PKV_EINVAL
+    assert _decode_raw(part=2048) == pkv.PKV_EINVAL
+    assert _decode_raw(scale=float("nan")) == pkv.PKV_EINVAL
+    assert _decode_raw(num_seqs=-1) == pkv.PKV_EINVAL
+    assert _decode_raw(num_seqs=0) == pkv.PKV_OK                 # no-op, nothing launched
+    # a multi-partition launch needs a workspace of the advertised size
+    need = pkv.pkv_decode_workspace_bytes(4, 8, 2, 128, 256, 64)
+    assert need == 4 * 8 * 4 * (2 + 128) * 4
+    assert _decode_raw(part=64, ws=None, ws_bytes=0) == pkv.PKV_EWORKSPACE
+    assert _decode_raw(part=64, ws=ctypes.c_void_p(0x1000), ws_bytes=need - 1) == pkv.PKV_EWORKSPACE
+    assert pkv.pkv_decode_workspace_bytes(4, 8, 2, 128, 256, 256) == 0   # single partition
+    assert pkv.lib.pkv_kv_append(None, None, None, None, None, None, 4, 16, 64, 2, 128, None, None) == pkv.PKV_EINVAL
+    assert pkv.lib.pkv_kv_append(None, None, None, None, None, None, 4, 16, 64, 2, 80, None, None) == pkv.PKV_EUNSUPPORTED
+    assert pkv.lib.pkv_copy_blocks(None, None, None, None, 0, 64, 2, 128, None, None) == pkv.PKV_OK
+    assert pkv.lib.pkv_copy_blocks(None, None, None, None, 3, 64, 2, 128, None, None) == pkv.PKV_EINVAL
+
+
+def test_default_partition():
+    import paged_kv_cache_468_amd as pkv
+    # LLaMA-3-8B shape: 64 x 8 x ceil(8192/512) = 8192 waves at 512 tokens
+    assert pkv.pkv_default_partition_tokens(64, 32, 8, 128, 8192) == 512
+    p = pkv.pkv_default_partition_tokens(128, 20, 4, 64, 2048)
+    assert p % 16 == 0 and 64 <= p <= 512
