@@ -1,0 +1,442 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of paged attention on one MI355X.
+
+One step is one decode iteration of the whole batch over every layer:
+  host    every sequence grows by one token through the block allocator
+          (pkv_seq_grow: a fresh block at each 16-token boundary), and the
+          tables and context lengths go to the device (async, pinned);
+  device  per layer: kv_append (the new token's K/V into its slot),
+          the partition kernel (scores, online softmax, P.V per context
+          partition) and the merge kernel (log-sum-exp merge of partitions).
+The default workload is the LLaMA-3-8B grouped-query shape (32 layers,
+32 query / 8 KV heads, head size 128, bf16 KV in 16-token blocks, 64
+sequences with contexts uniform in [1024, 8192], a 2,048-token prefix shared
+through refcounted blocks), and the same shape with private copies of the
+prefix (no sharing). Inputs are seeded synthetic N(0,1) values drawn on the
+device; the pool is fragmented (block ids handed out in a random order).
+
+Printed: one JSON line with the KV GB/s of the step (value), steps/s,
+the partition kernel's roofline (HIP events on the stream it runs on), the
+CPU oracle timed on a bounded sample of the same bytes, and the parity of
+that sample against the GPU output.
+
+  python bench.py [--steps K] [--warmup W] [--config 4] [--no-share-run/--skip-no-share]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workload as w  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+BLOCK = 16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_attn_partition_llama3-8b.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_468_amd", "csrc", "attention.hip")
+
+WORKLOAD_NAMES = {
+    1: "tiny-1layer-20q4kv-d64",
+    2: "0.5B-24layer-20q4kv-d64-B128",
+    3: "llama2-7b-mha-32layer-32q32kv-d128-B32-ctx4096",
+    4: "llama3-8b-gqa-32layer-32q8kv-d128-B64-ctx1024..8192-prefix2048",
+    5: "80layer-gqa-64q8kv-d128-B60-ctx8000",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workload state built through the library's own allocator
+
+class State:
+    pass
+
+
+def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens):
+    """Block tables from the refcounted allocator, pools filled on the
+    device, every layer's buffers, and pre-marshalled library calls."""
+    cl = w.context_lengths(shape, seed).astype(np.int32)
+    B = len(cl)
+    L, n_q, n_kv, d = shape.n_layers, shape.n_q, shape.n_kv, shape.d
+    final_ctx = cl + extra_tokens
+    max_blocks = int(math.ceil(int(final_ctx.max()) / BLOCK))
+    n_prefix = shape.prefix_tokens // BLOCK if share else 0
+    # blocks held at the end of the run: the prefix owner's, plus each
+    # sequence's own (the ones not shared)
+    own = [int(math.ceil(int(c) / BLOCK)) - min(n_prefix, int(math.ceil(int(c0) / BLOCK)))
+           + (1 if n_prefix and int(c0) <= shape.prefix_tokens else 0)
+           for c, c0 in zip(final_ctx, cl)]
+    num_blocks = n_prefix + sum(own)
+
+    alloc = pkv.Allocator(num_blocks)
+    # fragmented pool: take every block, give them back in a seeded random
+    # order; the LIFO free list then hands them out in that order
+    for _ in range(num_blocks):
+        alloc.pkv_block_alloc()
+    for b in w.rng(seed, 1).permutation(num_blocks):
+        alloc.pkv_block_decref(int(b))
+
+    tables = np.full((B, max_blocks), -1, np.int32)
+    nblk = np.zeros(B, np.int32)
+    cow = []
+    if n_prefix:
+        prefix = np.full(max_blocks, -1, np.int32)
+        st, n, _, _ = alloc.pkv_seq_grow(prefix, 0, shape.prefix_tokens)
+        assert st == pkv.PKV_OK and n == n_prefix
+        for s in range(B):
+            k = min(n_prefix, int(math.ceil(int(cl[s]) / BLOCK)))
+            alloc.pkv_seq_fork(prefix, k)
+            tables[s, :k] = prefix[:k]
+            nblk[s] = k
+    for s in range(B):
+        st, nblk[s], src, dst = alloc.pkv_seq_grow(tables[s], int(nblk[s]), int(cl[s]))
+        assert st == pkv.PKV_OK
+        if src >= 0:
+            cow.append((src, dst))
+
+    S = State()
+    S.shape, S.share, S.B, S.alloc = shape, share, B, alloc
+    S.ctx = cl.copy()
+    S.tables, S.nblk, S.num_blocks, S.max_blocks = tables, nblk, num_blocks, max_blocks
+    S.max_ctx = int(final_ctx.max())
+    S.n_cow = len(cow)
+    dev = torch.device("cuda")
+    S.k_pool = torch.empty((L, num_blocks, n_kv, BLOCK, d), dtype=torch.bfloat16, device=dev)
+    S.v_pool = torch.empty((L, num_blocks, n_kv, d, BLOCK), dtype=torch.bfloat16, device=dev)
+    base = seed * 1000 + (0 if share else 500)
+    w.device_normal_bf16_(S.k_pool, base + 1)
+    w.device_normal_bf16_(S.v_pool, base + 2)
+    S.q = w.device_normal_bf16_(torch.empty((L, B, n_q, d), dtype=torch.bfloat16, device=dev), base + 3)
+    S.k_new = w.device_normal_bf16_(torch.empty((L, B, n_kv, d), dtype=torch.bfloat16, device=dev), base + 4)
+    S.v_new = w.device_normal_bf16_(torch.empty((L, B, n_kv, d), dtype=torch.bfloat16, device=dev), base + 5)
+    S.out = torch.zeros((L, B, n_q, d), dtype=torch.float32, device=dev)
+    S.bt = torch.from_numpy(tables).to(dev)
+    S.cl = torch.from_numpy(S.ctx).to(dev)
+    S.err = torch.zeros(1, dtype=torch.int32, device=dev)
+    # staging for the per-step table upload: two pinned buffers, reused
+    # only after the copy that last read them has finished
+    S.pin_bt = [torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    S.pin_cl = [torch.empty((B,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    S.pin_done = [None, None]
+
+    if cow:   # copy-on-write of the prefix blocks the short sequences write into
+        src = torch.tensor([c[0] for c in cow], dtype=torch.int32, device=dev)
+        dst = torch.tensor([c[1] for c in cow], dtype=torch.int32, device=dev)
+        for l in range(L):
+            pkv.pkv_copy_blocks(S.k_pool[l], S.v_pool[l], src, dst, err_flag=S.err)
+
+    S.partition = partition_tokens or pkv.pkv_default_partition_tokens(B, n_q, n_kv, d, S.max_ctx)
+    ws_bytes = pkv.pkv_decode_workspace_bytes(B, n_q, n_kv, d, S.max_ctx, S.partition)
+    S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    S.calls = []
+    for l in range(L):
+        app = pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l], S.bt, S.cl,
+                                    err_flag=S.err)
+        part = pkv.prepare_paged_attn_partition(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
+                                                S.cl, shape.scale, S.max_ctx, S.partition,
+                                                workspace=S.ws, err_flag=S.err)
+        merge = pkv.prepare_paged_attn_merge(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
+                                             S.cl, shape.scale, S.max_ctx, S.partition,
+                                             workspace=S.ws, err_flag=S.err)
+        S.calls.append((app, part, merge))
+    torch.cuda.synchronize()
+    assert int(S.err.item()) == 0
+    return S
+
+
+def host_grow(pkv, S):
+    """The allocator's per-step work: every sequence takes one more token."""
+    S.ctx += 1
+    for s in range(S.B):
+        st, nb, src, dst = S.alloc.pkv_seq_grow(S.tables[s], int(S.nblk[s]), int(S.ctx[s]))
+        if st != pkv.PKV_OK or src >= 0:
+            raise RuntimeError(f"sequence {s}: grow returned {st}, copy-on-write ({src}, {dst})")
+        S.nblk[s] = nb
+
+
+def upload_tables(torch, S, i):
+    b = i & 1
+    if S.pin_done[b] is not None:
+        S.pin_done[b].synchronize()
+    S.pin_bt[b].numpy()[...] = S.tables
+    S.pin_cl[b].numpy()[...] = S.ctx
+    S.bt.copy_(S.pin_bt[b], non_blocking=True)
+    S.cl.copy_(S.pin_cl[b], non_blocking=True)
+    ev = torch.cuda.Event()
+    ev.record()
+    S.pin_done[b] = ev
+
+
+def kv_bytes(S, ctx):
+    """Algorithmic KV bytes of one layer: K and V of every cached token,
+    n_kv heads x head_dim x 2 bytes each."""
+    return 2 * S.shape.n_kv * S.shape.d * 2 * int(ctx.astype(np.int64).sum())
+
+
+def partition_alg_bytes(S, ctx):
+    """Algorithmic bytes of one partition-kernel launch (one layer): the KV
+    it must consume, plus q (bf16), the fp32 output rows, the block-table
+    entries and the context lengths."""
+    sh = S.shape
+    B = len(ctx)
+    tbl = 4 * int(np.ceil(ctx / BLOCK).astype(np.int64).sum())
+    return kv_bytes(S, ctx) + B * sh.n_q * sh.d * (2 + 4) + tbl + 4 * B
+
+
+def run(pkv, torch, S, steps, warmup):
+    L = S.shape.n_layers
+    for i in range(warmup):
+        host_grow(pkv, S)
+        upload_tables(torch, S, i)
+        for app, part, merge in S.calls:
+            app()
+            part()
+            merge()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+          for _ in range(steps)]
+    step_ctx = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        host_grow(pkv, S)
+        step_ctx.append(S.ctx.copy())
+        upload_tables(torch, S, warmup + i)
+        for l, (app, part, merge) in enumerate(S.calls):
+            e = ev[i][l]
+            e[0].record()
+            app()
+            e[1].record()
+            part()
+            e[2].record()
+            merge()
+            e[3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    err = int(S.err.item())
+    if err:
+        raise RuntimeError(f"device error flag {err}")
+    app_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(L)] for i in range(steps)])
+    part_ms = np.array([[ev[i][l][1].elapsed_time(ev[i][l][2]) for l in range(L)] for i in range(steps)])
+    merge_ms = np.array([[ev[i][l][2].elapsed_time(ev[i][l][3]) for l in range(L)] for i in range(steps)])
+    ms_per_step = max(gpu_ms, wall * 1e3) / steps
+    kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all steps
+    part_bytes = sum(partition_alg_bytes(S, c) for c in step_ctx) / steps   # per launch
+    part_us = float(part_ms.mean() * 1e3)
+    r = {
+        "ms_per_step": ms_per_step,
+        "steps_per_s": 1e3 / ms_per_step,
+        "kv_gbs": kvb / (ms_per_step * steps * 1e-3) / 1e9,
+        "seq_tokens_per_s": sum(int(c.astype(np.int64).sum()) for c in step_ctx) / (ms_per_step * steps * 1e-3),
+        "tokens_per_s": S.B / (ms_per_step * 1e-3),
+        "kv_bytes_per_step": kvb / steps,
+        "partition_us": part_us,
+        "append_us": float(app_ms.mean() * 1e3),
+        "merge_us": float(merge_ms.mean() * 1e3),
+        "partition_alg_bytes": part_bytes,
+        "partition_gbs": part_bytes / (part_us * 1e-6) / 1e9,
+        "partition_tokens": S.partition,
+        "num_blocks_per_layer": S.num_blocks,
+        "cow_copies": S.n_cow,
+        "gpu_event_ms_total": gpu_ms,
+        "host_wall_ms_total": wall * 1e3,
+    }
+    return r
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on a bounded sample of the same bytes (layer 0)
+
+def cpu_baseline(torch, S, budget_s):
+    import oracle
+    orc = oracle.default()
+    sh = S.shape
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    k0, v0, q0 = u16(S.k_pool[0]), u16(S.v_pool[0]), u16(S.q[0])
+    got = S.out[0].cpu().numpy().astype(np.float64)
+    done, kvb, t_used, worst = 0, 0, 0.0, 0.0
+    order = w.rng(12345, 7).permutation(S.B)
+    for s in order:
+        t0 = time.perf_counter()
+        want, rc = orc.decode(q0[s:s + 1], k0, v0, S.tables[s:s + 1], S.ctx[s:s + 1], sh.n_kv, sh.scale)
+        t_used += time.perf_counter() - t0
+        assert rc == 0
+        worst = max(worst, float(np.abs(want[0] - got[s]).max()))
+        kvb += 2 * sh.n_kv * sh.d * 2 * int(S.ctx[s])
+        done += 1
+        if t_used >= budget_s:
+            break
+    gbs = kvb / t_used / 1e9
+    return {
+        "value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"layer 0, {done} of {S.B} sequences in seeded random order "
+                   f"({int(sum(S.ctx[s] for s in order[:done]))} context tokens, all {sh.n_q} query heads), "
+                   f"single-threaded C oracle in float64, {t_used:.1f} s"),
+        "seconds": t_used,
+        "steps_per_s_equiv": gbs * 1e9 / (kv_bytes(S, S.ctx) * sh.n_layers),
+    }, worst, done
+
+
+def stored_traffic(part_alg_bytes):
+    """HBM bytes per partition-kernel launch from the committed counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    rec = None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if rec is None:
+        return None, "no record in counter summary"
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return rec["hbm_bytes_per_dispatch"], None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, choices=sorted(w.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-share", action="store_true", help="main run with private prefix copies")
+    ap.add_argument("--skip-no-share", action="store_true", help="skip the second, unshared run")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no collectives or sharding are implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_468_amd as pkv
+    torch.cuda.set_device(0)
+    shape = w.CONFIGS[args.config]
+    extra = args.steps + args.warmup
+
+    share_main = (not args.no_share) and shape.prefix_tokens > 0
+    log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")
+    S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens)
+    log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition}, cow {S.n_cow}; timing")
+    main_r = run(pkv, torch, S, args.steps, args.warmup)
+    log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step, {main_r['kv_gbs']:.0f} GB/s, "
+        f"partition {main_r['partition_us']:.1f} us = {main_r['partition_gbs']:.0f} GB/s")
+
+    cpu, parity, n_par = None, None, 0
+    if args.cpu_seconds > 0:
+        log("[bench] cpu oracle baseline")
+        cpu, parity, n_par = cpu_baseline(torch, S, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.3f} GB/s, parity max-abs {parity:.2e} over {n_par} seqs")
+    del S
+    torch.cuda.empty_cache()
+
+    extra_runs = {}
+    if shape.prefix_tokens > 0 and share_main and not args.skip_no_share:
+        log("[bench] no-share run")
+        S2 = build_state(pkv, torch, shape, args.seed, False, extra, args.partition_tokens)
+        r2 = run(pkv, torch, S2, args.steps, args.warmup)
+        log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step, {r2['kv_gbs']:.0f} GB/s, "
+            f"partition {r2['partition_us']:.1f} us = {r2['partition_gbs']:.0f} GB/s")
+        extra_runs["no_share"] = {
+            "value": r2["kv_gbs"], "unit": "GB/s", "ms_per_step": r2["ms_per_step"],
+            "steps_per_s": r2["steps_per_s"], "pct_hbm_peak": 100 * r2["kv_gbs"] / HBM_PEAK_GBS,
+            "partition_us": r2["partition_us"], "partition_gbs": r2["partition_gbs"],
+            "partition_frac": r2["partition_gbs"] / HBM_PEAK_GBS,
+            "num_blocks_per_layer": r2["num_blocks_per_layer"],
+        }
+        del S2
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    traffic, why = stored_traffic(main_r["partition_alg_bytes"]) if args.config == 4 and share_main else (None, "other workload")
+    line = {
+        "metric": "paged decode-attention KV GB/s (% of HBM peak) + steps/s, Llama-3-8B shape",
+        "value": main_r["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "layers": shape.n_layers, "batch": S_batch(shape), "n_q_heads": shape.n_q,
+            "n_kv_heads": shape.n_kv, "head_dim": shape.d, "block_tokens": BLOCK,
+            "context": ([int(c) for c in shape.fixed_ctx] if shape.fixed_ctx else [shape.ctx_lo, shape.ctx_hi]),
+            "shared_prefix_tokens": shape.prefix_tokens if share_main else 0,
+            "seed": args.seed, "partition_tokens": main_r["partition_tokens"],
+        },
+        "steps_per_s": main_r["steps_per_s"],
+        "seq_tokens_per_s": main_r["seq_tokens_per_s"],
+        "tokens_per_s": main_r["tokens_per_s"],
+        "pct_hbm_peak": 100 * main_r["kv_gbs"] / HBM_PEAK_GBS,
+        "kv_bytes_per_step": main_r["kv_bytes_per_step"],
+        "kernels_us": {"kv_append": main_r["append_us"], "paged_attn_partition": main_r["partition_us"],
+                       "paged_attn_merge": main_r["merge_us"]},
+        "roofline": {
+            "kernel": "paged_attn_partition_kernel<128>",
+            "bound": "hbm",
+            "achieved": main_r["partition_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": main_r["partition_gbs"] / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "traffic_note": why,
+            "alg_bytes_per_launch": main_r["partition_alg_bytes"],
+        },
+        "cpu_baseline": cpu,
+        "parity_sample_max_abs": parity,
+        **extra_runs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def S_batch(shape):
+    return len(shape.fixed_ctx) if shape.fixed_ctx else shape.batch
+
+
+if __name__ == "__main__":
+    main()

@@ -330,3 +330,83 @@ class Allocator:
     def pkv_seq_release(self, table: np.ndarray, n_blocks: int):
         _check(lib.pkv_seq_release(self._h, _i32_host(table, "table"), int(n_blocks)),
                "pkv_seq_release")
+
+
+# ---------------------------------------------------------------------------
+# pre-marshalled calls for loops that issue the same call many times
+
+class PreparedCall:
+    """One C-ABI call whose arguments were checked and marshalled once.
+
+    Built by prepare_*; calling it re-issues the C function with the same
+    pointers (the tensors must stay alive and keep their storage), which
+    removes the per-call Python checks from a step loop. Raises PkvError on
+    a non-OK status like the plain wrappers."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name, args, keep=()):
+        self.name = name
+        self.fn = getattr(lib, name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != PKV_OK:
+            raise PkvError(st, self.name)
+
+
+def prepare_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, err_flag=None,
+                      stream=None):
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(k_new, "k_new", torch.bfloat16, 3)
+    _dev(v_new, "v_new", torch.bfloat16, 3)
+    num_seqs = k_new.shape[0]
+    if tuple(k_new.shape) != (num_seqs, n_kv, d) or tuple(v_new.shape) != (num_seqs, n_kv, d):
+        raise ValueError("k_new / v_new: expected [num_seqs, n_kv, head_dim]")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens: first dim must be num_seqs")
+    args = (_dev(k_pool, "k_pool", torch.bfloat16), _dev(v_pool, "v_pool", torch.bfloat16),
+            _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16), bt, cl,
+            num_seqs, block_tables.shape[1], nb, n_kv, d, _flag(err_flag), _stream(stream))
+    return PreparedCall("pkv_kv_append", args,
+                        (k_pool, v_pool, k_new, v_new, block_tables, context_lens, err_flag))
+
+
+def _prepare_decode(name, out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                    max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                    stream=None):
+    args, ws = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                            max_context_len, partition_tokens, workspace, err_flag, stream)
+    return PreparedCall(name, args,
+                        (out, q, k_pool, v_pool, block_tables, context_lens, ws, err_flag))
+
+
+def prepare_paged_attn_decode(*a, **k):
+    return _prepare_decode("pkv_paged_attn_decode", *a, **k)
+
+
+def prepare_paged_attn_partition(*a, **k):
+    """The partition kernel alone; pass the same workspace to
+    prepare_paged_attn_merge (call.keep[6] is the workspace used)."""
+    return _prepare_decode("pkv_paged_attn_partition", *a, **k)
+
+
+def prepare_paged_attn_merge(*a, **k):
+    return _prepare_decode("pkv_paged_attn_merge", *a, **k)
+
+
+def prepare_copy_blocks(k_pool, v_pool, src, dst, err_flag=None, stream=None):
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    s = _dev(src, "src", torch.int32, 1)
+    t = _dev(dst, "dst", torch.int32, 1)
+    if src.shape != dst.shape:
+        raise ValueError("src / dst: same length required")
+    args = (_dev(k_pool, "k_pool", torch.bfloat16), _dev(v_pool, "v_pool", torch.bfloat16), s, t,
+            src.shape[0], nb, n_kv, d, _flag(err_flag), _stream(stream))
+    return PreparedCall("pkv_copy_blocks", args, (k_pool, v_pool, src, dst, err_flag))

@@ -1,0 +1,102 @@
+"""Parity at the full per-layer sizes of the four model shapes.
+
+One layer of each shape is built at its real size (batch, heads, head
+size, context distribution, shared prefix), pools drawn on the GPU with a
+seeded generator and copied back for the oracle. The library runs append +
+decode in the launch configuration the benchmark times (library-chosen
+partition size, max_context_len = largest context + the benchmark's 23
+extra decode steps). Checked:
+  * kv_append: the whole K and V pools after the append, bit for bit,
+    against the oracle's append on the pre-append bytes;
+  * decode: sampled (sequence, query head) rows, each recomputed by the
+    oracle one by one in float64, max-abs error <= 1e-3; the sample always
+    includes the shortest and the longest sequence and, for the shared
+    prefix, a sequence whose written block is a copy of a prefix block.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workload as w
+from gpu_util import TOL, max_abs, to_dev_i32, to_host_u16
+
+pytestmark = pytest.mark.gpu
+
+BENCH_EXTRA_STEPS = 23
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_468_amd as lib
+    return lib
+
+
+def _one_layer(shape):
+    return w.Shape(shape.name, 1, shape.n_q, shape.n_kv, shape.d, shape.batch, shape.ctx_lo,
+                   shape.ctx_hi, prefix_tokens=shape.prefix_tokens)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_layer(pkv, orc, cfg):
+    import torch
+    shape = _one_layer(w.CONFIGS[cfg])
+    seed = 40 + cfg
+    t = w.build_tables(shape, seed, share=True)
+    ks, vs = w.pool_shapes(t.num_blocks, shape.n_kv, shape.d)
+    print(f"config {cfg}: {t.num_blocks} blocks, {len(t.copies)} prefix copies", flush=True)
+    k_pool = w.device_normal_bf16_(torch.empty(ks, dtype=torch.bfloat16, device="cuda"), seed * 10 + 1)
+    v_pool = w.device_normal_bf16_(torch.empty(vs, dtype=torch.bfloat16, device="cuda"), seed * 10 + 2)
+    if len(t.copies):
+        dst = torch.from_numpy(t.copies[:, 0].astype(np.int64)).cuda()
+        src = torch.from_numpy(t.copies[:, 1].astype(np.int64)).cuda()
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]
+    B = len(t.context_lens)
+    g = w.rng(seed, 3)
+    q_h = w.normal_bf16(g, (B, shape.n_q, shape.d))
+    kn_h = w.normal_bf16(g, (B, shape.n_kv, shape.d))
+    vn_h = w.normal_bf16(g, (B, shape.n_kv, shape.d))
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k_new, v_new = dev(q_h), dev(kn_h), dev(vn_h)
+    bt = to_dev_i32(t.block_tables)
+    cl = to_dev_i32(t.context_lens)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((B, shape.n_q, shape.d), float("nan"), dtype=torch.float32, device="cuda")
+    max_ctx = int(t.context_lens.max()) + BENCH_EXTRA_STEPS
+    torch.cuda.synchronize()
+    k_ref, v_ref = to_host_u16(k_pool), to_host_u16(v_pool)
+
+    pkv.pkv_kv_append(k_pool, v_pool, k_new, v_new, bt, cl, err_flag=err)
+    pkv.pkv_paged_attn_decode(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    part = pkv.pkv_default_partition_tokens(B, shape.n_q, shape.n_kv, shape.d, max_ctx)
+    print(f"config {cfg}: partition {part} tokens, {math.ceil(max_ctx / part)} partitions", flush=True)
+
+    assert orc.kv_append(k_ref, v_ref, kn_h, vn_h, t.block_tables, t.context_lens) == 0
+    assert np.array_equal(to_host_u16(k_pool), k_ref), "kv_append K pool differs"
+    assert np.array_equal(to_host_u16(v_pool), v_ref), "kv_append V pool differs"
+
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    cl_h = t.context_lens
+    seqs = [int(np.argmin(cl_h)), int(np.argmax(cl_h))]
+    if len(t.copies):
+        short = np.nonzero(cl_h <= shape.prefix_tokens)[0]
+        if len(short):
+            seqs.append(int(short[0]))
+    pick = w.rng(seed, 9)
+    rows = [(s, int(pick.integers(shape.n_q))) for s in seqs]
+    rows += [(int(pick.integers(B)), int(pick.integers(shape.n_q))) for _ in range(24)]
+    G = shape.n_q // shape.n_kv
+    worst = 0.0
+    for s, j in rows:
+        want, rc = orc.decode_row(q_h[s, j], k_ref, v_ref, t.block_tables[s], int(cl_h[s]),
+                                  shape.n_kv, j // G, shape.scale)
+        assert rc == 0
+        worst = max(worst, max_abs(got[s, j], want))
+    print(f"config {cfg}: {len(rows)} sampled rows, max-abs {worst:.2e}")
+    assert worst <= TOL
