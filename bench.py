@@ -141,7 +141,8 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens):
         for l in range(L):
             pkv.pkv_copy_blocks(S.k_pool[l], S.v_pool[l], src, dst, err_flag=S.err)
 
-    S.partition = partition_tokens or pkv.pkv_default_partition_tokens(B, n_q, n_kv, d, S.max_ctx)
+    S.partition = partition_tokens
+    S.split_waves = pkv.pkv_decode_split_waves(B, n_q, n_kv, d, S.max_ctx) if partition_tokens == 0 else 0
     ws_bytes = pkv.pkv_decode_workspace_bytes(B, n_q, n_kv, d, S.max_ctx, S.partition)
     S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     S.calls = []
@@ -257,6 +258,7 @@ def run(pkv, torch, S, steps, warmup):
         "partition_alg_bytes": part_bytes,
         "partition_gbs": part_bytes / (part_us * 1e-6) / 1e9,
         "partition_tokens": S.partition,
+        "split_waves": S.split_waves,
         "num_blocks_per_layer": S.num_blocks,
         "cow_copies": S.n_cow,
         "gpu_event_ms_total": gpu_ms,
@@ -347,7 +349,7 @@ def main():
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")
     S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens)
-    log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition}, cow {S.n_cow}; timing")
+    log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
     main_r = run(pkv, torch, S, args.steps, args.warmup)
     log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step, {main_r['kv_gbs']:.0f} GB/s, "
         f"partition {main_r['partition_us']:.1f} us = {main_r['partition_gbs']:.0f} GB/s")
@@ -408,6 +410,7 @@ def main():
             "context": ([int(c) for c in shape.fixed_ctx] if shape.fixed_ctx else [shape.ctx_lo, shape.ctx_hi]),
             "shared_prefix_tokens": shape.prefix_tokens if share_main else 0,
             "seed": args.seed, "partition_tokens": main_r["partition_tokens"],
+            "split_waves": main_r["split_waves"],
         },
         "steps_per_s": main_r["steps_per_s"],
         "seq_tokens_per_s": main_r["seq_tokens_per_s"],

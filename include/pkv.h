@@ -147,15 +147,21 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
 /* ------------------------------------------------------------------------
  * paged_attn_decode: the attention above, for every sequence and query head.
  *
- * The context of each sequence is cut into partitions of partition_tokens
- * tokens (a multiple of 16 in [16, 1024]; 0 = library default). One
- * wavefront handles one (sequence, KV head, partition) and serves up to 16
- * query heads of that KV head from the same K/V tiles, so each KV byte is
- * read once for G <= 16 (larger groups take ceil(G/16) passes). If more than
- * one partition is needed (max_context_len > partition_tokens) a second
- * kernel merges the partial (max, sum, accumulator) triples; the workspace
- * holds them. Exactly ceil(max_context_len/partition_tokens) partitions are
- * provisioned per (sequence, head).
+ * Work split. A unit is one (sequence, KV head, group of up to 16 of its
+ * query heads); one wavefront serves all query heads of the group from the
+ * same K/V tiles, so each KV byte is read once for G <= 16 (larger groups
+ * take ceil(G/16) passes). A wavefront processes a run of consecutive
+ * 16-token tiles of a unit:
+ *   partition_tokens == 0 (default): balanced split. All tiles of the call,
+ *     ordered by (KV head, group, sequence, tile), are cut into
+ *     pkv_decode_split_waves(...) equal ranges, one per wavefront, so every
+ *     wavefront streams the same bytes whatever the context lengths. The
+ *     split depends on the context lengths only.
+ *   partition_tokens = P (a multiple of 16 in [16, 1024]): fixed
+ *     partitions, one wavefront per P tokens of each unit.
+ * A unit processed by one wavefront is written to out directly; otherwise
+ * each wavefront leaves a partial (reference max, sum, accumulator) in the
+ * workspace and a second kernel merges them (log-sum-exp rescaling).
  *
  * out        : device fp32 [num_seqs][n_q_heads][head_dim], written fully.
  * q          : device bf16 [num_seqs][n_q_heads][head_dim].
@@ -168,7 +174,14 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  *              bytes (may be NULL when that is 0); caller-owned.
  * Device errors: ctx_s outside [1, max_context_len], or a needed table
  * entry outside [0, num_blocks): out[s,:,:] becomes NaN for that sequence
- * and the PKV_DEVERR bit is set. num_seqs == 0 is a no-op. */
+ * and the PKV_DEVERR bit is set. num_seqs == 0 is a no-op. Host-side
+ * limits: num_seqs * ceil(max_context_len / 16) < 2^30.
+ *
+ * Workspace bytes: 4 * (head_dim + 2) * min(G, 16) * slots, with slots =
+ * units * ceil(max_context_len / P) for fixed partitions (0 if that is one
+ * partition) and units + min(8192, ceil(units * ceil(max_context_len/16) / 16))
+ * for the balanced split; units = num_seqs * n_kv_heads * ceil(G / 16).
+ * The balanced split needs no zeroing or other preparation of it. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim,
                                   int32_t max_context_len,
@@ -184,11 +197,11 @@ int pkv_paged_attn_decode(float* out, const void* q, const void* k_pool,
                           int32_t* err_flag, void* stream);
 /* The two kernels of pkv_paged_attn_decode as separate calls, with the
  * same arguments and checks; calling partition then merge on one stream is
- * exactly pkv_paged_attn_decode. pkv_paged_attn_partition writes out
- * directly when one partition covers max_context_len, else the partial
- * (max, sum, accumulator) triples into the workspace; pkv_paged_attn_merge
- * combines them into out and is a no-op in the single-partition case.
- * Separate calls let a caller time or overlap the two kernels. */
+ * exactly pkv_paged_attn_decode. pkv_paged_attn_partition writes the units
+ * one wavefront covers to out, and the partials of the others into the
+ * workspace; pkv_paged_attn_merge combines those into out and writes the
+ * NaN rows of sequences with an invalid context length. Separate calls let
+ * a caller time the two kernels. */
 int pkv_paged_attn_partition(float* out, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_tables,
                              const int32_t* context_lens, int32_t num_seqs,
@@ -207,12 +220,14 @@ int pkv_paged_attn_merge(float* out, const void* q, const void* k_pool,
                          int32_t max_context_len, int32_t partition_tokens,
                          void* workspace, size_t workspace_bytes,
                          int32_t* err_flag, void* stream);
-/* The partition size the library uses when partition_tokens == 0: the
- * largest of 512, 256, 128, 64 tokens that still gives at least 8192
- * wavefronts for num_seqs * n_kv_heads * ceil(G/16) * ceil(max_ctx / P). */
-int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t n_q_heads,
-                                     int32_t n_kv_heads, int32_t head_dim,
-                                     int32_t max_context_len);
+/* Wavefronts of the balanced split on the current device for this shape:
+ * the number resident at once on the device (compute units x resident
+ * wavefronts of the kernel), at most 8192, and at most one per 16 tiles of
+ * units * ceil(max_context_len / 16). Queries the HIP runtime; returns
+ * PKV_EINVAL / PKV_EUNSUPPORTED for bad shapes, PKV_EHIP without a device. */
+int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               int32_t max_context_len);
 
 /* ------------------------------------------------------------------------
  * copy_blocks: copy-on-write support ([DSS] "Paged attention": when

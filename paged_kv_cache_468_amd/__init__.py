@@ -48,7 +48,7 @@ SIGNATURES = {
                                                 _vp]),
     "pkv_paged_attn_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
-    "pkv_default_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
@@ -189,9 +189,11 @@ def pkv_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_co
                                               max_context_len, partition_tokens))
 
 
-def pkv_default_partition_tokens(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len):
-    return int(lib.pkv_default_partition_tokens(num_seqs, n_q_heads, n_kv_heads, head_dim,
-                                                max_context_len))
+def pkv_decode_split_waves(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len):
+    """Wavefronts of the balanced split (partition_tokens == 0) on the
+    current device; negative PKV_E* codes pass through."""
+    return int(lib.pkv_decode_split_waves(num_seqs, n_q_heads, n_kv_heads, head_dim,
+                                          max_context_len))
 
 
 def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,

@@ -1,9 +1,9 @@
 // Decode-phase attention over a paged KV cache, for gfx950 (MI355X).
 //
-// What is computed (see include/pkv.h for the layouts): for every sequence
-// s and query head j, the softmax-weighted sum of the values of every cached
-// token of s, weights from the scaled dot products of q[s, j] with the keys,
-// keys and values reached through the sequence's block table. Sources:
+// What is computed (include/pkv.h has the layouts): for every sequence s and
+// query head j, the softmax-weighted sum of the values of every cached token
+// of s, weights from the scaled dot products of q[s, j] with the keys, keys
+// and values reached through the sequence's block table. Sources:
 // "Module 23: Serving", 23.2 (decode reads the whole KV cache for one new
 // token per sequence) and 23.4 (16-token blocks behind a per-sequence
 // table); "Scaling LLM serving", "The KV cache" (grouped-query heads) and
@@ -13,27 +13,46 @@
 // (logical to physical block indirection).
 //
 // Work decomposition
-//   One wavefront = one (KV head h, query group, sequence s, partition).
-//   A partition is P consecutive tokens (P a multiple of 16); the wave walks
-//   its 16-token blocks. For each block it loads the K tile (16 x D bf16,
-//   token-major) and the V tile (D x 16 bf16, dim-major), both contiguous,
-//   and serves all (up to 16) query rows of the group from them, so every
-//   KV byte is read from HBM once.
+//   A unit is one (KV head h, query group qg, sequence s): the <= 16 query
+//   rows of head h's group (rows qg*16 .. qg*16+15) over the ceil(ctx/16)
+//   tiles of s. A segment is a run of consecutive tiles of one unit, and one
+//   wavefront processes a segment: for each 16-token block it loads the K
+//   tile (16 x D bf16, token-major) and the V tile (D x 16 bf16, dim-major),
+//   both contiguous, and serves all query rows of the group from them, so
+//   every KV byte is read from HBM once.
 //
-//   Scores:  S^T[t][g] = sum_k K[t][k] * Q[g][k]    16x16x32 bf16 MFMA, D/32 of them
-//   Values:  O^T[n][g] += sum_t V^T[n][t] * P^T[t][g] 16x16x16 bf16 MFMA, 2 per 16 dims
-//   The probabilities P (fp32) are split as P = hi + lo with hi, lo bf16, so
-//   the bf16 products keep ~16 bits of P; both halves go through the MFMA.
+//   Balanced split (partition_tokens == 0): all tiles of the launch, in
+//   (KV head, query group, sequence, tile) order, are cut into n_waves equal
+//   ranges, one per wave; a wave walks its range, which may cross unit
+//   boundaries, and processes one segment per unit it touches. Every wave
+//   streams the same number of bytes, whatever the mix of context lengths.
+//   The split depends only on the context lengths, never on block ids.
+//   Fixed partitions (partition_tokens = P > 0): one wave per (unit,
+//   partition of P tokens).
 //
-//   Lane (c = lane % 16, r = lane / 16) holds, after the score MFMA, the
-//   scores of tokens 4r..4r+3 for query row g = c. That is exactly the
-//   B-operand layout of the value MFMA, and the value MFMA's result puts
-//   dims 4r..4r+3 (+16m) of row g = c in the same lane, so the online
-//   softmax (running max m, running sum l, rescale of the accumulator) needs
-//   no data movement beyond a max over the four lanes of one column.
+//   A segment that covers its whole unit writes out directly. Otherwise it
+//   writes a partial (reference max m, sum l, unnormalised accumulator) to a
+//   workspace slot and the merge kernel combines the slots of the unit.
+//   Slot of a segment: balanced, wave + unit (unique: along the tile order
+//   both indices only grow, and each new segment starts a new wave or a new
+//   unit); fixed, unit * p_max + partition.
 //
-//   Softmax runs in the base-2 domain: x = score * scale * log2(e), weights
-//   exp2(x - m). The merge kernel uses the same convention.
+//   Per tile, with lane (c = lane % 16, r = lane / 16):
+//   Scores   S^T[t][g] = sum_k K[t][k] Q[g][k]   v_mfma_f32_16x16x32_bf16, D/32 of them;
+//            lane (c, r) then holds tokens 4r..4r+3 of query row g = c.
+//   Values   O^T[n][g] += sum_t V^T[n][t] P^T[t][g]  one v_mfma_f32_16x16x32_bf16
+//            per 16 dims: P (fp32) is split into bf16 hi + lo, and the MFMA's
+//            32-long k dimension holds (token, hi) and (token, lo) pairs, the
+//            V operand repeating each token's value for both, so the product
+//            carries ~16 bits of P. Lane (c, r) holds dims 4r..4r+3 (+16m) of
+//            row c: the same lanes as its scores, so the online softmax needs
+//            no data movement beyond a max over the four lanes of a column.
+//   Softmax  base 2: x = score * scale * log2(e), weights 2^(x - m). m is a
+//            reference maximum: it is raised (and l, acc rescaled) only when
+//            some row's tile maximum exceeds it by more than 8, so weights
+//            stay below 2^8 and most tiles skip the rescale. Any reference
+//            gives the same softmax, since it cancels between sum and
+//            accumulator; the merge kernel uses the same convention.
 //
 //   Grid: workgroups of 4 waves; the workgroup index is remapped so that
 //   consecutive work (same KV head, neighbouring sequences) lands on the
@@ -50,10 +69,15 @@ namespace pkv {
 typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
-constexpr int kWaves = 4;          // waves per workgroup
-constexpr int kXcds = 8;           // XCDs of an MI355X
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kXcds = 8;             // XCDs of an MI355X
+constexpr int kMaxSplitWaves = 8192; // cap of the balanced split's wave count
+constexpr int kMinTilesPerWave = 16; // balanced split: at least this much work per wave
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
 struct DecodeArgs {
   float* out;
@@ -62,13 +86,17 @@ struct DecodeArgs {
   const uint16_t* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_ml;      // [B][n_q][p_max][2]  (m in log2 units, l)
-  float* ws_acc;     // [B][n_q][p_max][D]  unnormalised accumulators
+  float* ws_ml;      // [slots][rows][2]  (reference max in log2 units, sum)
+  float* ws_acc;     // [slots][rows][D]  unnormalised accumulators
   int32_t* err_flag;
   int num_seqs, max_blocks, num_blocks;
-  int n_q, n_kv, group, n_qgroups;
-  int max_ctx, part_tokens, p_max;
-  int total_units, wg_per_xcd;
+  int n_q, n_kv, group, n_qgroups, rows;  // rows = min(group, 16) per slot
+  int max_ctx;
+  int part_tokens;   // 0: balanced split
+  int p_max;         // fixed partitions: partitions per unit
+  int n_units;       // n_kv * n_qgroups * num_seqs
+  int n_waves;       // waves launched by the partition kernel
+  int wg_per_xcd;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -85,8 +113,29 @@ __device__ inline float wave_sum_across_rows(float x) {
   return x;
 }
 
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ inline int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 __device__ inline void flag_error(int32_t* err_flag, int bit) {
   if (err_flag) atomicOr(err_flag, bit);
+}
+
+// Tiles of a sequence for the work split: 0 for an invalid context length
+// (the merge kernel reports those and writes NaN rows).
+__device__ inline int seq_tiles(int ctx, int max_ctx) {
+  return (ctx >= 1 && ctx <= max_ctx) ? (ctx + 15) >> 4 : 0;
 }
 
 // Round-to-nearest-even float -> bf16 bits (finite inputs).
@@ -95,81 +144,88 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void paged_attn_partition_kernel(DecodeArgs a) {
-  constexpr int KM = D / 32;   // score MFMAs per tile (k = 32 dims each)
-  constexpr int VM = D / 16;   // value MFMA column chunks (16 dims each)
+__device__ inline int logical_workgroup(const DecodeArgs& a) {
+  return (blockIdx.x % kXcds) * a.wg_per_xcd + blockIdx.x / kXcds;
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = lane & 15;     // query row in the group / token row of K
-  const int r = lane >> 4;     // quad: tokens 4r..4r+3 after the score MFMA
-
-  const int logical_wg = (blockIdx.x % kXcds) * a.wg_per_xcd + blockIdx.x / kXcds;
-  const int unit = logical_wg * kWaves + wave;
-  if (unit >= a.total_units) return;
-  const int part = unit % a.p_max;
-  const int rest = unit / a.p_max;
-  const int s = rest % a.num_seqs;
-  const int hq = rest / a.num_seqs;
-  const int h = hq / a.n_qgroups;
-  const int qg = hq % a.n_qgroups;
-
-  const int g_in_group = qg * 16 + c;
-  const bool row_valid = g_in_group < a.group;
-  const int j = h * a.group + g_in_group;           // query head of this lane's row
-  const bool direct = a.p_max == 1;
-
-  const int ctx = a.context_lens[s];
-  if (ctx < 1 || ctx > a.max_ctx) {
-    if (part == 0) {
-      if (hq == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
-      if (direct && row_valid) {
-        float* o = a.out + ((int64_t)s * a.n_q + j) * D;
-        for (int m = 0; m < VM; ++m)
-          *(f32x4_t*)(o + 16 * m + 4 * r) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""),
-                                                   __builtin_nanf(""), __builtin_nanf("")};
-      }
-    }
-    return;   // multi-partition: the merge kernel writes NaN for this sequence
+// Sum over all sequences of seq_tiles (identical in every lane).
+__device__ inline int total_seq_tiles(const DecodeArgs& a, int lane) {
+  int sum = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int i = base + lane;
+    sum += wave_sum(i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0);
   }
-  const int t0 = part * a.part_tokens;
-  if (t0 >= ctx) return;
-  const int t1 = min(t0 + a.part_tokens, ctx);
-  const int b0 = t0 >> 4;
-  const int nb = ((t1 + 15) >> 4) - b0;            // <= 64 (part_tokens <= 1024)
+  return sum;
+}
 
-  // Physical block ids of this partition: lane i holds entry b0 + i.
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks + b0;
-  const int my_id = lane < nb ? bt_row[lane] : 0;
-  const bool bad_id = lane < nb && (my_id < 0 || my_id >= a.num_blocks);
-  const bool any_bad = __ballot(bad_id) != 0;
+// The sequence holding tile r (0 <= r < total) of the per-unit-row tile
+// order, and the number of tiles of the sequences before it.
+__device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_out,
+                                   int& before_out) {
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int i = base + lane;
+    const int n = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0;
+    const int incl = wave_inclusive_scan(n, lane) + carry;
+    const uint64_t hit = __ballot(i < a.num_seqs && incl > r);
+    if (hit) {
+      const int ln = __builtin_ctzll(hit);
+      s_out = base + ln;
+      before_out = __builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(n, ln);
+      return;
+    }
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  s_out = a.num_seqs;   // not reached for r < total
+  before_out = carry;
+}
 
-  f32x4_t acc[VM];
+// One segment: tiles [ta, tb) of unit (h, qg, s). Leaves the running
+// reference max m (log2 units, per query row c, identical in the 4 lanes of
+// a column), the column's partial sum l (this lane's tokens only) and the
+// accumulator acc (dims 16m + 4r .. +3 of row c). Returns false if a block
+// id was out of range (nothing else is then meaningful).
+template <int D>
+__device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h, int j_row,
+                                       bool row_valid, int ctx, int ta, int tb, f32x4_t* acc,
+                                       float& m_run, float& l_run) {
+  constexpr int KM = D / 32;   // score MFMAs per tile (k = 32 dims each)
+  constexpr int VM = D / 16;   // value MFMAs per tile (16 dims each)
+  const int c = lane & 15;
+  const int r = lane >> 4;
+
 #pragma unroll
   for (int m = 0; m < VM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  m_run = -__builtin_inff();
+  l_run = 0.f;
 
-  if (!any_bad) {
-    // Q as the B operand of the score MFMA: lane (c, r) holds row g = c,
-    // dims 32m + 8r .. +8. Rows past the group are zero.
-    bf16x8_t qv[KM];
-    const uint16_t* q_row = a.q + ((int64_t)s * a.n_q + (row_valid ? j : 0)) * D;
+  // Q as the B operand of the score MFMA: lane (c, r) holds row c, dims
+  // 32m + 8r .. +8. Rows past the group are zero.
+  bf16x8_t qv[KM];
+  const uint16_t* q_row = a.q + ((int64_t)s * a.n_q + (row_valid ? j_row : 0)) * D;
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
-      qv[m] = row_valid ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+  for (int m = 0; m < KM; ++m) {
+    const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
+    qv[m] = row_valid ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
 
-    const int64_t tile_elems = 16 * D;
-    const int64_t head_off = (int64_t)h * tile_elems;
-    const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
-    const int k_lane_off = c * D + 8 * r;          // + 32m
-    const int v_lane_off = c * 16 + 4 * r;         // + 256m (16 dims x 16 tokens)
+  const int64_t tile_elems = 16 * D;
+  const int64_t head_off = (int64_t)h * tile_elems;
+  const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
+  const int k_lane_off = c * D + 8 * r;          // + 32m
+  const int v_lane_off = c * 16 + 4 * r;         // + 256m (16 dims x 16 tokens)
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  const int last_tile = (ctx - 1) >> 4;
+  const int last_valid = ctx - last_tile * 16;   // tokens in the sequence's last tile
 
-    bf16x8_t kA[KM], kB[KM];
-    bf16x4_t vA[VM], vB[VM];
+  bf16x8_t kA[KM], kB[KM];
+  bf16x4_t vA[VM], vB[VM];
+
+  for (int cb = ta; cb < tb; cb += 64) {
+    const int nb = min(64, tb - cb);
+    // Physical block ids of this chunk: lane i holds entry cb + i.
+    const int my_id = lane < nb ? bt_row[cb + lane] : 0;
+    if (__ballot(lane < nb && (my_id < 0 || my_id >= a.num_blocks)) != 0) return false;
 
     auto load_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
       const int blk = __builtin_amdgcn_readlane(my_id, i);
@@ -190,9 +246,8 @@ __global__ __launch_bounds__(256) void paged_attn_partition_kernel(DecodeArgs a)
       float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = sc[e] * a.scale_log2;
-      const int tok0 = (b0 + i) * 16;
-      if (tok0 + 16 > ctx) {   // the sequence's last, partly filled block
-        const int valid = ctx - tok0 - 4 * r;      // tokens of this quad still inside
+      if (cb + i == last_tile && last_valid < 16) {   // the partly filled last block
+        const int valid = last_valid - 4 * r;         // tokens of this quad still inside
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (e >= valid) x[e] = -__builtin_inff();
@@ -201,42 +256,40 @@ __global__ __launch_bounds__(256) void paged_attn_partition_kernel(DecodeArgs a)
         const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int m = 0; m < VM; ++m) {
-          typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-          u32x2_t w = __builtin_bit_cast(u32x2_t, vr[m]);
-          w[0] &= keep0;
-          w[1] &= keep1;
-          vr[m] = __builtin_bit_cast(bf16x4_t, w);
+          u32x2_t wv = __builtin_bit_cast(u32x2_t, vr[m]);
+          wv[0] &= keep0;
+          wv[1] &= keep1;
+          vr[m] = __builtin_bit_cast(bf16x4_t, wv);
         }
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = wave_max_across_rows(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < VM; ++m) acc[m] *= alpha;
+      }
       float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
-      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        acc[m][0] *= alpha; acc[m][1] *= alpha; acc[m][2] *= alpha; acc[m][3] *= alpha;
-      }
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
       // P = hi + lo, both bf16: hi by truncation (exact remainder), lo rounded.
-      uint32_t pu[4], lo[4];
+      uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pu[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
-        lo[e] = bf16_rne_bits(p[e] - __uint_as_float(pu[e]));
+        hi[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
+        lo[e] = bf16_rne_bits(p[e] - __uint_as_float(hi[e]));
       }
-      typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-      u32x2_t hi2 = u32x2_t{(pu[0] >> 16) | pu[1], (pu[2] >> 16) | pu[3]};
-      u32x2_t lo2 = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-      const bf16x4_t phi = __builtin_bit_cast(bf16x4_t, hi2);
-      const bf16x4_t plo = __builtin_bit_cast(bf16x4_t, lo2);
+      const u32x4_t pw = u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
+                                 lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int m = 0; m < VM; ++m) {
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[m], phi, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[m], plo, acc[m], 0, 0, 0);
+        const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[m], 0, 0, 0);
       }
     };
 
@@ -251,59 +304,213 @@ __global__ __launch_bounds__(256) void paged_attn_partition_kernel(DecodeArgs a)
       compute_tile(i + 1, kB, vB);
     }
     if (i < nb) compute_tile(i, kA, vA);
-  } else if (lane == 0) {
-    flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
   }
+  return true;
+}
 
+// Write a finished segment: out directly when it covers its whole unit,
+// else a partial into its workspace slot. Rows past the group write nothing.
+template <int D>
+__device__ inline void finish_segment(const DecodeArgs& a, int lane, bool ok, bool whole,
+                                      int64_t slot, int s, int j_row, int g_in_slot,
+                                      bool row_valid, const f32x4_t* acc, float m_run,
+                                      float l_run) {
+  constexpr int VM = D / 16;
+  const int r = lane >> 4;
   const float l_tot = wave_sum_across_rows(l_run);
+  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
   if (!row_valid) return;
   const float nan = __builtin_nanf("");
-  if (direct) {
-    const float inv = any_bad ? nan : 1.0f / l_tot;
-    float* o = a.out + ((int64_t)s * a.n_q + j) * D + 4 * r;
+  if (whole) {
+    const float inv = ok ? 1.0f / l_tot : nan;
+    float* o = a.out + ((int64_t)s * a.n_q + j_row) * D + 4 * r;
 #pragma unroll
-    for (int m = 0; m < VM; ++m)
-      *(f32x4_t*)(o + 16 * m) = acc[m] * inv;
+    for (int m = 0; m < VM; ++m) *(f32x4_t*)(o + 16 * m) = acc[m] * inv;
   } else {
-    const int64_t slot = ((int64_t)s * a.n_q + j) * a.p_max + part;
+    const int64_t row = slot * a.rows + g_in_slot;
     if (r == 0) {
-      a.ws_ml[2 * slot] = any_bad ? nan : m_run;
-      a.ws_ml[2 * slot + 1] = any_bad ? nan : l_tot;
+      a.ws_ml[2 * row] = ok ? m_run : nan;
+      a.ws_ml[2 * row + 1] = ok ? l_tot : nan;
     }
-    float* w = a.ws_acc + slot * D + 4 * r;
+    float* w = a.ws_acc + row * D + 4 * r;
 #pragma unroll
     for (int m = 0; m < VM; ++m) *(f32x4_t*)(w + 16 * m) = acc[m];
   }
 }
 
-// Merge of the partitions of one (sequence, query head) row: with per
-// partition maxima m_p, sums l_p and accumulators a_p (all relative to
-// exp2(x - m_p)), out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p,
-// M = max_p m_p. One wave per row; lane i owns dims 2i, 2i+1 (D = 128) or i.
+// Fixed partitions: one wave per (unit, partition).
+template <int D>
+__global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
+  constexpr int VM = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int unit_part = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
+  if (unit_part >= a.n_units * a.p_max) return;
+  const int part = unit_part % a.p_max;
+  const int u = unit_part / a.p_max;
+  const int s = u % a.num_seqs;
+  const int hq = u / a.num_seqs;
+  const int h = hq / a.n_qgroups;
+  const int qg = hq % a.n_qgroups;
+  const int g = qg * 16 + c;
+  const bool row_valid = g < a.group;
+  const int j = h * a.group + g;
+
+  const int ctx = a.context_lens[s];
+  const int nt = seq_tiles(ctx, a.max_ctx);       // invalid: 0, reported by the merge
+  const int tiles_per_part = a.part_tokens >> 4;
+  const int ta = part * tiles_per_part;
+  if (ta >= nt) return;
+  const int tb = min(ta + tiles_per_part, nt);
+
+  f32x4_t acc[VM];
+  float m_run, l_run;
+  const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, ta, tb, acc, m_run, l_run);
+  finish_segment<D>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, s, j, c,
+                    row_valid, acc, m_run, l_run);
+}
+
+// Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
+// (head, group, sequence, tile) order, T = all tiles of the launch.
+template <int D>
+__global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) {
+  constexpr int VM = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
+  if (w >= a.n_waves) return;
+
+  const int per_row = total_seq_tiles(a, lane);   // tiles of one (head, group)
+  const int n_hq = a.n_kv * a.n_qgroups;
+  const int64_t total = (int64_t)n_hq * per_row;
+  int64_t cur = total * w / a.n_waves;
+  const int64_t end = total * (w + 1) / a.n_waves;
+  if (cur >= end) {
+    // An empty range (fewer tiles than waves). If it sits inside a unit,
+    // the merge of that unit counts this wave: leave a neutral partial
+    // (weight 2^-inf, sum 0, accumulator 0) in its slot.
+    if (cur < total) {
+      const int hq = (int)(cur / per_row);
+      int s, before;
+      locate_tile(a, lane, (int)(cur - (int64_t)hq * per_row), s, before);
+      if (s >= a.num_seqs) return;
+      const int g = (hq % a.n_qgroups) * 16 + c;
+      const int j = (hq / a.n_qgroups) * a.group + g;
+      f32x4_t zero[VM];
+#pragma unroll
+      for (int m = 0; m < VM; ++m) zero[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      finish_segment<D>(a, lane, true, false, (int64_t)w + hq * a.num_seqs + s, s, j, c,
+                        g < a.group, zero, -__builtin_inff(), 0.f);
+    }
+    return;
+  }
+
+  int hq = (int)(cur / per_row);
+  int s, before;
+  locate_tile(a, lane, (int)(cur - (int64_t)hq * per_row), s, before);
+  if (s >= a.num_seqs) return;   // unreachable for consistent context lengths
+  int pos = (int)(cur - (int64_t)hq * per_row) - before;   // tile within the unit
+  int ctx = a.context_lens[s];
+
+  while (true) {
+    const int nt = seq_tiles(ctx, a.max_ctx);
+    const int tb = (int)min((int64_t)nt, pos + (end - cur));
+    const int h = hq / a.n_qgroups;
+    const int qg = hq % a.n_qgroups;
+    const int g = qg * 16 + c;
+    const bool row_valid = g < a.group;
+    const int j = h * a.group + g;
+    const int u = hq * a.num_seqs + s;
+
+    f32x4_t acc[VM];
+    float m_run, l_run;
+    const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, pos, tb, acc, m_run, l_run);
+    finish_segment<D>(a, lane, ok, pos == 0 && tb == nt, (int64_t)w + u, s, j, c, row_valid,
+                      acc, m_run, l_run);
+    cur += tb - pos;
+    if (cur >= end) break;
+    // next unit with work: following sequence, or the next (head, group)
+    pos = 0;
+    do {
+      if (++s == a.num_seqs) {
+        s = 0;
+        if (++hq >= n_hq) return;   // unreachable for consistent context lengths
+      }
+      ctx = a.context_lens[s];
+    } while (seq_tiles(ctx, a.max_ctx) == 0);
+  }
+}
+
+// First wave and last wave (inclusive) of the balanced split that touch
+// tiles [t0, t1) of the launch order, t1 > t0.
+__device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int n_waves,
+                                      int& w0, int& w1) {
+  // wave of tile x: the largest w with floor(w*total/W) <= x
+  w0 = (int)(((t0 + 1) * n_waves - 1) / total);
+  w1 = (int)((t1 * n_waves - 1) / total);
+}
+
+// Merge of the partials of one (unit, query row): with reference maxima
+// m_p, sums l_p and accumulators a_p (all relative to 2^(x - m_p)),
+// out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// One wave per row; lane i owns dims PER*i .. PER*i + PER - 1.
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= a.num_seqs * a.n_q) return;
-  const int s = row / a.n_q;
-  const int ctx = a.context_lens[s];
-  float* o = a.out + (int64_t)row * D + lane * PER;
+  if (row >= a.n_units * a.rows) return;
+  const int u = row / a.rows;
+  const int g_in_slot = row % a.rows;
+  const int s = u % a.num_seqs;
+  const int hq = u / a.num_seqs;
+  const int h = hq / a.n_qgroups;
+  const int qg = hq % a.n_qgroups;
+  const int g = qg * 16 + g_in_slot;
+  if (g >= a.group) return;
+  const int j = h * a.group + g;
+  float* o = a.out + ((int64_t)s * a.n_q + j) * D + lane * PER;
   const float nan = __builtin_nanf("");
-  if (ctx < 1 || ctx > a.max_ctx) {
+
+  const int ctx = a.context_lens[s];
+  const int nt = seq_tiles(ctx, a.max_ctx);
+  if (nt == 0) {
+    if (g_in_slot == 0 && hq == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = nan;
     return;
   }
-  const int n_parts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  const float* ml = a.ws_ml + (int64_t)row * a.p_max * 2;
+  int64_t first;
+  int n;
+  if (a.part_tokens > 0) {
+    const int tiles_per_part = a.part_tokens >> 4;
+    n = (nt + tiles_per_part - 1) / tiles_per_part;
+    first = (int64_t)u * a.p_max;
+  } else {
+    const int per_row = total_seq_tiles(a, lane);
+    int before = 0;
+    for (int base = 0; base < s; base += 64) {   // tiles of the sequences before s
+      const int i = base + lane;
+      before += wave_sum(i < s ? seq_tiles(a.context_lens[i], a.max_ctx) : 0);
+    }
+    const int64_t t0 = (int64_t)hq * per_row + before;
+    int w0, w1;
+    waves_of_range(t0, t0 + nt, (int64_t)(a.n_kv * a.n_qgroups) * per_row, a.n_waves, w0, w1);
+    n = w1 - w0 + 1;
+    first = (int64_t)w0 + u;
+  }
+  if (n <= 1) return;   // written directly by the partition kernel
+
+  const float* ml = a.ws_ml + (first * a.rows + g_in_slot) * 2;
+  const int64_t ml_stride = (int64_t)a.rows * 2;
   float mx = -__builtin_inff();
   bool bad = false;
-  for (int p = lane; p < n_parts; p += 64) {
-    const float mp = ml[2 * p];
+  for (int p = lane; p < n; p += 64) {
+    const float mp = ml[p * ml_stride];
     bad |= mp != mp;
     mx = fmaxf(mx, mp);
   }
+#pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (__ballot(bad) != 0) {
 #pragma unroll
@@ -311,52 +518,94 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     return;
   }
   float lsum = 0.f;
-  for (int p = lane; p < n_parts; p += 64)
-    lsum += ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - mx);
+  for (int p = lane; p < n; p += 64)
+    lsum += ml[p * ml_stride + 1] * __builtin_amdgcn_exp2f(ml[p * ml_stride] - mx);
+#pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+
   float res[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) res[e] = 0.f;
-  const float* acc = a.ws_acc + (int64_t)row * a.p_max * D + lane * PER;
-  for (int p = 0; p < n_parts; ++p) {
-    const float wgt = __builtin_amdgcn_exp2f(ml[2 * p] - mx);
+  const float* acc = a.ws_acc + (first * a.rows + g_in_slot) * D + lane * PER;
+  const int64_t acc_stride = (int64_t)a.rows * D;
+  int p = 0;
+  for (; p + 4 <= n; p += 4) {   // four independent loads in flight
+    float wg[4], v[4][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] += wgt * acc[(int64_t)p * D + e];
+    for (int k = 0; k < 4; ++k) {
+      wg[k] = __builtin_amdgcn_exp2f(ml[(p + k) * ml_stride] - mx);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = acc[(p + k) * acc_stride + e];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) res[e] += wg[k] * v[k][e];
+  }
+  for (; p < n; ++p) {
+    const float wg = __builtin_amdgcn_exp2f(ml[p * ml_stride] - mx);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) res[e] += wg * acc[p * acc_stride + e];
   }
   const float inv = 1.0f / lsum;
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = res[e] * inv;
 }
 
-int32_t default_partition_tokens(int num_seqs, int n_q, int n_kv, int max_ctx) {
+// ---------------------------------------------------------------------------
+// host side
+
+static int rows_per_slot(int n_q, int n_kv) { return (n_q / n_kv) < 16 ? (n_q / n_kv) : 16; }
+
+static int64_t n_units_of(int num_seqs, int n_q, int n_kv) {
   const int64_t qgroups = (n_q / n_kv + 15) / 16;
-  int p = 512;
-  while (p > 64 && (int64_t)num_seqs * n_kv * qgroups * ((max_ctx + p - 1) / p) < 8192) p >>= 1;
-  return p;
+  return (int64_t)n_kv * qgroups * num_seqs;
 }
 
-static int resolve_partition(int partition_tokens, int num_seqs, int n_q, int n_kv, int max_ctx) {
-  if (partition_tokens == 0) return default_partition_tokens(num_seqs, n_q, n_kv, max_ctx);
-  return partition_tokens;
+// Waves of the balanced split: at most what the device holds resident at
+// once (so every wave runs concurrently), at most kMaxSplitWaves, and no
+// more than leaves kMinTilesPerWave tiles of the upper bound per wave.
+static int64_t split_wave_cap(int num_seqs, int n_q, int n_kv, int max_ctx) {
+  const int64_t tiles_ub = n_units_of(num_seqs, n_q, n_kv) * ((max_ctx + 15) / 16);
+  int64_t w = (tiles_ub + kMinTilesPerWave - 1) / kMinTilesPerWave;
+  if (w > kMaxSplitWaves) w = kMaxSplitWaves;
+  return w < 1 ? 1 : w;
 }
 
-size_t workspace_bytes(int num_seqs, int n_q, int n_kv, int d, int max_ctx, int part) {
-  const int p_max = (max_ctx + part - 1) / part;
-  if (p_max <= 1) return 0;
-  return (size_t)num_seqs * n_q * p_max * (2 + d) * sizeof(float);
+static int resident_waves(int head_dim) {
+  static int cache[2][64];   // [head_dim == 128][device]
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int& slot = cache[head_dim == 128][dev];
+  if (slot > 0) return slot;
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  hipError_t e = head_dim == 128
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<128>, 256, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<64>, 256, 0);
+  if (e != hipSuccess || blocks < 1 || cus < 1) return -1;
+  slot = cus * blocks * kWaves;
+  return slot;
+}
+
+static size_t workspace_bytes(int num_seqs, int n_q, int n_kv, int d, int max_ctx, int part) {
+  const int64_t units = n_units_of(num_seqs, n_q, n_kv);
+  int64_t slots;
+  if (part > 0) {
+    const int p_max = (max_ctx + part - 1) / part;
+    if (p_max <= 1) return 0;
+    slots = units * p_max;
+  } else {
+    slots = split_wave_cap(num_seqs, n_q, n_kv, max_ctx) + units;
+  }
+  return (size_t)slots * rows_per_slot(n_q, n_kv) * (2 + d) * sizeof(float);
 }
 
 }  // namespace pkv
 
 using namespace pkv;
 
-extern "C" int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t n_q_heads,
-                                                int32_t n_kv_heads, int32_t head_dim,
-                                                int32_t max_context_len) {
-  (void)head_dim;
-  if (num_seqs <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || max_context_len <= 0) return 512;
-  return default_partition_tokens(num_seqs, n_q_heads, n_kv_heads, max_context_len);
-}
+static bool valid_partition_arg(int32_t p) { return p >= 0 && p % 16 == 0 && p <= 1024; }
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                              int32_t n_kv_heads, int32_t head_dim,
@@ -364,9 +613,21 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads
                                              int32_t partition_tokens) {
   if (num_seqs <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
     return 0;
-  if (partition_tokens < 0 || partition_tokens % 16 != 0 || partition_tokens > 1024) return 0;
-  const int part = resolve_partition(partition_tokens, num_seqs, n_q_heads, n_kv_heads, max_context_len);
-  return workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len, part);
+  if (n_q_heads % n_kv_heads != 0 || !valid_partition_arg(partition_tokens)) return 0;
+  return workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
+                         partition_tokens);
+}
+
+extern "C" int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_context_len <= 0 ||
+      n_q_heads % n_kv_heads != 0)
+    return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  const int res = resident_waves(head_dim);
+  if (res < 1) return PKV_EHIP;
+  const int64_t cap = split_wave_cap(num_seqs, n_q_heads, n_kv_heads, max_context_len);
+  return (int32_t)(res < cap ? res : cap);
 }
 
 // Host-side checks and launch geometry shared by the three entry points.
@@ -382,8 +643,7 @@ static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, 
   if (n_q_heads % n_kv_heads != 0) return PKV_EINVAL;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   if ((int64_t)max_context_len > 16 * (int64_t)max_blocks_per_seq) return PKV_EINVAL;
-  if (partition_tokens < 0 || partition_tokens % 16 != 0 || partition_tokens > 1024)
-    return PKV_EINVAL;
+  if (!valid_partition_arg(partition_tokens)) return PKV_EINVAL;
   if (!(scale == scale)) return PKV_EINVAL;
   if (num_seqs > 0 && (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens))
     return PKV_EINVAL;
@@ -402,39 +662,62 @@ static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, 
   a.n_kv = n_kv_heads;
   a.group = n_q_heads / n_kv_heads;
   a.n_qgroups = (a.group + 15) / 16;
+  a.rows = rows_per_slot(n_q_heads, n_kv_heads);
   a.max_ctx = max_context_len;
-  a.part_tokens = resolve_partition(partition_tokens, num_seqs, n_q_heads, n_kv_heads, max_context_len);
-  a.p_max = (max_context_len + a.part_tokens - 1) / a.part_tokens;
+  a.part_tokens = partition_tokens;
+  a.p_max = partition_tokens > 0 ? (max_context_len + partition_tokens - 1) / partition_tokens : 0;
   a.scale_log2 = scale * kLog2e;
   head_dim_out = head_dim;
 
-  const size_t need = workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len, a.part_tokens);
-  if (num_seqs > 0 && need > 0 && (workspace == nullptr || workspace_bytes_given < need))
-    return PKV_EWORKSPACE;
-  const int64_t rows_part = (int64_t)num_seqs * n_q_heads * a.p_max;
-  a.ws_ml = (float*)workspace;
-  a.ws_acc = need > 0 ? (float*)workspace + 2 * rows_part : nullptr;
+  const int64_t units = n_units_of(num_seqs, n_q_heads, n_kv_heads);
+  if (units > (int64_t)INT32_MAX / 64) return PKV_EINVAL;
+  // tiles of one (head, group) row of the split are counted in 32 bits
+  if ((int64_t)num_seqs * ((max_context_len + 15) / 16) > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
+  a.n_units = (int)units;
+  if (num_seqs == 0) return PKV_OK;
 
-  const int64_t units = (int64_t)n_kv_heads * a.n_qgroups * num_seqs * a.p_max;
-  if (units > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
-  a.total_units = (int)units;
-  const int64_t wgs = (units + kWaves - 1) / kWaves;
+  const size_t need = workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
+                                      partition_tokens);
+  if (need > 0 && (workspace == nullptr || workspace_bytes_given < need)) return PKV_EWORKSPACE;
+  const int64_t slots = need / (sizeof(float) * (2 + head_dim) * a.rows);
+  a.ws_ml = (float*)workspace;
+  a.ws_acc = need > 0 ? (float*)workspace + 2 * slots * a.rows : nullptr;
+
+  int64_t waves;
+  if (partition_tokens > 0) {
+    waves = units * a.p_max;
+    if (waves > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
+    a.n_waves = 0;
+  } else {
+    const int res = resident_waves(head_dim);
+    if (res < 1) return PKV_EHIP;
+    const int64_t cap = split_wave_cap(num_seqs, n_q_heads, n_kv_heads, max_context_len);
+    waves = res < cap ? res : cap;
+    a.n_waves = (int)waves;
+  }
+  const int64_t wgs = (waves + kWaves - 1) / kWaves;
   a.wg_per_xcd = (int)((wgs + kXcds - 1) / kXcds);
   return PKV_OK;
 }
 
 static int launch_partition(const DecodeArgs& a, int head_dim, hipStream_t st) {
   const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(paged_attn_partition_kernel<128>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(paged_attn_partition_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  if (a.part_tokens > 0) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(paged_attn_fixed_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(paged_attn_fixed_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  } else {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(paged_attn_balanced_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(paged_attn_balanced_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 static int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
-  if (a.p_max <= 1) return PKV_OK;
-  const unsigned mgrid = (unsigned)(((int64_t)a.num_seqs * a.n_q + kWaves - 1) / kWaves);
+  const unsigned mgrid = (unsigned)(((int64_t)a.n_units * a.rows + kWaves - 1) / kWaves);
   if (head_dim == 128)
     hipLaunchKernelGGL(paged_attn_merge_kernel<128>, dim3(mgrid), dim3(256), 0, st, a);
   else

@@ -3,8 +3,8 @@
 One layer of each shape is built at its real size (batch, heads, head
 size, context distribution, shared prefix), pools drawn on the GPU with a
 seeded generator and copied back for the oracle. The library runs append +
-decode in the launch configuration the benchmark times (library-chosen
-partition size, max_context_len = largest context + the benchmark's 23
+decode in the launch configuration the benchmark times (balanced split
+over the device's resident waves, max_context_len = largest context + the benchmark's 23
 extra decode steps). Checked:
   * kv_append: the whole K and V pools after the append, bit for bit,
     against the oracle's append on the pre-append bytes;
@@ -44,7 +44,9 @@ def test_full_size_layer(pkv, orc, cfg):
     import torch
     shape = _one_layer(w.CONFIGS[cfg])
     seed = 40 + cfg
-    t = w.build_tables(shape, seed, share=True)
+    cl0 = w.context_lengths(shape, seed)
+    max_ctx = int(cl0.max()) + BENCH_EXTRA_STEPS      # tables sized for the bench's growth
+    t = w.build_tables(shape, seed, share=True, max_blocks=math.ceil(max_ctx / w.BLOCK))
     ks, vs = w.pool_shapes(t.num_blocks, shape.n_kv, shape.d)
     print(f"config {cfg}: {t.num_blocks} blocks, {len(t.copies)} prefix copies", flush=True)
     k_pool = w.device_normal_bf16_(torch.empty(ks, dtype=torch.bfloat16, device="cuda"), seed * 10 + 1)
@@ -65,7 +67,6 @@ def test_full_size_layer(pkv, orc, cfg):
     cl = to_dev_i32(t.context_lens)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = torch.full((B, shape.n_q, shape.d), float("nan"), dtype=torch.float32, device="cuda")
-    max_ctx = int(t.context_lens.max()) + BENCH_EXTRA_STEPS
     torch.cuda.synchronize()
     k_ref, v_ref = to_host_u16(k_pool), to_host_u16(v_pool)
 
@@ -73,8 +74,8 @@ def test_full_size_layer(pkv, orc, cfg):
     pkv.pkv_paged_attn_decode(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx, err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    part = pkv.pkv_default_partition_tokens(B, shape.n_q, shape.n_kv, shape.d, max_ctx)
-    print(f"config {cfg}: partition {part} tokens, {math.ceil(max_ctx / part)} partitions", flush=True)
+    waves = pkv.pkv_decode_split_waves(B, shape.n_q, shape.n_kv, shape.d, max_ctx)
+    print(f"config {cfg}: balanced split over {waves} waves", flush=True)
 
     assert orc.kv_append(k_ref, v_ref, kn_h, vn_h, t.block_tables, t.context_lens) == 0
     assert np.array_equal(to_host_u16(k_pool), k_ref), "kv_append K pool differs"

@@ -77,7 +77,7 @@ def test_partition_merge_agrees(pkv, orc):
     split; the merged results agree to fp32 rounding."""
     hc = w.host_case(_shape(32, 8, 128), 77, context_lens=[1000, 777, 64, 1024])
     outs = []
-    for part in (16, 64, 512, 1024):
+    for part in (16, 64, 512, 1024, 0):
         dc = DevCase(hc)
         outs.append(gpu_step(pkv, dc, partition=part))
     for o in outs[1:]:
@@ -165,7 +165,7 @@ def test_device_errors_flagged(pkv):
     sh = _shape(8, 2, 128)
     hc = w.host_case(sh, 9, context_lens=[40, 90, 300])
     ref = gpu_step(pkv, DevCase(hc), partition=64, append=False)
-    for part in (64, 1024):
+    for part in (64, 1024, 0):
         bt = hc.tables.block_tables.copy()
         bt[1, 2] = hc.tables.num_blocks + 7
         dc = DevCase(hc)
@@ -194,15 +194,41 @@ def test_device_errors_flagged(pkv):
     assert np.array_equal(to_host_u16(dc.k_pool), k0)
 
 
-def test_decode_equals_partition_then_merge(pkv):
+@pytest.mark.parametrize("part", [128, 0])
+def test_decode_equals_partition_then_merge(pkv, part):
     import torch
     hc = w.host_case(_shape(32, 8, 128), 12, context_lens=[900, 40, 2000])
     a = DevCase(hc)
     b = DevCase(hc)
-    oa = gpu_step(pkv, a, partition=128, append=False)
+    oa = gpu_step(pkv, a, partition=part, append=False)
     ws = pkv.pkv_paged_attn_partition(b.out, b.q, b.k_pool, b.v_pool, b.bt, b.cl, 1 / 128 ** 0.5,
-                                      b.max_ctx, partition_tokens=128)
+                                      b.max_ctx, partition_tokens=part)
     pkv.pkv_paged_attn_merge(b.out, b.q, b.k_pool, b.v_pool, b.bt, b.cl, 1 / 128 ** 0.5,
-                             b.max_ctx, partition_tokens=128, workspace=ws)
+                             b.max_ctx, partition_tokens=part, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(oa, b.out.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("ctx", [[1, 2, 3], [1, 17, 40, 300], [5000, 1, 1, 1, 33]])
+def test_balanced_split_more_waves_than_tiles(pkv, orc, ctx):
+    """A max_context_len far above the actual contexts: the balanced split
+    then has more waves than tiles, and waves with empty ranges inside a
+    unit must leave neutral partials for the merge."""
+    hc = w.host_case(_shape(32, 8, 128), 50 + len(ctx), context_lens=ctx, max_blocks=1024)
+    dc = DevCase(hc)
+    got = gpu_step(pkv, dc, partition=0, max_ctx=16 * 1024)
+    want, rc, _, _ = oracle_step(orc, hc)
+    assert rc == 0 and int(dc.err.item()) == 0
+    assert max_abs(got, want) <= TOL
+
+
+def test_balanced_split_uneven_mix(pkv, orc):
+    """Many short sequences next to a few long ones: wave ranges cross many
+    unit boundaries in both directions."""
+    rnd = np.random.default_rng(5)
+    ctx = list(rnd.integers(1, 40, size=45)) + [3000, 2500, 1, 16, 17, 4095]
+    hc = w.host_case(_shape(20, 4, 64), 61, context_lens=ctx)
+    got = gpu_step(pkv, DevCase(hc), partition=0)
+    want, rc, _, _ = oracle_step(orc, hc)
+    assert rc == 0
+    assert max_abs(got, want) <= TOL
