@@ -200,28 +200,64 @@ def partition_alg_bytes(S, ctx):
     return kv_bytes(S, ctx) + B * sh.n_q * sh.d * (2 + 4) + tbl + 4 * B
 
 
-def run(pkv, torch, S, steps, warmup):
+def _eager_step(calls):
+    for app, part, merge in calls:
+        app()
+        part()
+        merge()
+
+
+def capture_step(pkv, torch, S):
+    """One step's launches (every layer: append, partition, merge) captured
+    into a HIP graph. The calls are marshalled inside the capture so that
+    they name the capture stream. Tables and context lengths are read from
+    the same device buffers the eager upload fills before each replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls = []
+        for l in range(S.shape.n_layers):
+            calls.append((
+                pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l], S.bt, S.cl,
+                                      err_flag=S.err),
+                pkv.prepare_paged_attn_partition(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
+                                                 S.cl, S.shape.scale, S.max_ctx, S.partition,
+                                                 workspace=S.ws, err_flag=S.err),
+                pkv.prepare_paged_attn_merge(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
+                                             S.cl, S.shape.scale, S.max_ctx, S.partition,
+                                             workspace=S.ws, err_flag=S.err)))
+        _eager_step(calls)
+    return g
+
+
+def run(pkv, torch, S, steps, warmup, graph=True):
+    """Warm-up, then K timed steps with per-kernel HIP events around every
+    launch (the kernels' durations), then, with graph=True, K timed steps
+    that replay the captured step (the step time). Each step first grows
+    every sequence by one token through the allocator and uploads the
+    tables."""
     L = S.shape.n_layers
-    for i in range(warmup):
+    step_no = 0
+    for _ in range(warmup):
         host_grow(pkv, S)
-        upload_tables(torch, S, i)
-        for app, part, merge in S.calls:
-            app()
-            part()
-            merge()
+        upload_tables(torch, S, step_no)
+        step_no += 1
+        _eager_step(S.calls)
     torch.cuda.synchronize()
+
+    # timed steps, eager, with events around each launch
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
           for _ in range(steps)]
-    step_ctx = []
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    eager_ctx = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    t0.record()
     for i in range(steps):
         host_grow(pkv, S)
-        step_ctx.append(S.ctx.copy())
-        upload_tables(torch, S, warmup + i)
+        eager_ctx.append(S.ctx.copy())
+        upload_tables(torch, S, step_no)
+        step_no += 1
         for l, (app, part, merge) in enumerate(S.calls):
             e = ev[i][l]
             e[0].record()
@@ -231,22 +267,48 @@ def run(pkv, torch, S, steps, warmup):
             e[2].record()
             merge()
             e[3].record()
-    t_end.record()
+    t1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = t_start.elapsed_time(t_end)
-    err = int(S.err.item())
-    if err:
-        raise RuntimeError(f"device error flag {err}")
+    eager_wall = time.perf_counter() - wall0
+    eager_ms = max(t0.elapsed_time(t1), eager_wall * 1e3) / steps
+    if int(S.err.item()):
+        raise RuntimeError(f"device error flag {int(S.err.item())}")
     app_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(L)] for i in range(steps)])
     part_ms = np.array([[ev[i][l][1].elapsed_time(ev[i][l][2]) for l in range(L)] for i in range(steps)])
     merge_ms = np.array([[ev[i][l][2].elapsed_time(ev[i][l][3]) for l in range(L)] for i in range(steps)])
-    ms_per_step = max(gpu_ms, wall * 1e3) / steps
-    kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all steps
-    part_bytes = sum(partition_alg_bytes(S, c) for c in step_ctx) / steps   # per launch
+
+    step_ctx, ms_per_step, mode = eager_ctx, eager_ms, "eager"
+    if graph:
+        g = capture_step(pkv, torch, S)
+        host_grow(pkv, S)                     # one warm-up replay
+        upload_tables(torch, S, step_no)
+        step_no += 1
+        g.replay()
+        torch.cuda.synchronize()
+        graph_ctx = []
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            host_grow(pkv, S)
+            graph_ctx.append(S.ctx.copy())
+            upload_tables(torch, S, step_no)
+            step_no += 1
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        if int(S.err.item()):
+            raise RuntimeError(f"device error flag {int(S.err.item())}")
+        step_ctx, ms_per_step, mode = graph_ctx, max(t0.elapsed_time(t1), wall * 1e3) / steps, "hip-graph"
+
+    kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all timed steps
+    part_bytes = sum(partition_alg_bytes(S, c) for c in eager_ctx) / steps   # per launch
     part_us = float(part_ms.mean() * 1e3)
-    r = {
+    return {
         "ms_per_step": ms_per_step,
+        "step_mode": mode,
+        "eager_ms_per_step": eager_ms,
         "steps_per_s": 1e3 / ms_per_step,
         "kv_gbs": kvb / (ms_per_step * steps * 1e-3) / 1e9,
         "seq_tokens_per_s": sum(int(c.astype(np.int64).sum()) for c in step_ctx) / (ms_per_step * steps * 1e-3),
@@ -261,10 +323,7 @@ def run(pkv, torch, S, steps, warmup):
         "split_waves": S.split_waves,
         "num_blocks_per_layer": S.num_blocks,
         "cow_copies": S.n_cow,
-        "gpu_event_ms_total": gpu_ms,
-        "host_wall_ms_total": wall * 1e3,
     }
-    return r
 
 
 # ---------------------------------------------------------------------------
@@ -327,6 +386,7 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-share", action="store_true", help="main run with private prefix copies")
     ap.add_argument("--skip-no-share", action="store_true", help="skip the second, unshared run")
+    ap.add_argument("--no-graph", action="store_true", help="time the step eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -344,13 +404,13 @@ def main():
     import paged_kv_cache_468_amd as pkv
     torch.cuda.set_device(0)
     shape = w.CONFIGS[args.config]
-    extra = args.steps + args.warmup
+    extra = args.warmup + 2 * args.steps + 1   # one token per step: eager, graph warm-up, graph
 
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")
     S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens)
     log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
-    main_r = run(pkv, torch, S, args.steps, args.warmup)
+    main_r = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
     log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step, {main_r['kv_gbs']:.0f} GB/s, "
         f"partition {main_r['partition_us']:.1f} us = {main_r['partition_gbs']:.0f} GB/s")
 
@@ -366,11 +426,12 @@ def main():
     if shape.prefix_tokens > 0 and share_main and not args.skip_no_share:
         log("[bench] no-share run")
         S2 = build_state(pkv, torch, shape, args.seed, False, extra, args.partition_tokens)
-        r2 = run(pkv, torch, S2, args.steps, args.warmup)
+        r2 = run(pkv, torch, S2, args.steps, args.warmup, graph=not args.no_graph)
         log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step, {r2['kv_gbs']:.0f} GB/s, "
             f"partition {r2['partition_us']:.1f} us = {r2['partition_gbs']:.0f} GB/s")
         extra_runs["no_share"] = {
             "value": r2["kv_gbs"], "unit": "GB/s", "ms_per_step": r2["ms_per_step"],
+            "step_mode": r2["step_mode"], "eager_ms_per_step": r2["eager_ms_per_step"],
             "steps_per_s": r2["steps_per_s"], "pct_hbm_peak": 100 * r2["kv_gbs"] / HBM_PEAK_GBS,
             "partition_us": r2["partition_us"], "partition_gbs": r2["partition_gbs"],
             "partition_frac": r2["partition_gbs"] / HBM_PEAK_GBS,
@@ -412,6 +473,8 @@ def main():
             "seed": args.seed, "partition_tokens": main_r["partition_tokens"],
             "split_waves": main_r["split_waves"],
         },
+        "step_mode": main_r["step_mode"],
+        "eager_ms_per_step": main_r["eager_ms_per_step"],
         "steps_per_s": main_r["steps_per_s"],
         "seq_tokens_per_s": main_r["seq_tokens_per_s"],
         "tokens_per_s": main_r["tokens_per_s"],
@@ -429,6 +492,10 @@ def main():
             "traffic": traffic,
             "traffic_note": why,
             "alg_bytes_per_launch": main_r["partition_alg_bytes"],
+            "note": ("duration from HIP events around each launch in the eager timed steps; "
+                     "with a shared prefix the algorithmic bytes count every sequence's whole "
+                     "context while the shared blocks are re-read from cache, so achieved can "
+                     "exceed HBM peak (no_share gives the all-unique case)"),
         },
         "cpu_baseline": cpu,
         "parity_sample_max_abs": parity,
