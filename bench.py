@@ -40,7 +40,8 @@ import workload as w  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 BLOCK = 16
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_attn_partition_llama3-8b.txt")
+# counter summaries: profiles/pmc_<kernel>_<workload>.txt, ending in a JSON record
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_paged_attn_balanced_{workload}.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_468_amd", "csrc", "attention.hip")
 
 WORKLOAD_NAMES = {
@@ -68,7 +69,7 @@ class State:
     pass
 
 
-def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens):
+def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, fused=True):
     """Block tables from the refcounted allocator, pools filled on the
     device, every layer's buffers, and pre-marshalled library calls."""
     cl = w.context_lengths(shape, seed).astype(np.int32)
@@ -145,20 +146,34 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens):
     S.split_waves = pkv.pkv_decode_split_waves(B, n_q, n_kv, d, S.max_ctx) if partition_tokens == 0 else 0
     ws_bytes = pkv.pkv_decode_workspace_bytes(B, n_q, n_kv, d, S.max_ctx, S.partition)
     S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    S.calls = []
-    for l in range(L):
-        app = pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l], S.bt, S.cl,
-                                    err_flag=S.err)
-        part = pkv.prepare_paged_attn_partition(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
-                                                S.cl, shape.scale, S.max_ctx, S.partition,
-                                                workspace=S.ws, err_flag=S.err)
-        merge = pkv.prepare_paged_attn_merge(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
-                                             S.cl, shape.scale, S.max_ctx, S.partition,
-                                             workspace=S.ws, err_flag=S.err)
-        S.calls.append((app, part, merge))
+    S.fused = fused
+    S.calls = layer_calls(pkv, S)
     torch.cuda.synchronize()
     assert int(S.err.item()) == 0
     return S
+
+
+def layer_calls(pkv, S):
+    """Per layer, the (name, call) pairs of one decode step, marshalled on
+    torch's current stream: the fused pkv_decode_step (one kernel with the
+    balanced split), or kv_append + partition + merge."""
+    sh, calls = S.shape, []
+    for l in range(sh.n_layers):
+        if S.fused:
+            calls.append([("decode_step", pkv.prepare_decode_step(
+                S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl,
+                sh.scale, S.max_ctx, S.partition, workspace=S.ws, err_flag=S.err))])
+        else:
+            calls.append([
+                ("kv_append", pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l],
+                                                    S.bt, S.cl, err_flag=S.err)),
+                ("paged_attn_partition", pkv.prepare_paged_attn_partition(
+                    S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale, S.max_ctx,
+                    S.partition, workspace=S.ws, err_flag=S.err)),
+                ("paged_attn_merge", pkv.prepare_paged_attn_merge(
+                    S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale, S.max_ctx,
+                    S.partition, workspace=S.ws, err_flag=S.err))])
+    return calls
 
 
 def host_grow(pkv, S):
@@ -190,52 +205,45 @@ def kv_bytes(S, ctx):
     return 2 * S.shape.n_kv * S.shape.d * 2 * int(ctx.astype(np.int64).sum())
 
 
-def partition_alg_bytes(S, ctx):
-    """Algorithmic bytes of one partition-kernel launch (one layer): the KV
-    it must consume, plus q (bf16), the fp32 output rows, the block-table
-    entries and the context lengths."""
+def attn_alg_bytes(S, ctx):
+    """Algorithmic bytes of one layer's attention: the KV it must consume,
+    plus q (bf16), the fp32 output rows, the block-table entries and the
+    context lengths."""
     sh = S.shape
     B = len(ctx)
     tbl = 4 * int(np.ceil(ctx / BLOCK).astype(np.int64).sum())
     return kv_bytes(S, ctx) + B * sh.n_q * sh.d * (2 + 4) + tbl + 4 * B
 
 
+def append_alg_bytes(S, B):
+    """kv_append of one layer: the new K and V rows read and written."""
+    return 2 * 2 * B * S.shape.n_kv * S.shape.d * 2
+
+
 def _eager_step(calls):
-    for app, part, merge in calls:
-        app()
-        part()
-        merge()
+    for layer in calls:
+        for _, call in layer:
+            call()
 
 
 def capture_step(pkv, torch, S):
-    """One step's launches (every layer: append, partition, merge) captured
-    into a HIP graph. The calls are marshalled inside the capture so that
-    they name the capture stream. Tables and context lengths are read from
-    the same device buffers the eager upload fills before each replay."""
+    """One step's launches (every layer) captured into a HIP graph. The
+    calls are marshalled inside the capture so that they name the capture
+    stream. Tables and context lengths are read from the same device
+    buffers the eager upload fills before each replay."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        calls = []
-        for l in range(S.shape.n_layers):
-            calls.append((
-                pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l], S.bt, S.cl,
-                                      err_flag=S.err),
-                pkv.prepare_paged_attn_partition(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
-                                                 S.cl, S.shape.scale, S.max_ctx, S.partition,
-                                                 workspace=S.ws, err_flag=S.err),
-                pkv.prepare_paged_attn_merge(S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt,
-                                             S.cl, S.shape.scale, S.max_ctx, S.partition,
-                                             workspace=S.ws, err_flag=S.err)))
-        _eager_step(calls)
+        _eager_step(layer_calls(pkv, S))
     return g
 
 
 def run(pkv, torch, S, steps, warmup, graph=True):
-    """Warm-up, then K timed steps with per-kernel HIP events around every
-    launch (the kernels' durations), then, with graph=True, K timed steps
-    that replay the captured step (the step time). Each step first grows
-    every sequence by one token through the allocator and uploads the
-    tables."""
+    """Warm-up, then K timed steps with HIP events around every launch (the
+    kernels' durations), then, with graph=True, K timed steps that replay the
+    captured step (the step time). Each step first grows every sequence by
+    one token through the allocator and uploads the tables."""
     L = S.shape.n_layers
+    names = [n for n, _ in S.calls[0]]
     step_no = 0
     for _ in range(warmup):
         host_grow(pkv, S)
@@ -245,7 +253,7 @@ def run(pkv, torch, S, steps, warmup, graph=True):
     torch.cuda.synchronize()
 
     # timed steps, eager, with events around each launch
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(L)]
           for _ in range(steps)]
     eager_ctx = []
     t0 = torch.cuda.Event(enable_timing=True)
@@ -258,24 +266,21 @@ def run(pkv, torch, S, steps, warmup, graph=True):
         eager_ctx.append(S.ctx.copy())
         upload_tables(torch, S, step_no)
         step_no += 1
-        for l, (app, part, merge) in enumerate(S.calls):
+        for l, layer in enumerate(S.calls):
             e = ev[i][l]
-            e[0].record()
-            app()
-            e[1].record()
-            part()
-            e[2].record()
-            merge()
-            e[3].record()
+            for k, (_, call) in enumerate(layer):
+                e[k].record()
+                call()
+            e[len(layer)].record()
     t1.record()
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - wall0
     eager_ms = max(t0.elapsed_time(t1), eager_wall * 1e3) / steps
     if int(S.err.item()):
         raise RuntimeError(f"device error flag {int(S.err.item())}")
-    app_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(L)] for i in range(steps)])
-    part_ms = np.array([[ev[i][l][1].elapsed_time(ev[i][l][2]) for l in range(L)] for i in range(steps)])
-    merge_ms = np.array([[ev[i][l][2].elapsed_time(ev[i][l][3]) for l in range(L)] for i in range(steps)])
+    kern_us = {n: float(np.mean([[ev[i][l][k].elapsed_time(ev[i][l][k + 1]) for l in range(L)]
+                                 for i in range(steps)]) * 1e3)
+               for k, n in enumerate(names)}
 
     step_ctx, ms_per_step, mode = eager_ctx, eager_ms, "eager"
     if graph:
@@ -286,7 +291,6 @@ def run(pkv, torch, S, steps, warmup, graph=True):
         g.replay()
         torch.cuda.synchronize()
         graph_ctx = []
-        torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t0.record()
         for i in range(steps):
@@ -302,9 +306,11 @@ def run(pkv, torch, S, steps, warmup, graph=True):
             raise RuntimeError(f"device error flag {int(S.err.item())}")
         step_ctx, ms_per_step, mode = graph_ctx, max(t0.elapsed_time(t1), wall * 1e3) / steps, "hip-graph"
 
+    # the roofline kernel: the one launch per layer that does the attention
+    dom = "decode_step" if S.fused else "paged_attn_partition"
+    dom_bytes = sum(attn_alg_bytes(S, c) + (append_alg_bytes(S, S.B) if S.fused else 0)
+                    for c in eager_ctx) / steps
     kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all timed steps
-    part_bytes = sum(partition_alg_bytes(S, c) for c in eager_ctx) / steps   # per launch
-    part_us = float(part_ms.mean() * 1e3)
     return {
         "ms_per_step": ms_per_step,
         "step_mode": mode,
@@ -314,11 +320,11 @@ def run(pkv, torch, S, steps, warmup, graph=True):
         "seq_tokens_per_s": sum(int(c.astype(np.int64).sum()) for c in step_ctx) / (ms_per_step * steps * 1e-3),
         "tokens_per_s": S.B / (ms_per_step * 1e-3),
         "kv_bytes_per_step": kvb / steps,
-        "partition_us": part_us,
-        "append_us": float(app_ms.mean() * 1e3),
-        "merge_us": float(merge_ms.mean() * 1e3),
-        "partition_alg_bytes": part_bytes,
-        "partition_gbs": part_bytes / (part_us * 1e-6) / 1e9,
+        "kernels_us": kern_us,
+        "dominant": dom,
+        "dominant_us": kern_us[dom],
+        "dominant_alg_bytes": dom_bytes,
+        "dominant_gbs": dom_bytes / (kern_us[dom] * 1e-6) / 1e9,
         "partition_tokens": S.partition,
         "split_waves": S.split_waves,
         "num_blocks_per_layer": S.num_blocks,
@@ -359,13 +365,15 @@ def cpu_baseline(torch, S, budget_s):
     }, worst, done
 
 
-def stored_traffic(part_alg_bytes):
-    """HBM bytes per partition-kernel launch from the committed counter
-    summary, if it was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary of this workload (profiles/pmc_*), if it was taken on the current
+    kernel source and the same entry point."""
+    path = PMC_FILE.format(workload=workload)
+    if not os.path.exists(path):
         return None, "no counter summary"
     rec = None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("{"):
                 rec = json.loads(line)
@@ -373,6 +381,8 @@ def stored_traffic(part_alg_bytes):
         return None, "no record in counter summary"
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
+    if rec.get("entry") != kernel:
+        return None, f"counters were taken on {rec.get('entry')}"
     return rec["hbm_bytes_per_dispatch"], None
 
 
@@ -387,6 +397,8 @@ def main():
     ap.add_argument("--no-share", action="store_true", help="main run with private prefix copies")
     ap.add_argument("--skip-no-share", action="store_true", help="skip the second, unshared run")
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly instead of replaying a HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="three launches per layer (kv_append, partition, merge) instead of pkv_decode_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -408,11 +420,13 @@ def main():
 
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")
-    S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens)
+    S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens,
+                    fused=not args.unfused)
     log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
     main_r = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
-    log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step, {main_r['kv_gbs']:.0f} GB/s, "
-        f"partition {main_r['partition_us']:.1f} us = {main_r['partition_gbs']:.0f} GB/s")
+    log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step ({main_r['step_mode']}), "
+        f"{main_r['kv_gbs']:.0f} GB/s; {main_r['dominant']} {main_r['dominant_us']:.1f} us = "
+        f"{main_r['dominant_gbs']:.0f} GB/s; kernels {main_r['kernels_us']}")
 
     cpu, parity, n_par = None, None, 0
     if args.cpu_seconds > 0:
@@ -425,16 +439,22 @@ def main():
     extra_runs = {}
     if shape.prefix_tokens > 0 and share_main and not args.skip_no_share:
         log("[bench] no-share run")
-        S2 = build_state(pkv, torch, shape, args.seed, False, extra, args.partition_tokens)
+        S2 = build_state(pkv, torch, shape, args.seed, False, extra, args.partition_tokens,
+                         fused=not args.unfused)
         r2 = run(pkv, torch, S2, args.steps, args.warmup, graph=not args.no_graph)
-        log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step, {r2['kv_gbs']:.0f} GB/s, "
-            f"partition {r2['partition_us']:.1f} us = {r2['partition_gbs']:.0f} GB/s")
+        log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step ({r2['step_mode']}), "
+            f"{r2['kv_gbs']:.0f} GB/s; {r2['dominant']} {r2['dominant_us']:.1f} us = "
+            f"{r2['dominant_gbs']:.0f} GB/s; kernels {r2['kernels_us']}")
+        t2, why2 = stored_traffic("llama3-8b-no-share", r2["dominant"]) if args.config == 4 else (None, "other workload")
         extra_runs["no_share"] = {
             "value": r2["kv_gbs"], "unit": "GB/s", "ms_per_step": r2["ms_per_step"],
             "step_mode": r2["step_mode"], "eager_ms_per_step": r2["eager_ms_per_step"],
             "steps_per_s": r2["steps_per_s"], "pct_hbm_peak": 100 * r2["kv_gbs"] / HBM_PEAK_GBS,
-            "partition_us": r2["partition_us"], "partition_gbs": r2["partition_gbs"],
-            "partition_frac": r2["partition_gbs"] / HBM_PEAK_GBS,
+            "kernels_us": r2["kernels_us"],
+            "roofline": {"kernel": r2["dominant"], "bound": "hbm", "achieved": r2["dominant_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r2["dominant_gbs"] / HBM_PEAK_GBS, "traffic": t2,
+                         "traffic_note": why2, "alg_bytes_per_launch": r2["dominant_alg_bytes"]},
             "num_blocks_per_layer": r2["num_blocks_per_layer"],
         }
         del S2
@@ -450,7 +470,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    traffic, why = stored_traffic(main_r["partition_alg_bytes"]) if args.config == 4 and share_main else (None, "other workload")
+    traffic, why = (stored_traffic("llama3-8b-shared" if share_main else "llama3-8b-no-share",
+                                   main_r["dominant"]) if args.config == 4 else (None, "other workload"))
     line = {
         "metric": "paged decode-attention KV GB/s (% of HBM peak) + steps/s, Llama-3-8B shape",
         "value": main_r["kv_gbs"],
@@ -480,18 +501,17 @@ def main():
         "tokens_per_s": main_r["tokens_per_s"],
         "pct_hbm_peak": 100 * main_r["kv_gbs"] / HBM_PEAK_GBS,
         "kv_bytes_per_step": main_r["kv_bytes_per_step"],
-        "kernels_us": {"kv_append": main_r["append_us"], "paged_attn_partition": main_r["partition_us"],
-                       "paged_attn_merge": main_r["merge_us"]},
+        "kernels_us": main_r["kernels_us"],
         "roofline": {
-            "kernel": "paged_attn_partition_kernel<128>",
+            "kernel": main_r["dominant"],
             "bound": "hbm",
-            "achieved": main_r["partition_gbs"],
+            "achieved": main_r["dominant_gbs"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": main_r["partition_gbs"] / HBM_PEAK_GBS,
+            "frac": main_r["dominant_gbs"] / HBM_PEAK_GBS,
             "traffic": traffic,
             "traffic_note": why,
-            "alg_bytes_per_launch": main_r["partition_alg_bytes"],
+            "alg_bytes_per_launch": main_r["dominant_alg_bytes"],
             "note": ("duration from HIP events around each launch in the eager timed steps; "
                      "with a shared prefix the algorithmic bytes count every sequence's whole "
                      "context while the shared blocks are re-read from cache, so achieved can "

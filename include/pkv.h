@@ -180,8 +180,11 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  * Workspace bytes: 4 * (head_dim + 2) * min(G, 16) * slots, with slots =
  * units * ceil(max_context_len / P) for fixed partitions (0 if that is one
  * partition) and units + min(8192, ceil(units * ceil(max_context_len/16) / 16))
- * for the balanced split; units = num_seqs * n_kv_heads * ceil(G / 16).
- * The balanced split needs no zeroing or other preparation of it. */
+ * for the balanced split; units = num_seqs * n_kv_heads * ceil(G / 16). The
+ * balanced split's workspace starts with 8 * units bytes (rounded up to a
+ * multiple of 256) of per-unit bookkeeping the partition kernel writes for
+ * the merge kernel. No initialisation is needed. One workspace serves one
+ * call at a time. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim,
                                   int32_t max_context_len,
@@ -220,6 +223,29 @@ int pkv_paged_attn_merge(float* out, const void* q, const void* k_pool,
                          int32_t max_context_len, int32_t partition_tokens,
                          void* workspace, size_t workspace_bytes,
                          int32_t* err_flag, void* stream);
+/* One layer's decode step: pkv_kv_append of (k_new, v_new), then
+ * pkv_paged_attn_decode, with the same arguments as those two calls (k_pool
+ * and v_pool are written). Results, pools included, are bit for bit those of
+ * the two calls. With the balanced split the append runs inside the
+ * attention's partition kernel (two launches instead of three): the
+ * wavefront that holds a sequence's last tile takes the new token's key and
+ * value from k_new / v_new and stores them into the pools (for the first
+ * query group of each KV head) during the attention. The block holding
+ * position ctx - 1
+ * must not be shared with another sequence (copy on write first, as
+ * pkv_seq_grow arranges). Invalid context lengths (outside
+ * [1, max_context_len]) and bad block ids are reported as for the two calls;
+ * such a sequence is not appended. k_new / v_new: device bf16
+ * [num_seqs][n_kv_heads][head_dim]. */
+int pkv_decode_step(float* out, const void* q, const void* k_new,
+                    const void* v_new, void* k_pool, void* v_pool,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, float scale, int32_t max_context_len,
+                    int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, int32_t* err_flag, void* stream);
+
 /* Wavefronts of the balanced split on the current device for this shape:
  * the number resident at once on the device (compute units x resident
  * wavefronts of the kernel), at most 8192, and at most one per 16 tiles of

@@ -49,6 +49,8 @@ SIGNATURES = {
     "pkv_paged_attn_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
@@ -235,6 +237,33 @@ def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, sc
     _check(lib.pkv_paged_attn_decode(*args), "pkv_paged_attn_decode")
 
 
+def _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+               max_context_len, partition_tokens, workspace, err_flag, stream):
+    torch = _torch()
+    args, ws = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                            max_context_len, partition_tokens, workspace, err_flag, stream)
+    _, n_kv, d = _pool_dims(k_pool, v_pool)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev(t, name, torch.bfloat16, 3)
+        if tuple(t.shape) != (q.shape[0], n_kv, d):
+            raise ValueError(f"{name}: expected [num_seqs, n_kv, head_dim]")
+    # C order: out, q, k_new, v_new, k_pool, v_pool, then as the decode
+    step = (args[0], args[1], _dev(k_new, "k_new", torch.bfloat16),
+            _dev(v_new, "v_new", torch.bfloat16), args[2], args[3]) + args[4:]
+    return step, ws
+
+
+def pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                    max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                    stream=None):
+    """kv_append of (k_new, v_new) and the decode attention of one layer;
+    with the balanced split the append runs inside the partition kernel.
+    workspace as for pkv_paged_attn_decode."""
+    args, _ = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                         max_context_len, partition_tokens, workspace, err_flag, stream)
+    _check(lib.pkv_decode_step(*args), "pkv_decode_step")
+
+
 def pkv_paged_attn_partition(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                              max_context_len, partition_tokens=0, workspace=None, err_flag=None,
                              stream=None):
@@ -386,6 +415,16 @@ def _prepare_decode(name, out, q, k_pool, v_pool, block_tables, context_lens, sc
                             max_context_len, partition_tokens, workspace, err_flag, stream)
     return PreparedCall(name, args,
                         (out, q, k_pool, v_pool, block_tables, context_lens, ws, err_flag))
+
+
+def prepare_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                        max_context_len, partition_tokens=0, workspace=None, err_flag=None,
+                        stream=None):
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, partition_tokens, workspace, err_flag, stream)
+    return PreparedCall("pkv_decode_step", args,
+                        (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
+                         err_flag))
 
 
 def prepare_paged_attn_decode(*a, **k):

@@ -86,8 +86,11 @@ struct DecodeArgs {
   const uint16_t* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const uint16_t* k_new;   // append fused into the attention: [B][n_kv][D], or null
+  const uint16_t* v_new;
   float* ws_ml;      // [slots][rows][2]  (reference max in log2 units, sum)
   float* ws_acc;     // [slots][rows][D]  unnormalised accumulators
+  int32_t* unit_info; // balanced split: per unit, first partial slot and partial count
   int32_t* err_flag;
   int num_seqs, max_blocks, num_blocks;
   int n_q, n_kv, group, n_qgroups, rows;  // rows = min(group, 16) per slot
@@ -185,10 +188,17 @@ __device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_
 // a column), the column's partial sum l (this lane's tokens only) and the
 // accumulator acc (dims 16m + 4r .. +3 of row c). Returns false if a block
 // id was out of range (nothing else is then meaningful).
+//
+// With a.k_new set and the segment ending at the unit's last tile, the token
+// at position ctx - 1 is this step's new one: its key and value come from
+// k_new / v_new (substituted into the tile's registers, so the result never
+// depends on the order of this wave's own store and load), and when
+// store_new is set (the unit of the head's first query group) they are also
+// written into the pools.
 template <int D>
 __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h, int j_row,
-                                       bool row_valid, int ctx, int ta, int tb, f32x4_t* acc,
-                                       float& m_run, float& l_run) {
+                                       bool row_valid, int ctx, int ta, int tb, bool store_new,
+                                       f32x4_t* acc, float& m_run, float& l_run) {
   constexpr int KM = D / 32;   // score MFMAs per tile (k = 32 dims each)
   constexpr int VM = D / 16;   // value MFMAs per tile (16 dims each)
   const int c = lane & 15;
@@ -217,15 +227,27 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
   const int last_tile = (ctx - 1) >> 4;
   const int last_valid = ctx - last_tile * 16;   // tokens in the sequence's last tile
+  const int new_slot = last_valid - 1;           // slot of position ctx - 1
+  const bool has_new = a.k_new != nullptr && tb > last_tile;
 
   bf16x8_t kA[KM], kB[KM];
   bf16x4_t vA[VM], vB[VM];
+  bf16x8_t kn[KM];   // new token: key dims 32m + 8r .. +7
+  short vn[VM];      // new token: value dim 16m + c
 
   for (int cb = ta; cb < tb; cb += 64) {
     const int nb = min(64, tb - cb);
     // Physical block ids of this chunk: lane i holds entry cb + i.
     const int my_id = lane < nb ? bt_row[cb + lane] : 0;
     if (__ballot(lane < nb && (my_id < 0 || my_id >= a.num_blocks)) != 0) return false;
+    const bool new_here = has_new && last_tile < cb + nb;
+    if (new_here) {
+      const int64_t row = ((int64_t)s * a.n_kv + h) * D;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) kn[m] = *(const bf16x8_t*)(a.k_new + row + 32 * m + 8 * r);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) vn[m] = (short)a.v_new[row + 16 * m + c];
+    }
 
     auto load_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
       const int blk = __builtin_amdgcn_readlane(my_id, i);
@@ -238,7 +260,31 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
       for (int m = 0; m < VM; ++m) vr[m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
     };
 
-    auto compute_tile = [&](int i, const bf16x8_t* kr, bf16x4_t* vr) {
+    auto compute_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
+      if (new_here && cb + i == last_tile) {
+        if (c == new_slot) {
+#pragma unroll
+          for (int m = 0; m < KM; ++m) kr[m] = kn[m];
+        }
+        if (r == (new_slot >> 2)) {
+#pragma unroll
+          for (int m = 0; m < VM; ++m) vr[m][new_slot & 3] = vn[m];
+        }
+        if (store_new) {
+          const int blk = __builtin_amdgcn_readlane(my_id, i);
+          const int64_t base = (int64_t)blk * block_stride + head_off;
+          uint16_t* kt = (uint16_t*)a.k_pool + base;
+          uint16_t* vt = (uint16_t*)a.v_pool + base;
+          if (c == new_slot) {
+#pragma unroll
+            for (int m = 0; m < KM; ++m) *(bf16x8_t*)(kt + new_slot * D + 32 * m + 8 * r) = kn[m];
+          }
+          if (r == 0) {
+#pragma unroll
+            for (int m = 0; m < VM; ++m) vt[(16 * m + c) * 16 + new_slot] = (uint16_t)vn[m];
+          }
+        }
+      }
       f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KM; ++m)
@@ -338,6 +384,15 @@ __device__ inline void finish_segment(const DecodeArgs& a, int lane, bool ok, bo
   }
 }
 
+// First wave and last wave (inclusive) of the balanced split that touch
+// tiles [t0, t1) of the launch order, t1 > t0.
+__device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int n_waves,
+                                      int& w0, int& w1) {
+  // wave of tile x: the largest w with floor(w*total/W) <= x
+  w0 = (int)(((t0 + 1) * n_waves - 1) / total);
+  w1 = (int)((t1 * n_waves - 1) / total);
+}
+
 // Fixed partitions: one wave per (unit, partition).
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
@@ -365,13 +420,16 @@ __global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
 
   f32x4_t acc[VM];
   float m_run, l_run;
-  const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, ta, tb, acc, m_run, l_run);
+  const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run,
+                                     l_run);
   finish_segment<D>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, s, j, c,
                     row_valid, acc, m_run, l_run);
 }
 
 // Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
-// (head, group, sequence, tile) order, T = all tiles of the launch.
+// (head, group, sequence, tile) order, T = all tiles of the launch. The
+// wave holding a unit's first tile records, for the merge kernel, the
+// unit's first partial slot and its number of partials (1: written here).
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) {
   constexpr int VM = D / 16;
@@ -386,21 +444,23 @@ __global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) 
   int64_t cur = total * w / a.n_waves;
   const int64_t end = total * (w + 1) / a.n_waves;
   if (cur >= end) {
-    // An empty range (fewer tiles than waves). If it sits inside a unit,
-    // the merge of that unit counts this wave: leave a neutral partial
-    // (weight 2^-inf, sum 0, accumulator 0) in its slot.
+    // An empty range (fewer tiles than waves). If it sits strictly inside a
+    // unit (after the unit's first tile), the merge of that unit counts
+    // this wave: leave a neutral partial (weight 2^-inf, sum 0, accumulator
+    // 0) in its slot. At a unit's first tile it belongs to no unit.
     if (cur < total) {
       const int hq = (int)(cur / per_row);
       int s, before;
       locate_tile(a, lane, (int)(cur - (int64_t)hq * per_row), s, before);
-      if (s >= a.num_seqs) return;
+      if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
       const int g = (hq % a.n_qgroups) * 16 + c;
       const int j = (hq / a.n_qgroups) * a.group + g;
+      const int u = hq * a.num_seqs + s;
       f32x4_t zero[VM];
 #pragma unroll
       for (int m = 0; m < VM; ++m) zero[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      finish_segment<D>(a, lane, true, false, (int64_t)w + hq * a.num_seqs + s, s, j, c,
-                        g < a.group, zero, -__builtin_inff(), 0.f);
+      finish_segment<D>(a, lane, true, false, (int64_t)w + u, s, j, c, g < a.group, zero,
+                        -__builtin_inff(), 0.f);
     }
     return;
   }
@@ -421,12 +481,19 @@ __global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) 
     const bool row_valid = g < a.group;
     const int j = h * a.group + g;
     const int u = hq * a.num_seqs + s;
+    const bool whole = pos == 0 && tb == nt;
 
+    if (pos == 0 && lane == 0) {
+      int w0, w1;
+      waves_of_range(cur, cur + nt, total, a.n_waves, w0, w1);
+      a.unit_info[2 * u] = w0 + u;
+      a.unit_info[2 * u + 1] = w1 - w0 + 1;
+    }
     f32x4_t acc[VM];
     float m_run, l_run;
-    const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, pos, tb, acc, m_run, l_run);
-    finish_segment<D>(a, lane, ok, pos == 0 && tb == nt, (int64_t)w + u, s, j, c, row_valid,
-                      acc, m_run, l_run);
+    const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
+                                       m_run, l_run);
+    finish_segment<D>(a, lane, ok, whole, (int64_t)w + u, s, j, c, row_valid, acc, m_run, l_run);
     cur += tb - pos;
     if (cur >= end) break;
     // next unit with work: following sequence, or the next (head, group)
@@ -441,43 +508,36 @@ __global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) 
   }
 }
 
-// First wave and last wave (inclusive) of the balanced split that touch
-// tiles [t0, t1) of the launch order, t1 > t0.
-__device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int n_waves,
-                                      int& w0, int& w1) {
-  // wave of tile x: the largest w with floor(w*total/W) <= x
-  w0 = (int)(((t0 + 1) * n_waves - 1) / total);
-  w1 = (int)((t1 * n_waves - 1) / total);
-}
-
-// Merge of the partials of one (unit, query row): with reference maxima
-// m_p, sums l_p and accumulators a_p (all relative to 2^(x - m_p)),
-// out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
-// One wave per row; lane i owns dims PER*i .. PER*i + PER - 1.
+// Merge kernel: one wave per (unit, query row). With reference maxima m_p,
+// sums l_p and accumulators a_p of the unit's partials (all relative to
+// 2^(x - m_p)): M = max_p m_p, L = sum_p l_p 2^(m_p - M) and
+// out = (sum_p 2^(m_p - M) a_p) / L. Lane p holds partial p's weight;
+// lane i owns dims PER*i .. PER*i + PER - 1. A NaN maximum (a bad block id
+// met by the partition kernel) makes the row NaN; a sequence with an
+// invalid context length gets NaN rows and the error bit. Units one wave
+// covered were written by the partition kernel and are skipped.
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= a.n_units * a.rows) return;
-  const int u = row / a.rows;
-  const int g_in_slot = row % a.rows;
+  const int row_id = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row_id >= a.n_units * a.rows) return;
+  const int u = row_id / a.rows;
+  const int g_in_slot = row_id % a.rows;
   const int s = u % a.num_seqs;
   const int hq = u / a.num_seqs;
-  const int h = hq / a.n_qgroups;
   const int qg = hq % a.n_qgroups;
   const int g = qg * 16 + g_in_slot;
   if (g >= a.group) return;
-  const int j = h * a.group + g;
+  const int j = (hq / a.n_qgroups) * a.group + g;
   float* o = a.out + ((int64_t)s * a.n_q + j) * D + lane * PER;
   const float nan = __builtin_nanf("");
 
-  const int ctx = a.context_lens[s];
-  const int nt = seq_tiles(ctx, a.max_ctx);
+  const int nt = seq_tiles(a.context_lens[s], a.max_ctx);
   if (nt == 0) {
-    if (g_in_slot == 0 && hq == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = nan;
+    if (hq == 0 && g == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
     return;
   }
   int64_t first;
@@ -487,26 +547,17 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     n = (nt + tiles_per_part - 1) / tiles_per_part;
     first = (int64_t)u * a.p_max;
   } else {
-    const int per_row = total_seq_tiles(a, lane);
-    int before = 0;
-    for (int base = 0; base < s; base += 64) {   // tiles of the sequences before s
-      const int i = base + lane;
-      before += wave_sum(i < s ? seq_tiles(a.context_lens[i], a.max_ctx) : 0);
-    }
-    const int64_t t0 = (int64_t)hq * per_row + before;
-    int w0, w1;
-    waves_of_range(t0, t0 + nt, (int64_t)(a.n_kv * a.n_qgroups) * per_row, a.n_waves, w0, w1);
-    n = w1 - w0 + 1;
-    first = (int64_t)w0 + u;
+    first = a.unit_info[2 * u];
+    n = a.unit_info[2 * u + 1];
   }
   if (n <= 1) return;   // written directly by the partition kernel
 
   const float* ml = a.ws_ml + (first * a.rows + g_in_slot) * 2;
-  const int64_t ml_stride = (int64_t)a.rows * 2;
+  const int64_t mls = (int64_t)a.rows * 2;
   float mx = -__builtin_inff();
   bool bad = false;
   for (int p = lane; p < n; p += 64) {
-    const float mp = ml[p * ml_stride];
+    const float mp = ml[p * mls];
     bad |= mp != mp;
     mx = fmaxf(mx, mp);
   }
@@ -518,8 +569,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     return;
   }
   float lsum = 0.f;
-  for (int p = lane; p < n; p += 64)
-    lsum += ml[p * ml_stride + 1] * __builtin_amdgcn_exp2f(ml[p * ml_stride] - mx);
+  for (int p = lane; p < n; p += 64) lsum += ml[p * mls + 1] * __builtin_amdgcn_exp2f(ml[p * mls] - mx);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
 
@@ -527,25 +577,29 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) res[e] = 0.f;
   const float* acc = a.ws_acc + (first * a.rows + g_in_slot) * D + lane * PER;
-  const int64_t acc_stride = (int64_t)a.rows * D;
-  int p = 0;
-  for (; p + 4 <= n; p += 4) {   // four independent loads in flight
-    float wg[4], v[4][PER];
+  const int64_t accs = (int64_t)a.rows * D;
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int np = min(64, n - p0);
+    const float my_w = lane < np ? __builtin_amdgcn_exp2f(ml[(p0 + lane) * mls] - mx) : 0.f;
+    int p = 0;
+    for (; p + 8 <= np; p += 8) {   // eight independent loads in flight
+      float v[8][PER];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      wg[k] = __builtin_amdgcn_exp2f(ml[(p + k) * ml_stride] - mx);
+      for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int e = 0; e < PER; ++e) v[k][e] = acc[(p + k) * acc_stride + e];
+        for (int e = 0; e < PER; ++e) v[k][e] = acc[(p0 + p + k) * accs + e];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wg = __shfl(my_w, p + k);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) res[e] += wg * v[k][e];
+      }
     }
+    for (; p < np; ++p) {
+      const float wg = __shfl(my_w, p);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < PER; ++e) res[e] += wg[k] * v[k][e];
-  }
-  for (; p < n; ++p) {
-    const float wg = __builtin_amdgcn_exp2f(ml[p * ml_stride] - mx);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] += wg * acc[p * acc_stride + e];
+      for (int e = 0; e < PER; ++e) res[e] += wg * acc[(p0 + p) * accs + e];
+    }
   }
   const float inv = 1.0f / lsum;
 #pragma unroll
@@ -588,17 +642,26 @@ static int resident_waves(int head_dim) {
   return slot;
 }
 
-static size_t workspace_bytes(int num_seqs, int n_q, int n_kv, int d, int max_ctx, int part) {
+// Workspace of the balanced split: per unit its first partial slot and
+// partial count (2 x int32, rounded up to 256 bytes), then the partial
+// slots. Fixed partitions: the partial slots only.
+static size_t unit_info_bytes(int num_seqs, int n_q, int n_kv) {
+  return (size_t)((n_units_of(num_seqs, n_q, n_kv) * 8 + 255) / 256 * 256);
+}
+
+static int64_t slot_count(int num_seqs, int n_q, int n_kv, int max_ctx, int part) {
   const int64_t units = n_units_of(num_seqs, n_q, n_kv);
-  int64_t slots;
   if (part > 0) {
     const int p_max = (max_ctx + part - 1) / part;
-    if (p_max <= 1) return 0;
-    slots = units * p_max;
-  } else {
-    slots = split_wave_cap(num_seqs, n_q, n_kv, max_ctx) + units;
+    return p_max <= 1 ? 0 : units * p_max;
   }
-  return (size_t)slots * rows_per_slot(n_q, n_kv) * (2 + d) * sizeof(float);
+  return split_wave_cap(num_seqs, n_q, n_kv, max_ctx) + units;
+}
+
+static size_t workspace_bytes(int num_seqs, int n_q, int n_kv, int d, int max_ctx, int part) {
+  const size_t slots_bytes = (size_t)slot_count(num_seqs, n_q, n_kv, max_ctx, part) *
+                             rows_per_slot(n_q, n_kv) * (2 + d) * sizeof(float);
+  return (part > 0 ? 0 : unit_info_bytes(num_seqs, n_q, n_kv)) + slots_bytes;
 }
 
 }  // namespace pkv
@@ -679,9 +742,13 @@ static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, 
   const size_t need = workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
                                       partition_tokens);
   if (need > 0 && (workspace == nullptr || workspace_bytes_given < need)) return PKV_EWORKSPACE;
-  const int64_t slots = need / (sizeof(float) * (2 + head_dim) * a.rows);
-  a.ws_ml = (float*)workspace;
-  a.ws_acc = need > 0 ? (float*)workspace + 2 * slots * a.rows : nullptr;
+  const int64_t slots = slot_count(num_seqs, n_q_heads, n_kv_heads, max_context_len, partition_tokens);
+  const size_t info = partition_tokens > 0 ? 0 : unit_info_bytes(num_seqs, n_q_heads, n_kv_heads);
+  a.unit_info = partition_tokens > 0 ? nullptr : (int32_t*)workspace;
+  a.ws_ml = slots > 0 ? (float*)((char*)workspace + info) : nullptr;
+  a.ws_acc = slots > 0 ? a.ws_ml + 2 * slots * a.rows : nullptr;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
 
   int64_t waves;
   if (partition_tokens > 0) {
@@ -752,12 +819,42 @@ extern "C" int pkv_paged_attn_merge(PKV_DECODE_PARAMS) {
   return launch_merge(a, d, (hipStream_t)stream);
 }
 
+// The partition kernel, then the merge kernel.
+static int decode_launch(DecodeArgs& a, int d, hipStream_t st) {
+  const int rc = launch_partition(a, d, st);
+  return rc != PKV_OK ? rc : launch_merge(a, d, st);
+}
+
 extern "C" int pkv_paged_attn_decode(PKV_DECODE_PARAMS) {
   DecodeArgs a;
   int d = 0;
-  int rc = prepare(a, d, PKV_DECODE_ARGS);
+  const int rc = prepare(a, d, PKV_DECODE_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
-  rc = launch_partition(a, d, (hipStream_t)stream);
-  if (rc != PKV_OK) return rc;
-  return launch_merge(a, d, (hipStream_t)stream);
+  return decode_launch(a, d, (hipStream_t)stream);
+}
+
+extern "C" int pkv_decode_step(float* out, const void* q, const void* k_new, const void* v_new,
+                               void* k_pool, void* v_pool, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float scale,
+                               int32_t max_context_len, int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes_given, int32_t* err_flag, void* stream) {
+  DecodeArgs a;
+  int d = 0;
+  const int rc = prepare(a, d, out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                         max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads, head_dim, scale,
+                         max_context_len, partition_tokens, workspace, workspace_bytes_given,
+                         err_flag);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (!k_new || !v_new) return PKV_EINVAL;
+  if (partition_tokens == 0) {
+    a.k_new = (const uint16_t*)k_new;
+    a.v_new = (const uint16_t*)v_new;
+    return decode_launch(a, d, (hipStream_t)stream);
+  }
+  const int arc = pkv_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                                num_seqs, max_blocks_per_seq, num_blocks, n_kv_heads, head_dim,
+                                err_flag, stream);
+  return arc != PKV_OK ? arc : decode_launch(a, d, (hipStream_t)stream);
 }

@@ -47,15 +47,23 @@ class DevCase:
         self.max_ctx = int(hc.tables.context_lens.max())
 
 
-def gpu_step(pkv, dc: DevCase, partition=0, append=True, scale=None, max_ctx=None):
+def gpu_step(pkv, dc: DevCase, partition=0, append=True, scale=None, max_ctx=None, fused=False):
+    """append (unless append=False) and decode; fused=True runs both as
+    pkv_decode_step."""
     torch = torch_mod()
     sh = dc.hc.shape
-    if append:
-        pkv.pkv_kv_append(dc.k_pool, dc.v_pool, dc.k_new, dc.v_new, dc.bt, dc.cl, err_flag=dc.err)
-    pkv.pkv_paged_attn_decode(dc.out, dc.q, dc.k_pool, dc.v_pool, dc.bt, dc.cl,
-                              sh.scale if scale is None else scale,
-                              dc.max_ctx if max_ctx is None else max_ctx,
-                              partition_tokens=partition, err_flag=dc.err)
+    scale = sh.scale if scale is None else scale
+    max_ctx = dc.max_ctx if max_ctx is None else max_ctx
+    if fused:
+        assert append
+        pkv.pkv_decode_step(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt, dc.cl,
+                            scale, max_ctx, partition_tokens=partition, err_flag=dc.err)
+    else:
+        if append:
+            pkv.pkv_kv_append(dc.k_pool, dc.v_pool, dc.k_new, dc.v_new, dc.bt, dc.cl,
+                              err_flag=dc.err)
+        pkv.pkv_paged_attn_decode(dc.out, dc.q, dc.k_pool, dc.v_pool, dc.bt, dc.cl, scale, max_ctx,
+                                  partition_tokens=partition, err_flag=dc.err)
     torch.cuda.synchronize()
     return dc.out.cpu().numpy().astype(np.float64)
 

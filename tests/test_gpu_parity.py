@@ -27,9 +27,9 @@ def _shape(n_q, n_kv, d, prefix=0):
     return w.Shape(f"{n_q}/{n_kv} d{d}", 1, n_q, n_kv, d, 1, 1, 1, prefix_tokens=prefix)
 
 
-def _check_case(pkv, orc, hc, partition=0, scale=None):
+def _check_case(pkv, orc, hc, partition=0, scale=None, fused=False):
     dc = DevCase(hc)
-    got = gpu_step(pkv, dc, partition=partition, scale=scale)
+    got = gpu_step(pkv, dc, partition=partition, scale=scale, fused=fused)
     want, rc, k_ref, v_ref = oracle_step(orc, hc, scale=scale)
     assert rc == 0
     assert int(dc.err.item()) == 0
@@ -64,11 +64,12 @@ CASES = [  # n_q, n_kv, d, contexts, partition
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["append+decode", "decode_step"])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_random_shapes(pkv, orc, case):
+def test_random_shapes(pkv, orc, case, fused):
     n_q, n_kv, d, ctx, part = CASES[case]
     hc = w.host_case(_shape(n_q, n_kv, d), 1000 + case, context_lens=ctx, spare_blocks=5)
-    _, err = _check_case(pkv, orc, hc, partition=part)
+    _, err = _check_case(pkv, orc, hc, partition=part, fused=fused)
     print(f"case {CASES[case]}: max-abs {err:.2e}")
 
 
@@ -232,3 +233,72 @@ def test_balanced_split_uneven_mix(pkv, orc):
     want, rc, _, _ = oracle_step(orc, hc)
     assert rc == 0
     assert max_abs(got, want) <= TOL
+
+
+@pytest.mark.parametrize("part", [0, 128])
+@pytest.mark.parametrize("shape", [(32, 8, 128), (40, 2, 128), (20, 4, 64), (8, 1, 128)])
+def test_decode_step_equals_append_then_decode(pkv, shape, part):
+    """pkv_decode_step (one kernel with the balanced split) against
+    pkv_kv_append + pkv_paged_attn_decode: pools and outputs bit for bit."""
+    ctx = [1, 15, 16, 17, 300, 1000, 2049]
+    hc = w.host_case(_shape(*shape), 90 + shape[0], context_lens=ctx, spare_blocks=3)
+    a = DevCase(hc)
+    b = DevCase(hc)
+    oa = gpu_step(pkv, a, partition=part)
+    ob = gpu_step(pkv, b, partition=part, fused=True)
+    assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+    assert np.array_equal(to_host_u16(a.k_pool), to_host_u16(b.k_pool))
+    assert np.array_equal(to_host_u16(a.v_pool), to_host_u16(b.v_pool))
+    assert np.array_equal(oa, ob)
+
+
+def test_workspace_needs_no_initialisation(pkv):
+    """The workspace may hold anything before a call (here all bits set),
+    and repeated calls on one workspace give the same bits."""
+    import torch
+    sh = _shape(32, 8, 128)
+    ctx = [4000, 3000, 17, 1, 2500, 800]
+    hc = w.host_case(sh, 95, context_lens=ctx)
+    dc = DevCase(hc)
+    B = len(ctx)
+    for part in (0, 256):
+        need = pkv.pkv_decode_workspace_bytes(B, 32, 8, 128, dc.max_ctx, part)
+        ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+        outs = []
+        for _ in range(3):
+            pkv.pkv_paged_attn_decode(dc.out, dc.q, dc.k_pool, dc.v_pool, dc.bt, dc.cl, sh.scale,
+                                      dc.max_ctx, part, workspace=ws, err_flag=dc.err)
+            torch.cuda.synchronize()
+            outs.append(dc.out.cpu().numpy())
+            ws.fill_(255)
+        assert int(dc.err.item()) == 0
+        assert np.isfinite(outs[0]).all()
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_decode_step_device_errors(pkv):
+    """Invalid context lengths and bad block ids through pkv_decode_step:
+    flagged, NaN rows, other sequences unaffected, nothing appended for the
+    bad sequences."""
+    sh = _shape(8, 2, 128)
+    hc = w.host_case(sh, 96, context_lens=[40, 90, 300, 77])
+    ref = gpu_step(pkv, DevCase(hc), partition=0, fused=True)
+    bt = hc.tables.block_tables.copy()
+    bt[1, (90 - 1) // 16] = hc.tables.num_blocks + 3      # the block being written
+    cl = hc.tables.context_lens.copy()
+    cl[2] = 0
+    dc = DevCase(hc)
+    dc.bt = to_dev_i32(bt)
+    dc.cl = to_dev_i32(cl)
+    k0 = to_host_u16(dc.k_pool)
+    got = gpu_step(pkv, dc, partition=0, fused=True)
+    err = int(dc.err.item())
+    assert err & pkv.PKV_DEVERR_BLOCK_ID and err & pkv.PKV_DEVERR_CONTEXT
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    # the split moves with the context lengths: the healthy rows agree to rounding
+    assert np.abs(got[[0, 3]] - ref[[0, 3]]).max() <= 1e-5
+    k1 = to_host_u16(dc.k_pool)
+    # only sequences 0 and 3 were appended
+    changed = np.nonzero((k0 != k1).any(axis=(1, 2, 3)))[0]
+    expect = {int(hc.tables.block_tables[0, 39 // 16]), int(hc.tables.block_tables[3, 76 // 16])}
+    assert set(int(b) for b in changed) <= expect
