@@ -162,6 +162,9 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  * A unit processed by one wavefront is written to out directly; otherwise
  * each wavefront leaves a partial (reference max, sum, accumulator) in the
  * workspace and a second kernel merges them (log-sum-exp rescaling).
+ * Loads: a sequence whose first block is also the first block of a
+ * neighbouring sequence (a shared prefix) is read through the caches; any
+ * other is streamed with non-temporal loads. This only affects speed.
  *
  * out        : device fp32 [num_seqs][n_q_heads][head_dim], written fully.
  * q          : device bf16 [num_seqs][n_q_heads][head_dim].
@@ -247,8 +250,8 @@ int pkv_decode_step(float* out, const void* q, const void* k_new,
                     size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 /* Wavefronts of the balanced split on the current device for this shape:
- * the number resident at once on the device (compute units x resident
- * wavefronts of the kernel), at most 8192, and at most one per 16 tiles of
+ * one per SIMD (4 per compute unit, fewer if the kernel's occupancy were
+ * lower), at most 8192, and at most one per 16 tiles of
  * units * ceil(max_context_len / 16). Queries the HIP runtime; returns
  * PKV_EINVAL / PKV_EUNSUPPORTED for bad shapes, PKV_EHIP without a device. */
 int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads,

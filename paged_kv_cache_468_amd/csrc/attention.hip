@@ -183,6 +183,18 @@ __device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_
   before_out = carry;
 }
 
+// Load policy of a sequence: if its first block is also the first block of
+// a neighbouring sequence in the batch, the sequences share a prefix and its
+// blocks are read again by others, so they are loaded through the caches;
+// otherwise every tile is read once and is streamed past them. Only the
+// speed depends on this guess, never the result.
+__device__ inline bool shares_first_block(const DecodeArgs& a, int s) {
+  const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+  const int first = row[0];
+  return (s > 0 && row[-a.max_blocks] == first) ||
+         (s + 1 < a.num_seqs && row[a.max_blocks] == first);
+}
+
 // One segment: tiles [ta, tb) of unit (h, qg, s). Leaves the running
 // reference max m (log2 units, per query row c, identical in the 4 lanes of
 // a column), the column's partial sum l (this lane's tokens only) and the
@@ -195,7 +207,11 @@ __device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_
 // depends on the order of this wave's own store and load), and when
 // store_new is set (the unit of the head's first query group) they are also
 // written into the pools.
-template <int D>
+//
+// STREAM selects non-temporal K/V loads (the tile is used once, so it is not
+// kept in cache at the expense of other data); without it the loads are
+// ordinary, for blocks that other sequences read too.
+template <int D, bool STREAM>
 __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h, int j_row,
                                        bool row_valid, int ctx, int ta, int tb, bool store_new,
                                        f32x4_t* acc, float& m_run, float& l_run) {
@@ -254,10 +270,19 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
       const int64_t base = (int64_t)blk * block_stride + head_off;
       const uint16_t* kt = a.k_pool + base;
       const uint16_t* vt = a.v_pool + base;
+      if (STREAM) {
 #pragma unroll
-      for (int m = 0; m < KM; ++m) kr[m] = *(const bf16x8_t*)(kt + k_lane_off + 32 * m);
+        for (int m = 0; m < KM; ++m)
+          kr[m] = __builtin_nontemporal_load((const bf16x8_t*)(kt + k_lane_off + 32 * m));
 #pragma unroll
-      for (int m = 0; m < VM; ++m) vr[m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
+        for (int m = 0; m < VM; ++m)
+          vr[m] = __builtin_nontemporal_load((const bf16x4_t*)(vt + v_lane_off + 256 * m));
+      } else {
+#pragma unroll
+        for (int m = 0; m < KM; ++m) kr[m] = *(const bf16x8_t*)(kt + k_lane_off + 32 * m);
+#pragma unroll
+        for (int m = 0; m < VM; ++m) vr[m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
+      }
     };
 
     auto compute_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
@@ -395,7 +420,7 @@ __device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int
 
 // Fixed partitions: one wave per (unit, partition).
 template <int D>
-__global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_fixed_kernel(DecodeArgs a) {
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -420,8 +445,10 @@ __global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
 
   f32x4_t acc[VM];
   float m_run, l_run;
-  const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run,
-                                     l_run);
+  const bool ok =
+      shares_first_block(a, s)
+          ? process_segment<D, false>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run, l_run)
+          : process_segment<D, true>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run, l_run);
   finish_segment<D>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, s, j, c,
                     row_valid, acc, m_run, l_run);
 }
@@ -431,7 +458,7 @@ __global__ __launch_bounds__(256) void paged_attn_fixed_kernel(DecodeArgs a) {
 // wave holding a unit's first tile records, for the merge kernel, the
 // unit's first partial slot and its number of partials (1: written here).
 template <int D>
-__global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_balanced_kernel(DecodeArgs a) {
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -491,7 +518,11 @@ __global__ __launch_bounds__(256) void paged_attn_balanced_kernel(DecodeArgs a) 
     }
     f32x4_t acc[VM];
     float m_run, l_run;
-    const bool ok = process_segment<D>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
+    const bool ok =
+        shares_first_block(a, s)
+            ? process_segment<D, false>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
+                                        m_run, l_run)
+            : process_segment<D, true>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
                                        m_run, l_run);
     finish_segment<D>(a, lane, ok, whole, (int64_t)w + u, s, j, c, row_valid, acc, m_run, l_run);
     cur += tb - pos;
@@ -616,9 +647,9 @@ static int64_t n_units_of(int num_seqs, int n_q, int n_kv) {
   return (int64_t)n_kv * qgroups * num_seqs;
 }
 
-// Waves of the balanced split: at most what the device holds resident at
-// once (so every wave runs concurrently), at most kMaxSplitWaves, and no
-// more than leaves kMinTilesPerWave tiles of the upper bound per wave.
+// Upper bound of the balanced split's wave count: at most kMaxSplitWaves,
+// and no more than leaves kMinTilesPerWave tiles of the upper bound of the
+// tile count per wave. The launch uses min(this, resident_waves()).
 static int64_t split_wave_cap(int num_seqs, int n_q, int n_kv, int max_ctx) {
   const int64_t tiles_ub = n_units_of(num_seqs, n_q, n_kv) * ((max_ctx + 15) / 16);
   int64_t w = (tiles_ub + kMinTilesPerWave - 1) / kMinTilesPerWave;
@@ -638,7 +669,10 @@ static int resident_waves(int head_dim) {
       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<128>, 256, 0)
       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<64>, 256, 0);
   if (e != hipSuccess || blocks < 1 || cus < 1) return -1;
-  slot = cus * blocks * kWaves;
+  // the split uses at most one wave per SIMD (4 per compute unit): longer
+  // ranges per wave, fewer per-wave start-up costs, and every wave resident
+  const int per_cu = blocks * kWaves < 4 ? blocks * kWaves : 4;
+  slot = cus * per_cu;
   return slot;
 }
 
