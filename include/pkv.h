@@ -250,8 +250,8 @@ int pkv_decode_step(float* out, const void* q, const void* k_new,
                     size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 /* Wavefronts of the balanced split on the current device for this shape:
- * one per SIMD (4 per compute unit, fewer if the kernel's occupancy were
- * lower), at most 8192, and at most one per 16 tiles of
+ * one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the
+ * kernel's occupancy were lower), at most 8192, and at most one per 16 tiles of
  * units * ceil(max_context_len / 16). Queries the HIP runtime; returns
  * PKV_EINVAL / PKV_EUNSUPPORTED for bad shapes, PKV_EHIP without a device. */
 int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads,

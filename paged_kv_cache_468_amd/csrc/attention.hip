@@ -195,6 +195,50 @@ __device__ inline bool shares_first_block(const DecodeArgs& a, int s) {
          (s + 1 < a.num_seqs && row[a.max_blocks] == first);
 }
 
+// The context lengths read once per wave: for up to 256 sequences each
+// lane loads its (at most four) lengths together and keeps their tile
+// counts in registers, from which both the total and the location of a
+// tile follow; longer batches use the chunked loops above.
+struct TileScan {
+  int n[4];   // tiles of sequences lane, lane + 64, lane + 128, lane + 192
+};
+
+__device__ inline int tile_scan_total(const DecodeArgs& a, int lane, TileScan& ts) {
+  if (a.num_seqs > 256) return total_seq_tiles(a, lane);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = lane + 64 * k;
+    ts.n[k] = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0;
+  }
+  int total = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) total += wave_sum(ts.n[k]);
+  return total;
+}
+
+__device__ inline void tile_scan_locate(const DecodeArgs& a, int lane, const TileScan& ts, int r,
+                                        int& s_out, int& before_out) {
+  if (a.num_seqs > 256) {
+    locate_tile(a, lane, r, s_out, before_out);
+    return;
+  }
+  int carry = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int incl = wave_inclusive_scan(ts.n[k], lane) + carry;
+    const uint64_t hit = __ballot(lane + 64 * k < a.num_seqs && incl > r);
+    if (hit) {
+      const int ln = __builtin_ctzll(hit);
+      s_out = 64 * k + ln;
+      before_out = __builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(ts.n[k], ln);
+      return;
+    }
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  s_out = a.num_seqs;   // not reached for r < total
+  before_out = carry;
+}
+
 // One segment: tiles [ta, tb) of unit (h, qg, s). Leaves the running
 // reference max m (log2 units, per query row c, identical in the 4 lanes of
 // a column), the column's partial sum l (this lane's tokens only) and the
@@ -465,7 +509,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
   if (w >= a.n_waves) return;
 
-  const int per_row = total_seq_tiles(a, lane);   // tiles of one (head, group)
+  TileScan ts;
+  const int per_row = tile_scan_total(a, lane, ts);   // tiles of one (head, group)
   const int n_hq = a.n_kv * a.n_qgroups;
   const int64_t total = (int64_t)n_hq * per_row;
   int64_t cur = total * w / a.n_waves;
@@ -478,7 +523,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (cur < total) {
       const int hq = (int)(cur / per_row);
       int s, before;
-      locate_tile(a, lane, (int)(cur - (int64_t)hq * per_row), s, before);
+      tile_scan_locate(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
       if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
       const int g = (hq % a.n_qgroups) * 16 + c;
       const int j = (hq / a.n_qgroups) * a.group + g;
@@ -494,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   int hq = (int)(cur / per_row);
   int s, before;
-  locate_tile(a, lane, (int)(cur - (int64_t)hq * per_row), s, before);
+  tile_scan_locate(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
   if (s >= a.num_seqs) return;   // unreachable for consistent context lengths
   int pos = (int)(cur - (int64_t)hq * per_row) - before;   // tile within the unit
   int ctx = a.context_lens[s];
@@ -669,9 +714,11 @@ static int resident_waves(int head_dim) {
       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<128>, 256, 0)
       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<64>, 256, 0);
   if (e != hipSuccess || blocks < 1 || cus < 1) return -1;
-  // the split uses at most one wave per SIMD (4 per compute unit): longer
-  // ranges per wave, fewer per-wave start-up costs, and every wave resident
-  const int per_cu = blocks * kWaves < 4 ? blocks * kWaves : 4;
+  // the split uses one wave per SIMD (4 per compute unit) for head_dim 128
+  // and two for head_dim 64, whose tiles are half the bytes: enough loads in
+  // flight, few per-wave start-up costs, and every wave resident
+  const int want = head_dim == 128 ? 4 : 8;
+  const int per_cu = blocks * kWaves < want ? blocks * kWaves : want;
   slot = cus * per_cu;
   return slot;
 }

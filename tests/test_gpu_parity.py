@@ -302,3 +302,17 @@ def test_decode_step_device_errors(pkv):
     changed = np.nonzero((k0 != k1).any(axis=(1, 2, 3)))[0]
     expect = {int(hc.tables.block_tables[0, 39 // 16]), int(hc.tables.block_tables[3, 76 // 16])}
     assert set(int(b) for b in changed) <= expect
+
+
+@pytest.mark.parametrize("B", [256, 257, 300])
+def test_balanced_split_large_batches(pkv, orc, B):
+    """Batches around and above 256 sequences, where the kernel switches from
+    context lengths held in registers to chunked scans."""
+    rnd = np.random.default_rng(B)
+    ctx = list(rnd.integers(1, 200, size=B))
+    hc = w.host_case(_shape(8, 2, 64), 300 + B, context_lens=ctx)
+    for fused in (False, True):
+        got = gpu_step(pkv, DevCase(hc), partition=0, fused=fused)
+        want, rc, _, _ = oracle_step(orc, hc)
+        assert rc == 0
+        assert max_abs(got, want) <= TOL
