@@ -2,10 +2,12 @@
 
 One layer of each shape is built at its real size (batch, heads, head
 size, context distribution, shared prefix), pools drawn on the GPU with a
-seeded generator and copied back for the oracle. The library runs append +
-decode in the launch configuration the benchmark times (balanced split
-over the device's resident waves, max_context_len = largest context + the benchmark's 23
-extra decode steps). Checked:
+seeded generator and copied back for the oracle. The library runs the
+benchmark's call in its launch configuration: pkv_decode_step (the append
+inside the attention's partition kernel, then the merge), the balanced
+split over the device's waves, max_context_len = largest context + the
+benchmark's 44 extra decode steps; one shape also runs the unfused
+kv_append + decode. Checked:
   * kv_append: the whole K and V pools after the append, bit for bit,
     against the oracle's append on the pre-append bytes;
   * decode: sampled (sequence, query head) rows, each recomputed by the
@@ -23,7 +25,7 @@ from gpu_util import TOL, max_abs, to_dev_i32, to_host_u16
 
 pytestmark = pytest.mark.gpu
 
-BENCH_EXTRA_STEPS = 23
+BENCH_EXTRA_STEPS = 44   # warm-up 3 + eager 20 + graph warm-up 1 + graph 20
 
 
 @pytest.fixture(scope="module")
@@ -39,8 +41,8 @@ def _one_layer(shape):
                    shape.ctx_hi, prefix_tokens=shape.prefix_tokens)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_layer(pkv, orc, cfg):
+@pytest.mark.parametrize("cfg,fused", [(2, True), (3, True), (4, True), (5, True), (4, False)])
+def test_full_size_layer(pkv, orc, cfg, fused):
     import torch
     shape = _one_layer(w.CONFIGS[cfg])
     seed = 40 + cfg
@@ -70,8 +72,13 @@ def test_full_size_layer(pkv, orc, cfg):
     torch.cuda.synchronize()
     k_ref, v_ref = to_host_u16(k_pool), to_host_u16(v_pool)
 
-    pkv.pkv_kv_append(k_pool, v_pool, k_new, v_new, bt, cl, err_flag=err)
-    pkv.pkv_paged_attn_decode(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx, err_flag=err)
+    if fused:   # the benchmark's call: append inside the attention kernel
+        pkv.pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, bt, cl, shape.scale, max_ctx,
+                            err_flag=err)
+    else:
+        pkv.pkv_kv_append(k_pool, v_pool, k_new, v_new, bt, cl, err_flag=err)
+        pkv.pkv_paged_attn_decode(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx,
+                                  err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     waves = pkv.pkv_decode_split_waves(B, shape.n_q, shape.n_kv, shape.d, max_ctx)
