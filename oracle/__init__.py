@@ -7,7 +7,7 @@ runs anything here, and nothing here imports the product path.
 
 Contents
   * ``liboracle.so`` (built from ``oracle.c`` by ``oracle/build.py``): append,
-    copy-on-write, decode in double precision, the KV-size closed form.
+    multi-token write, copy-on-write, decode in double precision, the KV-size closed form.
   * ``allocator_model``: a pure-Python reference model of the refcounted
     block allocator.
 
@@ -40,6 +40,9 @@ def _bind(path):
     lib.oracle_kv_append.restype = c_int
     lib.oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p,
                                      c_int, c_int, c_int, c_int, c_int]
+    lib.oracle_kv_write.restype = c_int
+    lib.oracle_kv_write.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p, i32p, c_int, c_int,
+                                    c_int, c_int, c_int, c_int]
     lib.oracle_copy_blocks.restype = c_int
     lib.oracle_copy_blocks.argtypes = [u16p, u16p, i32p, i32p, c_int, c_int,
                                        c_int, c_int]
@@ -106,6 +109,26 @@ class Oracle:
             _ptr(k_new, ctypes.c_uint16), _ptr(v_new, ctypes.c_uint16),
             _ptr(bt, ctypes.c_int32), _ptr(cl, ctypes.c_int32),
             num_seqs, bt.shape[1], num_blocks, n_kv, d)
+
+    def kv_write(self, k_pool, v_pool, k_src, v_src, block_tables, seq_rows, positions):
+        """In-place write of token i of k_src/v_src (uint16 [n, n_kv, d]) at
+        row seq_rows[i], position positions[i]. Returns the C status (0 ok,
+        -1 some token skipped)."""
+        k_src = _u16(k_src, "k_src")
+        v_src = _u16(v_src, "v_src")
+        bt = _i32(block_tables, "block_tables")
+        rows = _i32(seq_rows, "seq_rows")
+        pos = _i32(positions, "positions")
+        if k_pool.dtype != np.uint16 or v_pool.dtype != np.uint16 or not (
+                k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
+            raise TypeError("pools must be contiguous uint16 (written in place)")
+        n, n_kv, d = k_src.shape
+        num_blocks = k_pool.size // (n_kv * 16 * d)
+        return self.lib.oracle_kv_write(
+            _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+            _ptr(k_src, ctypes.c_uint16), _ptr(v_src, ctypes.c_uint16),
+            _ptr(bt, ctypes.c_int32), _ptr(rows, ctypes.c_int32), _ptr(pos, ctypes.c_int32),
+            n, bt.shape[0], bt.shape[1], num_blocks, n_kv, d)
 
     def copy_blocks(self, k_pool, v_pool, src, dst, n_kv, d):
         """In-place copy-on-write of whole blocks src[p] -> dst[p]."""
@@ -184,6 +207,10 @@ def kv_append(*a, **k):
 
 def copy_blocks(*a, **k):
     return default().copy_blocks(*a, **k)
+
+
+def kv_write(*a, **k):
+    return default().kv_write(*a, **k)
 
 
 def decode(*a, **k):

@@ -97,6 +97,42 @@ int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
 }
 
 /* ------------------------------------------------------------------------
+ * Write of arbitrary tokens ([M23] 23.4: a token's position selects its
+ * block through the sequence's table): token i of the source goes to row
+ * seq_rows[i] at position positions[i], i.e. slot (table[row][pos / 16],
+ * pos % 16). Bit copy. Returns 0, or -1 if some token was skipped (row,
+ * position or block id out of range); the others are still written. */
+int oracle_kv_write(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_src,
+                    const uint16_t* v_src, const int32_t* block_tables,
+                    const int32_t* seq_rows, const int32_t* positions, int n_tokens,
+                    int num_seqs, int max_blocks_per_seq, int num_blocks, int n_kv,
+                    int d) {
+  int status = 0;
+  for (int tok = 0; tok < n_tokens; ++tok) {
+    int row = seq_rows[tok];
+    int pos = positions[tok];
+    if (row < 0 || row >= num_seqs || pos < 0 || pos >= ORACLE_BLOCK * max_blocks_per_seq) {
+      status = -1;
+      continue;
+    }
+    int32_t blk = block_tables[(size_t)row * max_blocks_per_seq + pos / ORACLE_BLOCK];
+    if (blk < 0 || blk >= num_blocks) {
+      status = -1;
+      continue;
+    }
+    int slot = pos % ORACLE_BLOCK;
+    for (int h = 0; h < n_kv; ++h) {
+      for (int i = 0; i < d; ++i) {
+        size_t src = ((size_t)tok * n_kv + h) * d + i;
+        k_pool[k_index(blk, h, slot, i, n_kv, d)] = k_src[src];
+        v_pool[v_index(blk, h, slot, i, n_kv, d)] = v_src[src];
+      }
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------
  * Copy on write ([DSS] "Paged attention"): block dst[p] becomes a copy of
  * block src[p], K and V, every head and slot. */
 int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src,

@@ -86,6 +86,40 @@ def check_append_golden(orc):
     return k_pool, v_pool
 
 
+def check_write_golden(orc):
+    """A multi-token write against a pool image worked out by hand
+    (tests/golden/write_tiny.json), invalid tokens included."""
+    g = _load("write_tiny.json")
+    n_kv, d, nb = g["n_kv"], g["d"], g["num_blocks"]
+    k_pool = np.zeros(nb * n_kv * 16 * d, np.uint16)
+    v_pool = np.zeros_like(k_pool)
+    toks = np.array(g["tokens"], np.int32)
+    rc = orc.kv_write(k_pool, v_pool, np.array(g["k_src_bits"], np.uint16),
+                      np.array(g["v_src_bits"], np.uint16), np.array(g["block_tables"], np.int32),
+                      toks[:, 0].copy(), toks[:, 1].copy())
+    assert rc == g["expect_status"]
+    ek = np.zeros_like(k_pool)
+    ev = np.zeros_like(v_pool)
+    for i, val in g["expect_k_nonzero"].items():
+        ek[int(i)] = val
+    for i, val in g["expect_v_nonzero"].items():
+        ev[int(i)] = val
+    assert np.array_equal(k_pool, ek), np.nonzero(k_pool != ek)
+    assert np.array_equal(v_pool, ev), np.nonzero(v_pool != ev)
+
+
+def check_write_equals_append(orc):
+    """Writing each sequence's token at position ctx - 1 is the append."""
+    hc = w.host_case(_small_shape(8, 2, 64), 7, context_lens=[1, 16, 17, 40, 300], nan_fill=False)
+    k1, v1 = hc.k_pool.copy(), hc.v_pool.copy()
+    k2, v2 = hc.k_pool.copy(), hc.v_pool.copy()
+    cl = hc.tables.context_lens
+    assert orc.kv_append(k1, v1, hc.k_new, hc.v_new, hc.tables.block_tables, cl) == 0
+    assert orc.kv_write(k2, v2, hc.k_new, hc.v_new, hc.tables.block_tables,
+                        np.arange(len(cl), dtype=np.int32), (cl - 1).astype(np.int32)) == 0
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
 def check_decode_golden(orc):
     """Closed form worked by hand for the pool image above."""
     g = _load("append_tiny.json")
@@ -285,7 +319,8 @@ def check_invalid_inputs(orc):
     assert rc == -1 and np.isnan(out[0]).all() and np.isfinite(out[1]).all()
 
 
-ALL_CHECKS = [check_kv_sizes, check_kv_linearity, check_append_golden, check_decode_golden,
+ALL_CHECKS = [check_kv_sizes, check_kv_linearity, check_append_golden, check_write_golden,
+              check_write_equals_append, check_decode_golden,
               check_append_touches_only_its_slots, check_copy_blocks, check_single_token,
               check_constant_values, check_equal_keys, check_sdpa, check_large_logits,
               check_block_permutation, check_shared_prefix, check_group_equals_repeat,

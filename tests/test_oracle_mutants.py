@@ -28,8 +28,12 @@ MUTANTS = {
     "context_off_by_one": ("for (int t = 0; t < ctx; ++t) {\n    int32_t blk",
                            "for (int t = 0; t < ctx - 1; ++t) {\n    int32_t blk"),
     "no_normalisation": ("out_row[i] = num / denom;", "out_row[i] = num;"),
-    "append_slot_shift": ("int slot = pos % ORACLE_BLOCK;", "int slot = (pos + 1) % ORACLE_BLOCK;"),
-    "append_table_entry": ("+ pos / ORACLE_BLOCK];", "+ ctx / ORACLE_BLOCK];"),
+    "append_slot_shift": ("    int slot = pos % ORACLE_BLOCK;\n    for (int h = 0; h < n_kv; ++h) {\n      for (int i = 0; i < d; ++i) {\n        size_t src = ((size_t)s",
+                          "    int slot = (pos + 1) % ORACLE_BLOCK;\n    for (int h = 0; h < n_kv; ++h) {\n      for (int i = 0; i < d; ++i) {\n        size_t src = ((size_t)s"),
+    "append_table_entry": ("(size_t)s * max_blocks_per_seq + pos / ORACLE_BLOCK];", "(size_t)s * max_blocks_per_seq + ctx / ORACLE_BLOCK];"),
+    "write_slot_from_row": ("    int slot = pos % ORACLE_BLOCK;\n    for (int h = 0; h < n_kv; ++h) {\n      for (int i = 0; i < d; ++i) {\n        size_t src = ((size_t)tok",
+                            "    int slot = row % ORACLE_BLOCK;\n    for (int h = 0; h < n_kv; ++h) {\n      for (int i = 0; i < d; ++i) {\n        size_t src = ((size_t)tok"),
+    "write_source_row": ("        size_t src = ((size_t)tok * n_kv + h) * d + i;", "        size_t src = ((size_t)row * n_kv + h) * d + i;"),
     "copy_k_only": ("      v_pool[(size_t)dst[p] * per_block + e] = v_pool[(size_t)src[p] * per_block + e];\n", ""),
     "kv_bytes_no_two": ("return (uint64_t)2 * (uint64_t)n_layers", "return (uint64_t)n_layers"),
     "kv_bytes_no_precision": (" *\n         (uint64_t)bytes_per_value;", ";"),
