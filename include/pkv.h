@@ -145,6 +145,29 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * kv_write: scatter arbitrary tokens' keys and values into the pools
+ * ([M23] 23.4: a position selects its block through the sequence's table).
+ * Token t of k_src / v_src goes to row seq_rows[t] at position positions[t]:
+ * K/V element (bt[row][pos/16], h, pos%16, i). For the keys and values a
+ * prefill computed for a newly admitted request, or recomputed for a
+ * preempted one ([DSS] "Continuous batching": admit it, run its prefill;
+ * "Scheduling": preemption by recompute). Pure bit copy.
+ *
+ * k_src, v_src : device bf16 [n_tokens][n_kv_heads][head_dim].
+ * seq_rows, positions : device int32 [n_tokens].
+ * block_tables : device int32 [num_seqs][max_blocks_per_seq].
+ * The blocks written must not be shared with another sequence. Device
+ * errors: a row outside [0, num_seqs) or a position outside
+ * [0, 16*max_blocks_per_seq) -> PKV_DEVERR_CONTEXT; a table entry outside
+ * [0, num_blocks) -> PKV_DEVERR_BLOCK_ID; that token is skipped. */
+int pkv_kv_write(void* k_pool, void* v_pool, const void* k_src,
+                 const void* v_src, const int32_t* block_tables,
+                 const int32_t* seq_rows, const int32_t* positions,
+                 int32_t n_tokens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                 int32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------
  * paged_attn_decode: the attention above, for every sequence and query head.
  *
  * Work split. A unit is one (sequence, KV head, group of up to 16 of its
@@ -320,6 +343,77 @@ int pkv_seq_fork(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
 /* A finished sequence: decref each of its n_blocks blocks.
  * All-or-nothing: on an invalid id nothing is changed. */
 int pkv_seq_release(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
+
+/* ------------------------------------------------------------------------
+ * Continuous batching ([DSS] "Continuous batching": before every token step
+ * the scheduler releases the cache blocks of finished sequences, admits
+ * waiting requests into the freed space and runs one decode step for what
+ * is resident; [M23] 23.3; [SLS] "Batching: static to continuous";
+ * [DSS] "Scheduling: when prefill meets decode": when memory runs out a
+ * sequence yields, its blocks discarded and recomputed on resumption).
+ *
+ * Host only, not thread-safe. The batcher owns a block allocator of
+ * num_blocks blocks and, if prefix_tokens > 0, the blocks of a shared prefix
+ * (a system prompt) that requests submitted with shares_prefix begin with.
+ *
+ * pkv_batcher_step, in order:
+ *  1. every request resident in the previous plan has produced one token;
+ *     those that have produced gen_len are finished and release their
+ *     blocks (finished_ids);
+ *  2. every other resident request grows by this step's token
+ *     (pkv_seq_grow: a block at each 16-token boundary, copy on write of a
+ *     shared last block). With no free block, the most recently admitted
+ *     resident request is preempted (preempted_ids): its blocks are
+ *     released and it returns to the front of the queue with everything it
+ *     has so far as its prompt (recomputed on re-admission);
+ *  3. waiting requests are admitted in submission order while the batch
+ *     holds fewer than max_batch requests and the free blocks cover the
+ *     request's prompt plus its first token plus one block per resident
+ *     request. A prefix-sharing request forks the prefix's blocks; the
+ *     prefix's partly filled last block is copied on write before its own
+ *     tokens go there.
+ * The caller then, on the device and for every layer: copies the cow pairs
+ * (pkv_copy_blocks), writes the fill tokens' keys and values (pkv_kv_write;
+ * a prompt's prefill output, or a preempted request's recomputed tokens),
+ * uploads the tables and context lengths, and runs pkv_decode_step for the
+ * plan's rows. The plan's arrays stay valid until the next step. */
+typedef struct pkv_batcher pkv_batcher;
+
+typedef struct {
+  int32_t num_seqs;              /* resident requests, rows 0 .. num_seqs-1 (admission order) */
+  int32_t max_blocks_per_seq;    /* row stride of block_tables */
+  const int32_t* block_tables;   /* [num_seqs][max_blocks_per_seq], -1 padded */
+  const int32_t* context_lens;   /* [num_seqs], each including this step's token */
+  const int64_t* request_ids;    /* [num_seqs] */
+  int32_t n_cow;                 /* copy-on-write pairs, to copy before any write */
+  const int32_t* cow_src;
+  const int32_t* cow_dst;
+  int32_t n_fill;                /* prompt tokens to write this step */
+  const int32_t* fill_rows;      /* [n_fill] row of this plan */
+  const int32_t* fill_positions; /* [n_fill] position within that row's sequence */
+  int32_t n_finished;            /* requests finished and released in this step */
+  const int64_t* finished_ids;
+  int32_t n_preempted;           /* requests preempted in this step */
+  const int64_t* preempted_ids;
+  int32_t num_free_blocks;       /* after this step's allocations (occupancy) */
+  int32_t num_waiting;
+} pkv_step_plan;
+
+/* max_blocks_per_seq: the table width (longest request / 16, rounded up). */
+int pkv_batcher_create(int32_t num_blocks, int32_t max_batch,
+                       int32_t max_blocks_per_seq, int32_t prefix_tokens,
+                       pkv_batcher** out);
+void pkv_batcher_destroy(pkv_batcher* b); /* NULL ok */
+/* The prefix's table (*table, max_blocks_per_seq entries) and its number of
+ * blocks; the caller writes the prefix's keys and values through it once. */
+int32_t pkv_batcher_prefix_table(const pkv_batcher* b, const int32_t** table);
+/* Queue a request: prompt_len >= 1 tokens (at least the prefix if
+ * shares_prefix), then gen_len >= 1 decode steps. EINVAL for a bad shape or
+ * more than 16*max_blocks_per_seq tokens in all; ENOMEM if it could never
+ * fit in the pool beside the prefix. */
+int pkv_batcher_submit(pkv_batcher* b, int64_t request_id, int32_t prompt_len,
+                       int32_t gen_len, int32_t shares_prefix);
+int pkv_batcher_step(pkv_batcher* b, pkv_step_plan* plan);
 
 #ifdef __cplusplus
 }

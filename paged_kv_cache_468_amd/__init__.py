@@ -52,6 +52,8 @@ SIGNATURES = {
     "pkv_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _vp, _vp]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
     "pkv_block_alloc": (ctypes.c_int, [_vp, _i32p]),
@@ -63,7 +65,29 @@ SIGNATURES = {
     "pkv_seq_grow": (ctypes.c_int, [_vp, _i32p, _i32p, _i32, _i32, _i32p, _i32p]),
     "pkv_seq_fork": (ctypes.c_int, [_vp, _i32p, _i32]),
     "pkv_seq_release": (ctypes.c_int, [_vp, _i32p, _i32]),
+    "pkv_batcher_create": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pkv_batcher_destroy": (None, [_vp]),
+    "pkv_batcher_prefix_table": (_i32, [_vp, ctypes.POINTER(_i32p)]),
+    "pkv_batcher_submit": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32]),
+    "pkv_batcher_step": (ctypes.c_int, [_vp, ctypes.c_void_p]),
 }
+
+
+class StepPlan(ctypes.Structure):
+    """pkv_step_plan (include/pkv.h)."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("block_tables", ctypes.POINTER(ctypes.c_int32)),
+        ("context_lens", ctypes.POINTER(ctypes.c_int32)),
+        ("request_ids", ctypes.POINTER(ctypes.c_int64)),
+        ("n_cow", ctypes.c_int32), ("cow_src", ctypes.POINTER(ctypes.c_int32)),
+        ("cow_dst", ctypes.POINTER(ctypes.c_int32)),
+        ("n_fill", ctypes.c_int32), ("fill_rows", ctypes.POINTER(ctypes.c_int32)),
+        ("fill_positions", ctypes.POINTER(ctypes.c_int32)),
+        ("n_finished", ctypes.c_int32), ("finished_ids", ctypes.POINTER(ctypes.c_int64)),
+        ("n_preempted", ctypes.c_int32), ("preempted_ids", ctypes.POINTER(ctypes.c_int64)),
+        ("num_free_blocks", ctypes.c_int32), ("num_waiting", ctypes.c_int32),
+    ]
 
 
 class PkvError(RuntimeError):
@@ -283,6 +307,29 @@ def pkv_paged_attn_merge(out, q, k_pool, v_pool, block_tables, context_lens, sca
     _check(lib.pkv_paged_attn_merge(*args), "pkv_paged_attn_merge")
 
 
+def pkv_kv_write(k_pool, v_pool, k_src, v_src, block_tables, seq_rows, positions, err_flag=None,
+                 stream=None):
+    """Token t of k_src / v_src ([n, n_kv, d] bf16) into row seq_rows[t] at
+    position positions[t] (both int32 [n] on the device)."""
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(k_src, "k_src", torch.bfloat16, 3)
+    _dev(v_src, "v_src", torch.bfloat16, 3)
+    n = k_src.shape[0]
+    if tuple(k_src.shape) != (n, n_kv, d) or tuple(v_src.shape) != (n, n_kv, d):
+        raise ValueError("k_src / v_src: expected [n_tokens, n_kv, head_dim]")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    rows = _dev(seq_rows, "seq_rows", torch.int32, 1)
+    pos = _dev(positions, "positions", torch.int32, 1)
+    if seq_rows.shape[0] != n or positions.shape[0] != n:
+        raise ValueError("seq_rows / positions: one entry per token")
+    _check(lib.pkv_kv_write(_dev(k_pool, "k_pool", torch.bfloat16),
+                            _dev(v_pool, "v_pool", torch.bfloat16),
+                            _dev(k_src, "k_src", torch.bfloat16), _dev(v_src, "v_src", torch.bfloat16),
+                            bt, rows, pos, n, block_tables.shape[0], block_tables.shape[1], nb, n_kv,
+                            d, _flag(err_flag), _stream(stream)), "pkv_kv_write")
+
+
 def pkv_copy_blocks(k_pool, v_pool, src, dst, err_flag=None, stream=None):
     torch = _torch()
     nb, n_kv, d = _pool_dims(k_pool, v_pool)
@@ -451,3 +498,71 @@ def prepare_copy_blocks(k_pool, v_pool, src, dst, err_flag=None, stream=None):
     args = (_dev(k_pool, "k_pool", torch.bfloat16), _dev(v_pool, "v_pool", torch.bfloat16), s, t,
             src.shape[0], nb, n_kv, d, _flag(err_flag), _stream(stream))
     return PreparedCall("pkv_copy_blocks", args, (k_pool, v_pool, src, dst, err_flag))
+
+
+# ---------------------------------------------------------------------------
+# continuous batching (host)
+
+def _arr(ptr, n, dtype):
+    if n == 0:
+        return np.zeros(0, dtype)
+    return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+
+class Plan:
+    """One step of pkv_batcher_step, copied into numpy arrays."""
+
+    def __init__(self, c: StepPlan):
+        n, mb = c.num_seqs, c.max_blocks_per_seq
+        self.num_seqs = n
+        self.block_tables = _arr(c.block_tables, n * mb, np.int32).reshape(n, mb)
+        self.context_lens = _arr(c.context_lens, n, np.int32)
+        self.request_ids = _arr(c.request_ids, n, np.int64)
+        self.cow_src = _arr(c.cow_src, c.n_cow, np.int32)
+        self.cow_dst = _arr(c.cow_dst, c.n_cow, np.int32)
+        self.fill_rows = _arr(c.fill_rows, c.n_fill, np.int32)
+        self.fill_positions = _arr(c.fill_positions, c.n_fill, np.int32)
+        self.finished_ids = _arr(c.finished_ids, c.n_finished, np.int64)
+        self.preempted_ids = _arr(c.preempted_ids, c.n_preempted, np.int64)
+        self.num_free_blocks = c.num_free_blocks
+        self.num_waiting = c.num_waiting
+
+
+class Batcher:
+    """Owner of a pkv_batcher handle (host memory, one thread)."""
+
+    def __init__(self, num_blocks: int, max_batch: int, max_blocks_per_seq: int,
+                 prefix_tokens: int = 0):
+        h = ctypes.c_void_p()
+        _check(lib.pkv_batcher_create(num_blocks, max_batch, max_blocks_per_seq, prefix_tokens,
+                                      ctypes.byref(h)), "pkv_batcher_create")
+        self._h = h
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def close(self):
+        if self._h:
+            lib.pkv_batcher_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def prefix_table(self):
+        """(table int32 [max_blocks_per_seq], number of prefix blocks)."""
+        p = _i32p()
+        n = lib.pkv_batcher_prefix_table(self._h, ctypes.byref(p))
+        if n < 0:
+            raise PkvError(n, "pkv_batcher_prefix_table")
+        return _arr(p, self.max_blocks_per_seq, np.int32), int(n)
+
+    def submit(self, request_id: int, prompt_len: int, gen_len: int, shares_prefix: bool = False):
+        _check(lib.pkv_batcher_submit(self._h, int(request_id), int(prompt_len), int(gen_len),
+                                      1 if shares_prefix else 0), "pkv_batcher_submit")
+
+    def step(self) -> Plan:
+        c = StepPlan()
+        _check(lib.pkv_batcher_step(self._h, ctypes.byref(c)), "pkv_batcher_step")
+        return Plan(c)

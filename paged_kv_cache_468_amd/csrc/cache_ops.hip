@@ -1,4 +1,5 @@
-// Writes into the paged pools: append of the step's new K/V, and whole-block
+// Writes into the paged pools: append of the step's new K/V, a write of
+// arbitrary tokens (a prompt's K/V after its prefill), and whole-block
 // copies for copy-on-write. Layouts are the ones include/pkv.h documents.
 //
 // Append ("Module 23: Serving", 23.4; "Designing an LLM serving system",
@@ -52,6 +53,42 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   for (int i = lane; i < d; i += 64) vdst[(int64_t)i * 16] = vn[i];
 }
 
+// Write of arbitrary tokens: token t goes to row seq_rows[t] at position
+// positions[t]. One wave per (token, KV head), the same stores as the
+// append.
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_rows,
+    const int32_t* __restrict__ positions, int n_tokens, int num_seqs, int max_blocks,
+    int num_blocks, int n_kv, int d, int32_t* err_flag) {
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= n_tokens * n_kv) return;
+  const int tok = unit / n_kv;
+  const int h = unit % n_kv;
+  const int row = seq_rows[tok];
+  const int pos = positions[tok];
+  if (row < 0 || row >= num_seqs || pos < 0 || pos >= 16 * max_blocks) {
+    if (h == 0 && lane == 0 && err_flag) atomicOr(err_flag, PKV_DEVERR_CONTEXT);
+    return;
+  }
+  const int blk = block_tables[(int64_t)row * max_blocks + pos / 16];
+  if (blk < 0 || blk >= num_blocks) {
+    if (h == 0 && lane == 0 && err_flag) atomicOr(err_flag, PKV_DEVERR_BLOCK_ID);
+    return;
+  }
+  const int slot = pos % 16;
+  const int64_t tile = ((int64_t)blk * n_kv + h) * 16 * d;
+  const uint16_t* kn = k_src + ((int64_t)tok * n_kv + h) * d;
+  const uint16_t* vn = v_src + ((int64_t)tok * n_kv + h) * d;
+  uint32_t* kdst = (uint32_t*)(k_pool + tile + (int64_t)slot * d);
+  const uint32_t* ksrc = (const uint32_t*)kn;
+  for (int i = lane; i < d / 2; i += 64) kdst[i] = ksrc[i];
+  uint16_t* vdst = v_pool + tile + slot;
+  for (int i = lane; i < d; i += 64) vdst[(int64_t)i * 16] = vn[i];
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
     uint4* __restrict__ k_pool, uint4* __restrict__ v_pool, const int32_t* __restrict__ src,
     const int32_t* __restrict__ dst, int num_blocks, int64_t chunks_per_block, int32_t* err_flag) {
@@ -92,6 +129,26 @@ extern "C" int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, cons
                      (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
                      (const uint16_t*)v_new, block_tables, context_lens, num_seqs,
                      max_blocks_per_seq, num_blocks, n_kv_heads, head_dim, err_flag);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+extern "C" int pkv_kv_write(void* k_pool, void* v_pool, const void* k_src, const void* v_src,
+                            const int32_t* block_tables, const int32_t* seq_rows,
+                            const int32_t* positions, int32_t n_tokens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t* err_flag, void* stream) {
+  if (n_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || n_kv_heads < 1)
+    return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (n_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_src || !v_src || !block_tables || !seq_rows || !positions)
+    return PKV_EINVAL;
+  if ((int64_t)n_tokens * n_kv_heads > INT32_MAX / 2) return PKV_EINVAL;
+  const unsigned grid = (unsigned)(((int64_t)n_tokens * n_kv_heads + 3) / 4);
+  hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_src,
+                     (const uint16_t*)v_src, block_tables, seq_rows, positions, n_tokens,
+                     num_seqs, max_blocks_per_seq, num_blocks, n_kv_heads, head_dim, err_flag);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

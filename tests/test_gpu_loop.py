@@ -1,0 +1,135 @@
+"""Continuous batching on the GPU, step by step against the oracle.
+
+Requests arrive over time, some beginning with a shared prefix whose last
+block is partly filled, in a pool small enough that requests are preempted
+and recomputed. Every step runs the native batcher, then per layer the
+copy-on-write copies, the prompt writes (pkv_kv_write) and pkv_decode_step.
+Checked at every step:
+  * the pools, bit for bit, against a host mirror that applies the same
+    plan with the oracle's copy, write and append;
+  * every resident request's output, within 1e-3, against the oracle run on
+    a cache rebuilt contiguously from that request's token history (its
+    keys and values are a fixed function of (layer, request, position), the
+    shared prefix's where it shares), i.e. attention recomputed from a
+    contiguous cache;
+  * every request finishes after exactly gen_len decode steps.
+"""
+import numpy as np
+import pytest
+
+import workload as w
+import loop_util as lu
+from gpu_util import TOL, max_abs, to_dev_bf16, to_host_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_468_amd as lib
+    return lib
+
+
+@pytest.mark.parametrize("d,n_kv,n_tok", [(64, 2, 1), (128, 8, 300), (64, 1, 4099)])
+def test_kv_write_bit_exact(pkv, orc, d, n_kv, n_tok):
+    """Prompt tokens written at (row, position) through the tables, against
+    the oracle's write: bit for bit, with invalid rows, positions and table
+    entries skipped and flagged on both sides."""
+    import torch
+    num_blocks, num_seqs, max_blocks = 700, 9, 40
+    g = w.rng(31 + n_tok, 8)
+    tables = g.permutation(num_blocks)[:num_seqs * max_blocks].astype(np.int32)
+    tables = tables.reshape(num_seqs, max_blocks)
+    tables[3, 5:] = -1                            # a short table
+    # distinct (row, position) pairs, a few invalid
+    flat = g.choice(num_seqs * 16 * max_blocks, size=n_tok, replace=False)
+    rows = (flat // (16 * max_blocks)).astype(np.int32)
+    pos = (flat % (16 * max_blocks)).astype(np.int32)
+    if n_tok > 10:
+        rows[1], pos[2], pos[3] = num_seqs, 16 * max_blocks, -1
+    ks = w.normal_bf16(g, (n_tok, n_kv, d))
+    vs = w.normal_bf16(g, (n_tok, n_kv, d))
+    sk, sv = w.pool_shapes(num_blocks, n_kv, d)
+    hk = w.normal_bf16(g, sk)
+    hv = w.normal_bf16(g, sv)
+    dk, dv = to_dev_bf16(hk), to_dev_bf16(hv)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_kv_write(dk, dv, to_dev_bf16(ks), to_dev_bf16(vs), torch.from_numpy(tables).cuda(),
+                     torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda(), err_flag=err)
+    torch.cuda.synchronize()
+    rc = orc.kv_write(hk, hv, ks, vs, tables, rows, pos)
+    skipped = bool((rows >= num_seqs).any() or (pos < 0).any() or (pos >= 16 * max_blocks).any()
+                   or (tables[np.clip(rows, 0, num_seqs - 1),
+                              np.clip(pos, 0, 16 * max_blocks - 1) // 16] < 0).any())
+    assert (rc == -1) == skipped
+    assert (int(err.item()) != 0) == skipped
+    assert np.array_equal(to_host_u16(dk), hk)
+    assert np.array_equal(to_host_u16(dv), hv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_continuous_batching_matches_contiguous_recompute(pkv, orc, d):
+    import torch
+    from paged_kv_cache_468_amd.loop import ServingLoop
+    L = lu.L
+    scale = 1.0 / np.sqrt(d)
+    reqs = lu.requests(d)
+    hist = lu.History(d, {rid: r[3] for rid, r in reqs.items()})
+    b = pkv.Batcher(lu.NUM_BLOCKS, lu.MAX_BATCH, lu.MAX_BLOCKS, lu.PREFIX)
+    sk, sv = w.pool_shapes(lu.NUM_BLOCKS, lu.N_KV, d)
+    host_k = [np.full(sk, w.BF16_NAN, np.uint16) for _ in range(L)]
+    host_v = [np.full(sv, w.BF16_NAN, np.uint16) for _ in range(L)]
+    kp = [to_dev_bf16(x) for x in host_k]
+    vp = [to_dev_bf16(x) for x in host_v]
+    loop = ServingLoop(b, kp, vp, lu.N_Q, scale, lu.MAX_BATCH)
+
+    # the shared prefix, written once through its own table
+    ptable, _ = b.prefix_table()
+    loop.write_prefix([to_dev_bf16(hist.pk[l]) for l in range(L)],
+                      [to_dev_bf16(hist.pv[l]) for l in range(L)])
+    for l in range(L):
+        assert orc.kv_write(host_k[l], host_v[l], hist.pk[l], hist.pv[l], ptable.reshape(1, -1),
+                            np.zeros(lu.PREFIX, np.int32),
+                            np.arange(lu.PREFIX, dtype=np.int32)) == 0
+
+    steps_seen, finished, preempted = {}, [], 0
+    for step in range(2000):
+        for rid, (arr, prompt, gen, shares) in reqs.items():
+            if arr == step:
+                b.submit(rid, prompt, gen, shares)
+        p = loop.schedule()
+        n = p.num_seqs
+        ids = [int(x) for x in p.request_ids]
+        finished += [int(x) for x in p.finished_ids]
+        preempted += len(p.preempted_ids)
+        if n == 0 and p.num_waiting == 0 and step > 30:
+            break
+        fill = [hist.fill(l, ids, p) for l in range(L)]
+        new = [hist.new_token(l, ids, p) for l in range(L)]
+        g = w.rng(50000 + step, 7)
+        q_h = [w.normal_bf16(g, (n, lu.N_Q, d)) for _ in range(L)]
+        if step % 25 == 0:
+            print(f"d={d} step {step}: {n} rows, {len(p.fill_rows)} fill, {len(p.cow_src)} cow",
+                  flush=True)
+        out = loop.run(lambda l: (to_dev_bf16(fill[l][0]), to_dev_bf16(fill[l][1])),
+                       [to_dev_bf16(x) for x in q_h], [to_dev_bf16(x[0]) for x in new],
+                       [to_dev_bf16(x[1]) for x in new])
+        torch.cuda.synchronize()
+        assert int(loop.err.item()) == 0, f"step {step}"
+        got = out.cpu().numpy().astype(np.float64)
+        for l in range(L):
+            lu.mirror_step(orc, host_k[l], host_v[l], p, fill[l], new[l][0], new[l][1], d)
+            assert np.array_equal(to_host_u16(kp[l]), host_k[l]), f"K pool differs at step {step}"
+            assert np.array_equal(to_host_u16(vp[l]), host_v[l]), f"V pool differs at step {step}"
+            if n:
+                want = lu.contiguous_decode(orc, q_h[l], hist, l, ids, p.context_lens, scale)
+                err = max_abs(got[l], want)
+                assert err <= TOL, f"step {step} layer {l}: {err}"
+        for rid in ids:
+            steps_seen[rid] = steps_seen.get(rid, 0) + 1
+
+    assert sorted(finished) == sorted(reqs)
+    assert all(steps_seen[rid] == reqs[rid][2] for rid in reqs)
+    assert preempted > 0, "the pool was meant to force preemption"
