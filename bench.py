@@ -398,6 +398,106 @@ def stored_traffic(workload, kernel):
     return rec["hbm_bytes_per_dispatch"], None
 
 
+def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
+    """Continuous batching at a model shape: requests with prompts uniform in
+    [prefix, ctx_hi - 256] tokens (all beginning with the shared prefix when
+    the shape has one) and 32..256 generated tokens, queued ahead; the
+    batcher keeps max_batch of them resident, finished ones release their
+    blocks and waiting ones are admitted with their prompt keys/values
+    written (pkv_kv_write). Every step is the whole loop: the batcher's
+    plan, its upload, per layer copies + prompt writes + pkv_decode_step,
+    and a synchronisation (a server samples from the outputs before the
+    next step). Keys, values and queries are seeded N(0,1) on the device."""
+    from paged_kv_cache_468_amd.loop import ServingLoop
+    L, B, n_kv, d = shape.n_layers, shape.batch, shape.n_kv, shape.d
+    max_blocks = -(-shape.ctx_hi // BLOCK)
+    prefix = shape.prefix_tokens
+    num_blocks = B * max_blocks + -(-prefix // BLOCK)
+    b = pkv.Batcher(num_blocks, B, max_blocks, prefix)
+    rnd = np.random.default_rng(seed)
+    n_req = 4000
+    lo = max(prefix, shape.ctx_lo)
+    prompts = rnd.integers(lo, shape.ctx_hi - 256 + 1, n_req)
+    gens = rnd.integers(32, 257, n_req)
+    for rid in range(n_req):
+        b.submit(rid, int(prompts[rid]), int(gens[rid]), prefix > 0)
+    ks, vs = w.pool_shapes(num_blocks, n_kv, d)
+    kp = [torch.empty(ks, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    vp = [torch.empty(vs, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    for l in range(L):
+        w.device_normal_bf16_(kp[l], seed * 1000 + 2 * l)
+        w.device_normal_bf16_(vp[l], seed * 1000 + 2 * l + 1)
+    cap = B * BLOCK * max_blocks
+    src_k = torch.empty((cap, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    src_v = torch.empty_like(src_k)
+    w.device_normal_bf16_(src_k, seed * 1000 + 900)
+    w.device_normal_bf16_(src_v, seed * 1000 + 901)
+    q = torch.empty((L, B, shape.n_q, d), dtype=torch.bfloat16, device="cuda")
+    kn = torch.empty((L, B, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    for i, t in enumerate((q, kn, vn)):
+        w.device_normal_bf16_(t, seed * 1000 + 950 + i)
+    loop = ServingLoop(b, kp, vp, shape.n_q, shape.scale, B)
+    if prefix:
+        loop.write_prefix([src_k[:prefix]] * L, [src_v[:prefix]] * L)
+    stream = loop.stream
+    per_token = 2 * n_kv * d * 2 * L          # K and V bytes of one cached token, all layers
+
+    def one_step(acc):
+        t = time.perf_counter()
+        p = loop.schedule()
+        acc["host_s"] += time.perf_counter() - t
+        n, n_fill = p.num_seqs, len(p.fill_rows)
+        loop.run(lambda l: (src_k[:n_fill], src_v[:n_fill]), q[:, :n], kn[:, :n], vn[:, :n])
+        stream.synchronize()
+        acc["tokens"] += n
+        acc["kv_bytes"] += per_token * int(p.context_lens.astype(np.int64).sum())
+        acc["fill"] += n_fill
+        ids = set(p.request_ids.tolist())
+        acc["admitted"] += len(ids - acc["prev"])
+        acc["prev"] = ids
+        acc["finished"] += len(p.finished_ids)
+        acc["cow"] += len(p.cow_src)
+
+    def fresh():
+        return dict(host_s=0.0, tokens=0, kv_bytes=0, fill=0, admitted=0, finished=0, cow=0,
+                    prev=set())
+
+    acc = fresh()
+    for _ in range(warmup):
+        one_step(acc)
+    torch.cuda.synchronize()
+    prev = acc["prev"]
+    acc = fresh()
+    acc["prev"] = prev
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(acc)
+        if (i + 1) % 100 == 0:
+            log(f"[loop] {i + 1}/{steps} steps")
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert int(loop.err.item()) == 0, "device error flag set in the loop"
+    return {
+        "metric": "continuous-batching decode tokens/s (whole loop)",
+        "value": acc["tokens"] / dt, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": 1e3 * dt / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "continuous-batching-" + name, "layers": L, "max_batch": B, "n_q_heads": shape.n_q,
+                   "n_kv_heads": n_kv, "head_dim": d, "prefix_tokens": prefix,
+                   "prompt_tokens": [int(lo), int(shape.ctx_hi - 256)], "gen_tokens": [32, 256],
+                   "blocks_per_layer": num_blocks, "seed": seed},
+        "kv_gbs": acc["kv_bytes"] / dt / 1e9,
+        "pct_hbm_peak": 100 * acc["kv_bytes"] / dt / 1e9 / HBM_PEAK_GBS,
+        "rows_per_step": acc["tokens"] / steps,
+        "host_ms_per_step": 1e3 * acc["host_s"] / steps,
+        "prompt_tokens_written_per_step": acc["fill"] / steps,
+        "admitted_per_step": acc["admitted"] / steps,
+        "finished_per_step": acc["finished"] / steps,
+        "cow_per_step": acc["cow"] / steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +512,10 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per layer (kv_append, partition, merge) instead of pkv_decode_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    ap.add_argument("--loop", action="store_true",
+                    help="continuous batching instead: the batcher's plans carried out step by step")
+    ap.add_argument("--loop-steps", type=int, default=300)
+    ap.add_argument("--loop-warmup", type=int, default=300)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -428,6 +532,11 @@ def main():
     import paged_kv_cache_468_amd as pkv
     torch.cuda.set_device(0)
     shape = w.CONFIGS[args.config]
+    if args.loop:
+        log(f"[bench] continuous batching, {WORKLOAD_NAMES[args.config]}")
+        line = loop_bench(pkv, torch, shape, WORKLOAD_NAMES[args.config], args.seed, args.loop_steps, args.loop_warmup)
+        print(json.dumps(line), flush=True)
+        return
     extra = args.warmup + 2 * args.steps + 1   # one token per step: eager, graph warm-up, graph
 
     share_main = (not args.no_share) and shape.prefix_tokens > 0

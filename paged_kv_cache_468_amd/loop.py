@@ -5,7 +5,9 @@ every token step finished sequences release their blocks, waiting requests
 are admitted, one decode step runs for the resident batch):
   1. pkv_batcher_step (native, host): releases, growth, preemption,
      admission; the plan;
-  2. the plan's tables and context lengths go to the device;
+  2. the plan's tables, context lengths, copy pairs and fill coordinates go
+     to the device from pinned staging buffers, asynchronously, on the
+     loop's stream;
   3. for every layer, in stream order: pkv_copy_blocks for the plan's
      copy-on-write pairs, pkv_kv_write for the prompt tokens admitted this
      step (their keys and values come from the caller: a prefill's output,
@@ -15,6 +17,9 @@ are admitted, one decode step runs for the resident batch):
 Everything runs in the library's kernels and its native batcher; this
 module only moves arguments. The keys, values and queries are the
 caller's: in a model they come from the layers' projections.
+
+The staging buffers are reused every step: schedule() waits until the
+previous step's uploads have left them (an event, not a device-wide sync).
 """
 import numpy as np
 
@@ -38,15 +43,37 @@ class ServingLoop:
         self.max_blocks = batcher.max_blocks_per_seq
         self.max_ctx = 16 * self.max_blocks
         dev = k_pools[0].device
-        self.stream = stream
-        self.bt = torch.full((max_batch, self.max_blocks), -1, dtype=torch.int32, device=dev)
-        self.cl = torch.ones((max_batch,), dtype=torch.int32, device=dev)
+        self.dev = dev
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        i32 = torch.int32
+        self.bt = torch.full((max_batch, self.max_blocks), -1, dtype=i32, device=dev)
+        self.cl = torch.ones((max_batch,), dtype=i32, device=dev)
+        self.bt_h = torch.empty((max_batch, self.max_blocks), dtype=i32, pin_memory=True)
+        self.cl_h = torch.empty((max_batch,), dtype=i32, pin_memory=True)
+        # copy pairs (src, dst) and fill coordinates (row, position); grown on demand
+        self.cow_h = self.cow = self.fill_h = self.fill = None
+        self._size_cow(2 * max_batch)
+        self._size_fill(max_batch * 16)
         self.out = torch.empty((self.n_layers, max_batch, n_q, self.d), dtype=torch.float32,
                                device=dev)
-        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=i32, device=dev)
         ws = pkv_decode_workspace_bytes(max_batch, n_q, self.n_kv, self.d, self.max_ctx, 0)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.uploaded = torch.cuda.Event()
+        self.uploaded.record(self.stream)
         self.plan = None
+
+    def _size_cow(self, n):
+        if self.cow_h is None or self.cow_h.shape[1] < n:
+            torch = _torch()
+            self.cow_h = torch.empty((2, n), dtype=torch.int32, pin_memory=True)
+            self.cow = torch.empty((2, n), dtype=torch.int32, device=self.dev)
+
+    def _size_fill(self, n):
+        if self.fill_h is None or self.fill_h.shape[1] < n:
+            torch = _torch()
+            self.fill_h = torch.empty((2, n), dtype=torch.int32, pin_memory=True)
+            self.fill = torch.empty((2, n), dtype=torch.int32, device=self.dev)
 
     def write_prefix(self, k_src, v_src):
         """Keys and values of the shared prefix ([L][prefix_tokens, n_kv, d]
@@ -55,53 +82,64 @@ class ServingLoop:
         table, n = self.b.prefix_table()
         if n == 0:
             return
-        dev = self.k_pools[0].device
-        bt = torch.from_numpy(table.reshape(1, -1)).to(dev)
-        n_tok = k_src[0].shape[0]
-        rows = torch.zeros(n_tok, dtype=torch.int32, device=dev)
-        pos = torch.arange(n_tok, dtype=torch.int32, device=dev)
-        for l in range(self.n_layers):
-            pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src[l], v_src[l], bt, rows, pos,
-                         err_flag=self.err, stream=self.stream)
+        with torch.cuda.stream(self.stream):
+            bt = torch.from_numpy(table.reshape(1, -1)).to(self.dev)
+            n_tok = k_src[0].shape[0]
+            rows = torch.zeros(n_tok, dtype=torch.int32, device=self.dev)
+            pos = torch.arange(n_tok, dtype=torch.int32, device=self.dev)
+            for l in range(self.n_layers):
+                pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src[l], v_src[l], bt, rows, pos,
+                             err_flag=self.err, stream=self.stream)
 
     def schedule(self):
-        """Host half of a step: the batcher's plan, tables uploaded."""
+        """Host half of a step: the batcher's plan, its arrays uploaded
+        (asynchronously, on the loop's stream)."""
         torch = _torch()
         p = self.b.step()
         self.plan = p
-        n = p.num_seqs
-        if n:
-            self.bt[:n].copy_(torch.from_numpy(p.block_tables))
-            self.cl[:n].copy_(torch.from_numpy(p.context_lens))
+        n, n_cow, n_fill = p.num_seqs, len(p.cow_src), len(p.fill_rows)
+        self.uploaded.synchronize()       # the staging buffers are free again
+        self._size_cow(n_cow)
+        self._size_fill(n_fill)
+        with torch.cuda.stream(self.stream):
+            if n:
+                self.bt_h.numpy()[:n] = p.block_tables
+                self.cl_h.numpy()[:n] = p.context_lens
+                self.bt[:n].copy_(self.bt_h[:n], non_blocking=True)
+                self.cl[:n].copy_(self.cl_h[:n], non_blocking=True)
+            if n_cow:
+                self.cow_h.numpy()[0, :n_cow] = p.cow_src
+                self.cow_h.numpy()[1, :n_cow] = p.cow_dst
+                self.cow[:, :n_cow].copy_(self.cow_h[:, :n_cow], non_blocking=True)
+            if n_fill:
+                self.fill_h.numpy()[0, :n_fill] = p.fill_rows
+                self.fill_h.numpy()[1, :n_fill] = p.fill_positions
+                self.fill[:, :n_fill].copy_(self.fill_h[:, :n_fill], non_blocking=True)
+            self.uploaded.record(self.stream)
         return p
 
     def run(self, fill_kv, q, k_new, v_new):
         """Device half of the scheduled step. fill_kv(l) -> (k_src, v_src)
-        bf16 [n_fill, n_kv, d] for the plan's fill tokens of layer l (None
-        if none); q [L][n, n_q, d], k_new / v_new [L][n, n_kv, d] for the
-        plan's rows. Returns the outputs [L][n, n_q, d] (views)."""
+        bf16 [n_fill, n_kv, d] for the plan's fill tokens of layer l (not
+        called when there are none); q [L][n, n_q, d], k_new / v_new
+        [L][n, n_kv, d] for the plan's rows. Returns the outputs
+        [L][n, n_q, d] (a view, valid until the next run)."""
         torch = _torch()
         p = self.plan
-        n = p.num_seqs
-        dev = self.k_pools[0].device
-        src = dst = rows = pos = None
-        if len(p.cow_src):
-            src = torch.from_numpy(p.cow_src).to(dev)
-            dst = torch.from_numpy(p.cow_dst).to(dev)
-        if len(p.fill_rows):
-            rows = torch.from_numpy(p.fill_rows).to(dev)
-            pos = torch.from_numpy(p.fill_positions).to(dev)
-        for l in range(self.n_layers):
-            if src is not None:
-                pkv_copy_blocks(self.k_pools[l], self.v_pools[l], src, dst, err_flag=self.err,
-                                stream=self.stream)
-            if rows is not None:
-                k_src, v_src = fill_kv(l)
-                pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src, v_src, self.bt[:n], rows,
-                             pos, err_flag=self.err, stream=self.stream)
-            if n:
-                pkv_decode_step(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
-                                self.v_pools[l], self.bt[:n], self.cl[:n], self.scale,
-                                self.max_ctx, 0, workspace=self.ws, err_flag=self.err,
-                                stream=self.stream)
+        n, n_cow, n_fill = p.num_seqs, len(p.cow_src), len(p.fill_rows)
+        with torch.cuda.stream(self.stream):
+            for l in range(self.n_layers):
+                if n_cow:
+                    pkv_copy_blocks(self.k_pools[l], self.v_pools[l], self.cow[0, :n_cow],
+                                    self.cow[1, :n_cow], err_flag=self.err, stream=self.stream)
+                if n_fill:
+                    k_src, v_src = fill_kv(l)
+                    pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src, v_src, self.bt[:n],
+                                 self.fill[0, :n_fill], self.fill[1, :n_fill], err_flag=self.err,
+                                 stream=self.stream)
+                if n:
+                    pkv_decode_step(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
+                                    self.v_pools[l], self.bt[:n], self.cl[:n], self.scale,
+                                    self.max_ctx, 0, workspace=self.ws, err_flag=self.err,
+                                    stream=self.stream)
         return self.out[:, :n]
