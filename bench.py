@@ -155,14 +155,20 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
 
 def layer_calls(pkv, S):
     """Per layer, the (name, call) pairs of one decode step, marshalled on
-    torch's current stream: the fused pkv_decode_step (one kernel with the
-    balanced split), or kv_append + partition + merge."""
+    torch's current stream: pkv_decode_step as its two launches (the
+    partition kernel with the append inside, then the merge kernel), or
+    kv_append + partition + merge."""
     sh, calls = S.shape, []
     for l in range(sh.n_layers):
         if S.fused:
-            calls.append([("decode_step", pkv.prepare_decode_step(
-                S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl,
-                sh.scale, S.max_ctx, S.partition, workspace=S.ws, err_flag=S.err))])
+            # pkv_decode_step as its two launches, so that events can time each
+            calls.append([
+                ("decode_step_partition", pkv.prepare_decode_step_partition(
+                    S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt,
+                    S.cl, sh.scale, S.max_ctx, S.partition, workspace=S.ws, err_flag=S.err)),
+                ("paged_attn_merge", pkv.prepare_paged_attn_merge(
+                    S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale, S.max_ctx,
+                    S.partition, workspace=S.ws, err_flag=S.err))])
         else:
             calls.append([
                 ("kv_append", pkv.prepare_kv_append(S.k_pool[l], S.v_pool[l], S.k_new[l], S.v_new[l],
@@ -306,8 +312,9 @@ def run(pkv, torch, S, steps, warmup, graph=True):
             raise RuntimeError(f"device error flag {int(S.err.item())}")
         step_ctx, ms_per_step, mode = graph_ctx, max(t0.elapsed_time(t1), wall * 1e3) / steps, "hip-graph"
 
-    # the roofline kernel: the one launch per layer that does the attention
-    dom = "decode_step" if S.fused else "paged_attn_partition"
+    # the roofline kernel: the partition kernel, which reads the KV cache
+    # (with the append inside when fused); the merge reads only partials
+    dom = "decode_step_partition" if S.fused else "paged_attn_partition"
     dom_bytes = sum(attn_alg_bytes(S, c) + (append_alg_bytes(S, S.B) if S.fused else 0)
                     for c in eager_ctx) / steps
     kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all timed steps
@@ -393,9 +400,10 @@ def stored_traffic(workload, kernel):
         return None, "no record in counter summary"
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
-    if rec.get("entry") != kernel:
-        return None, f"counters were taken on {rec.get('entry')}"
-    return rec["hbm_bytes_per_dispatch"], None
+    per = rec.get("hbm_bytes_per_dispatch", {})
+    if kernel not in per:
+        return None, f"no counters for {kernel}"
+    return per[kernel], None
 
 
 def loop_bench(pkv, torch, shape, name, seed, steps, warmup):

@@ -272,6 +272,22 @@ int pkv_decode_step(float* out, const void* q, const void* k_new,
                     int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* The first half of pkv_decode_step: the append and the partition kernel
+ * (with the balanced split one launch, the append inside it). Same arguments
+ * as pkv_decode_step; pkv_paged_attn_merge with the same arguments then
+ * finishes the step. Together the two calls are pkv_decode_step, bit for
+ * bit; apart, each kernel can be timed or scheduled on its own. */
+int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
+                              const void* v_new, void* k_pool, void* v_pool,
+                              const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t num_blocks,
+                              int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, float scale,
+                              int32_t max_context_len, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t* err_flag, void* stream);
+
 /* Wavefronts of the balanced split on the current device for this shape:
  * one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the
  * kernel's occupancy were lower), at most 8192, and at most one per 16 tiles of

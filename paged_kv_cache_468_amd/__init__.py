@@ -51,6 +51,9 @@ SIGNATURES = {
     "pkv_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_decode_step_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                                 _vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp]),
@@ -288,6 +291,17 @@ def pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_
     _check(lib.pkv_decode_step(*args), "pkv_decode_step")
 
 
+def pkv_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                              scale, max_context_len, partition_tokens=0, workspace=None,
+                              err_flag=None, stream=None):
+    """The append and the partition kernel of pkv_decode_step; returns the
+    workspace used (pass it to pkv_paged_attn_merge to finish the step)."""
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, partition_tokens, workspace, err_flag, stream)
+    _check(lib.pkv_decode_step_partition(*args), "pkv_decode_step_partition")
+    return ws
+
+
 def pkv_paged_attn_partition(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                              max_context_len, partition_tokens=0, workspace=None, err_flag=None,
                              stream=None):
@@ -470,6 +484,18 @@ def prepare_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, cont
     args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
                           max_context_len, partition_tokens, workspace, err_flag, stream)
     return PreparedCall("pkv_decode_step", args,
+                        (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
+                         err_flag))
+
+
+def prepare_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                  context_lens, scale, max_context_len, partition_tokens=0,
+                                  workspace=None, err_flag=None, stream=None):
+    """The first half of prepare_decode_step; prepare_paged_attn_merge with
+    the same arguments (and call.keep[8], the workspace) finishes it."""
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, partition_tokens, workspace, err_flag, stream)
+    return PreparedCall("pkv_decode_step_partition", args,
                         (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
                          err_flag))
 

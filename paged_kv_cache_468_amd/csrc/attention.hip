@@ -914,15 +914,17 @@ extern "C" int pkv_paged_attn_decode(PKV_DECODE_PARAMS) {
   return decode_launch(a, d, (hipStream_t)stream);
 }
 
-extern "C" int pkv_decode_step(float* out, const void* q, const void* k_new, const void* v_new,
-                               void* k_pool, void* v_pool, const int32_t* block_tables,
-                               const int32_t* context_lens, int32_t num_seqs,
-                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_q_heads,
-                               int32_t n_kv_heads, int32_t head_dim, float scale,
-                               int32_t max_context_len, int32_t partition_tokens, void* workspace,
-                               size_t workspace_bytes_given, int32_t* err_flag, void* stream) {
-  DecodeArgs a;
-  int d = 0;
+#define PKV_STEP_PARAMS                                                                      \
+  float *out, const void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool, \
+      const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,              \
+      int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,   \
+      int32_t head_dim, float scale, int32_t max_context_len, int32_t partition_tokens,        \
+      void *workspace, size_t workspace_bytes_given, int32_t *err_flag, void *stream
+
+// The append and the partition kernel of a decode step: with the balanced
+// split one launch (the append inside the partition kernel), with a fixed
+// partition size kv_append then the partition kernel.
+static int step_partition(DecodeArgs& a, int& d, PKV_STEP_PARAMS) {
   const int rc = prepare(a, d, out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                          max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads, head_dim, scale,
                          max_context_len, partition_tokens, workspace, workspace_bytes_given,
@@ -932,10 +934,29 @@ extern "C" int pkv_decode_step(float* out, const void* q, const void* k_new, con
   if (partition_tokens == 0) {
     a.k_new = (const uint16_t*)k_new;
     a.v_new = (const uint16_t*)v_new;
-    return decode_launch(a, d, (hipStream_t)stream);
+    return launch_partition(a, d, (hipStream_t)stream);
   }
   const int arc = pkv_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens,
                                 num_seqs, max_blocks_per_seq, num_blocks, n_kv_heads, head_dim,
                                 err_flag, stream);
-  return arc != PKV_OK ? arc : decode_launch(a, d, (hipStream_t)stream);
+  return arc != PKV_OK ? arc : launch_partition(a, d, (hipStream_t)stream);
+}
+
+#define PKV_STEP_ARGS                                                                         \
+  out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, num_seqs,                 \
+      max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads, head_dim, scale, max_context_len, \
+      partition_tokens, workspace, workspace_bytes_given, err_flag, stream
+
+extern "C" int pkv_decode_step_partition(PKV_STEP_PARAMS) {
+  DecodeArgs a;
+  int d = 0;
+  return step_partition(a, d, PKV_STEP_ARGS);
+}
+
+extern "C" int pkv_decode_step(PKV_STEP_PARAMS) {
+  DecodeArgs a;
+  int d = 0;
+  const int rc = step_partition(a, d, PKV_STEP_ARGS);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  return launch_merge(a, d, (hipStream_t)stream);
 }

@@ -47,14 +47,23 @@ class DevCase:
         self.max_ctx = int(hc.tables.context_lens.max())
 
 
-def gpu_step(pkv, dc: DevCase, partition=0, append=True, scale=None, max_ctx=None, fused=False):
+def gpu_step(pkv, dc: DevCase, partition=0, append=True, scale=None, max_ctx=None, fused=False,
+             halves=False):
     """append (unless append=False) and decode; fused=True runs both as
-    pkv_decode_step."""
+    pkv_decode_step, or with halves=True as its two calls
+    (pkv_decode_step_partition, then pkv_paged_attn_merge)."""
     torch = torch_mod()
     sh = dc.hc.shape
     scale = sh.scale if scale is None else scale
     max_ctx = dc.max_ctx if max_ctx is None else max_ctx
-    if fused:
+    if fused and halves:
+        assert append
+        ws = pkv.pkv_decode_step_partition(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool,
+                                           dc.bt, dc.cl, scale, max_ctx,
+                                           partition_tokens=partition, err_flag=dc.err)
+        pkv.pkv_paged_attn_merge(dc.out, dc.q, dc.k_pool, dc.v_pool, dc.bt, dc.cl, scale, max_ctx,
+                                 partition_tokens=partition, workspace=ws, err_flag=dc.err)
+    elif fused:
         assert append
         pkv.pkv_decode_step(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt, dc.cl,
                             scale, max_ctx, partition_tokens=partition, err_flag=dc.err)

@@ -126,7 +126,11 @@ def test_balanced_workspace_formula():
 def test_decode_step_host_checks():
     import paged_kv_cache_468_amd as pkv
     dummy = ctypes.c_void_p(0x1000)
-    f = pkv.lib.pkv_decode_step
+    for f in (pkv.lib.pkv_decode_step, pkv.lib.pkv_decode_step_partition):
+        _decode_step_host_checks(pkv, f, dummy)
+
+
+def _decode_step_host_checks(pkv, f, dummy):
     # bad head_dim / group / missing k_new are rejected before anything runs
     assert f(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 4, 16, 64, 8, 2, 96, 0.1,
              256, 0, dummy, 1 << 30, None, None) == pkv.PKV_EUNSUPPORTED

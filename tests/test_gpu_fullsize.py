@@ -3,8 +3,9 @@
 One layer of each shape is built at its real size (batch, heads, head
 size, context distribution, shared prefix), pools drawn on the GPU with a
 seeded generator and copied back for the oracle. The library runs the
-benchmark's call in its launch configuration: pkv_decode_step (the append
-inside the attention's partition kernel, then the merge), the balanced
+benchmark's calls in their launch configuration: pkv_decode_step as its two
+halves (pkv_decode_step_partition, the append inside the attention's
+partition kernel, then pkv_paged_attn_merge), the balanced
 split over the device's waves, max_context_len = largest context + the
 benchmark's 44 extra decode steps; one shape also runs the unfused
 kv_append + decode. Checked:
@@ -72,9 +73,11 @@ def test_full_size_layer(pkv, orc, cfg, fused):
     torch.cuda.synchronize()
     k_ref, v_ref = to_host_u16(k_pool), to_host_u16(v_pool)
 
-    if fused:   # the benchmark's call: append inside the attention kernel
-        pkv.pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, bt, cl, shape.scale, max_ctx,
-                            err_flag=err)
+    if fused:   # the benchmark's calls: append inside the partition kernel, then the merge
+        ws = pkv.pkv_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, bt, cl,
+                                           shape.scale, max_ctx, err_flag=err)
+        pkv.pkv_paged_attn_merge(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx,
+                                 workspace=ws, err_flag=err)
     else:
         pkv.pkv_kv_append(k_pool, v_pool, k_new, v_new, bt, cl, err_flag=err)
         pkv.pkv_paged_attn_decode(out, q, k_pool, v_pool, bt, cl, shape.scale, max_ctx,

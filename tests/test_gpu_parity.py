@@ -238,18 +238,21 @@ def test_balanced_split_uneven_mix(pkv, orc):
 @pytest.mark.parametrize("part", [0, 128])
 @pytest.mark.parametrize("shape", [(32, 8, 128), (40, 2, 128), (20, 4, 64), (8, 1, 128)])
 def test_decode_step_equals_append_then_decode(pkv, shape, part):
-    """pkv_decode_step (one kernel with the balanced split) against
+    """pkv_decode_step (one kernel with the balanced split), and its two
+    halves (pkv_decode_step_partition, pkv_paged_attn_merge), against
     pkv_kv_append + pkv_paged_attn_decode: pools and outputs bit for bit."""
     ctx = [1, 15, 16, 17, 300, 1000, 2049]
     hc = w.host_case(_shape(*shape), 90 + shape[0], context_lens=ctx, spare_blocks=3)
-    a = DevCase(hc)
-    b = DevCase(hc)
+    a, b, c = DevCase(hc), DevCase(hc), DevCase(hc)
     oa = gpu_step(pkv, a, partition=part)
     ob = gpu_step(pkv, b, partition=part, fused=True)
-    assert int(a.err.item()) == 0 and int(b.err.item()) == 0
-    assert np.array_equal(to_host_u16(a.k_pool), to_host_u16(b.k_pool))
-    assert np.array_equal(to_host_u16(a.v_pool), to_host_u16(b.v_pool))
-    assert np.array_equal(oa, ob)
+    oc = gpu_step(pkv, c, partition=part, fused=True, halves=True)
+    for x in (a, b, c):
+        assert int(x.err.item()) == 0
+    for x in (b, c):
+        assert np.array_equal(to_host_u16(a.k_pool), to_host_u16(x.k_pool))
+        assert np.array_equal(to_host_u16(a.v_pool), to_host_u16(x.v_pool))
+    assert np.array_equal(oa, ob) and np.array_equal(oa, oc)
 
 
 def test_workspace_needs_no_initialisation(pkv):
