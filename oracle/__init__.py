@@ -7,9 +7,12 @@ runs anything here, and nothing here imports the product path.
 
 Contents
   * ``liboracle.so`` (built from ``oracle.c`` by ``oracle/build.py``): append,
-    multi-token write, copy-on-write, decode in double precision, the KV-size closed form.
+    multi-token write, copy-on-write, decode and the multi-token verification
+    attention in double precision, the KV-size closed form.
+  * ``speculative``: the acceptance rule of speculative decoding (accept,
+    leftover distribution, replacement draw) in plain Python.
   * ``allocator_model``: a pure-Python reference model of the refcounted
-    block allocator.
+    block allocator; ``batcher_model``: the continuous-batching scheduler.
 
 Inputs are numpy arrays; bf16 tensors travel as their uint16 bit patterns.
 Pinning: every function is checked in tests/test_oracle_pins.py against
@@ -54,6 +57,9 @@ def _bind(path):
     lib.oracle_decode.argtypes = [f64p, u16p, u16p, u16p, i32p, i32p, c_int,
                                   c_int, c_int, c_int, c_int, c_int,
                                   ctypes.c_double]
+    lib.oracle_verify.restype = c_int
+    lib.oracle_verify.argtypes = [f64p, u16p, u16p, u16p, i32p, i32p, c_int, c_int,
+                                  c_int, c_int, c_int, c_int, c_int, ctypes.c_double]
     return lib
 
 
@@ -164,6 +170,30 @@ class Oracle:
             raise ValueError("oracle_decode: n_q must be a multiple of n_kv")
         return out, rc
 
+    def verify(self, q, k_pool, v_pool, block_tables, context_lens, n_kv, scale):
+        """Verification attention of q_len query tokens per sequence, query
+        token i at position ctx - q_len + i seeing tokens [0, ctx - q_len + i].
+        q: uint16 [num_seqs, q_len, n_q, d]. Returns (out float64
+        [num_seqs, q_len, n_q, d], status)."""
+        q = _u16(q, "q")
+        k_pool = _u16(k_pool, "k_pool")
+        v_pool = _u16(v_pool, "v_pool")
+        bt = _i32(block_tables, "block_tables")
+        cl = _i32(context_lens, "context_lens")
+        num_seqs, q_len, n_q, d = q.shape
+        num_blocks = k_pool.size // (n_kv * 16 * d)
+        out = np.empty((num_seqs, q_len, n_q, d), dtype=np.float64)
+        rc = self.lib.oracle_verify(
+            _ptr(out, ctypes.c_double), _ptr(q, ctypes.c_uint16),
+            _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+            _ptr(bt, ctypes.c_int32), _ptr(cl, ctypes.c_int32),
+            num_seqs, q_len, bt.shape[1], num_blocks, n_q, n_kv, d, float(scale))
+        if rc == -2:
+            raise MemoryError("oracle_verify: out of host memory")
+        if rc == -3:
+            raise ValueError("oracle_verify: bad heads or q_len")
+        return out, rc
+
     def decode_row(self, q_row, k_pool, v_pool, table_row, ctx, n_kv, h, scale):
         """One output row (one sequence, one query head, KV head h)."""
         q_row = _u16(q_row, "q_row")
@@ -215,6 +245,10 @@ def kv_write(*a, **k):
 
 def decode(*a, **k):
     return default().decode(*a, **k)
+
+
+def verify(*a, **k):
+    return default().verify(*a, **k)
 
 
 def decode_row(*a, **k):

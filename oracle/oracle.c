@@ -241,3 +241,47 @@ int oracle_decode(double* out, const uint16_t* q, const uint16_t* k_pool,
   }
   return status;
 }
+
+/* ------------------------------------------------------------------------
+ * Verification pass of speculative decoding ([M23] 23.5: the large model
+ * checks all drafted tokens in one pass; [SLS] "Speculative decoding";
+ * [DSS] "Speculative decoding"). Each sequence brings q_len query tokens:
+ * the last q_len of its ctx cached tokens (their keys and values are
+ * already in the pool). Query token i sits at position ctx - q_len + i and,
+ * as in any decode step, attends to every cached token up to and including
+ * its own position, i.e. to the first ctx - q_len + i + 1 tokens: each row
+ * is oracle_decode_row over the sequence cut at that length.
+ * q and out: [num_seqs][q_len][n_q][d]. A sequence with ctx < q_len (or ctx
+ * past its table) is invalid: its rows are NaN. Returns 0, -1 if any
+ * sequence was invalid, -2 on allocation failure, -3 on bad heads. */
+int oracle_verify(double* out, const uint16_t* q, const uint16_t* k_pool,
+                  const uint16_t* v_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, int num_seqs, int q_len,
+                  int max_blocks_per_seq, int num_blocks, int n_q, int n_kv,
+                  int d, double scale) {
+  if (n_kv <= 0 || n_q % n_kv != 0 || q_len < 1) return -3;
+  int group = n_q / n_kv;
+  int status = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    int ctx = context_lens[s];
+    int bad_ctx = ctx < q_len || ctx > ORACLE_BLOCK * max_blocks_per_seq;
+    for (int i = 0; i < q_len; ++i) {
+      int seen = ctx - q_len + i + 1; /* tokens up to query i's own position */
+      for (int j = 0; j < n_q; ++j) {
+        size_t row_index = ((size_t)s * q_len + i) * n_q + j;
+        double* row = out + row_index * d;
+        if (bad_ctx) {
+          for (int e = 0; e < d; ++e) row[e] = NAN;
+          status = -1;
+          continue;
+        }
+        int rc = oracle_decode_row(row, q + row_index * d, k_pool, v_pool,
+                                   block_tables + (size_t)s * max_blocks_per_seq,
+                                   seen, num_blocks, n_kv, j / group, d, scale);
+        if (rc == -2) return -2;
+        if (rc != 0) status = -1;
+      }
+    }
+  }
+  return status;
+}

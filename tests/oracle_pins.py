@@ -319,9 +319,100 @@ def check_invalid_inputs(orc):
     assert rc == -1 and np.isnan(out[0]).all() and np.isfinite(out[1]).all()
 
 
+# ---------------------------------------------------------------------------
+# verification attention (q_len query tokens per sequence, causal among them)
+
+def _verify_case(seed, n_q, n_kv, d, ctx, q_len):
+    case = w.host_case(_small_shape(n_q, n_kv, d), seed, context_lens=ctx)
+    g = w.rng(seed, 11)
+    qv = w.normal_bf16(g, (len(ctx), q_len, n_q, d))
+    return case, qv
+
+
+def _verify(orc, case, qv, scale=None):
+    sh = case.shape
+    sc = sh.scale if scale is None else scale
+    return orc.verify(qv, case.k_pool, case.v_pool, case.tables.block_tables,
+                      case.tables.context_lens, sh.n_kv, sc)
+
+
+def check_verify_one_token_is_decode(orc):
+    """q_len = 1 is the decode step itself."""
+    case, qv = _verify_case(21, 8, 2, 64, [1, 16, 17, 90], 1)
+    case.q[:] = qv[:, 0]
+    got, rc = _verify(orc, case, qv)
+    want, rc2 = _decode(orc, case)
+    assert rc == 0 and rc2 == 0
+    assert np.array_equal(got[:, 0], want)
+
+
+VERIFY_SDPA_CASES = [  # (n_q, n_kv, d, context lengths, q_len)
+    (8, 2, 64, [5, 16, 17, 40], 5),
+    (20, 4, 64, [33, 64, 100], 3),
+    (32, 8, 128, [16, 31, 200], 8),
+    (4, 4, 128, [2, 9], 2),
+]
+
+
+def check_verify_sdpa(orc):
+    """Against torch's scaled_dot_product_attention in float64 on the
+    contiguous cache, with the causal mask aligned to the sequence's end:
+    query i may see token t iff t <= ctx - q_len + i."""
+    import torch
+    import torch.nn.functional as F
+    for k, (n_q, n_kv, d, ctx, q_len) in enumerate(VERIFY_SDPA_CASES):
+        case, qv = _verify_case(30 + k, n_q, n_kv, d, ctx, q_len)
+        got, rc = _verify(orc, case, qv)
+        assert rc == 0
+        for s, c in enumerate(ctx):
+            kc, vc = w.gather_contiguous(case.k_pool, case.v_pool, case.tables, s)
+            qt = torch.from_numpy(w.bf16_to_f32(qv[s]).astype(np.float64)).permute(1, 0, 2)[None]
+            kt = torch.from_numpy(w.bf16_to_f32(kc).astype(np.float64))[None]
+            vt = torch.from_numpy(w.bf16_to_f32(vc).astype(np.float64))[None]
+            mask = torch.arange(c)[None, :] <= (c - q_len + torch.arange(q_len))[:, None]
+            o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=1.0 / math.sqrt(d),
+                                               enable_gqa=n_q != n_kv)
+            ref = o[0].permute(1, 0, 2).numpy()                      # [q_len, n_q, d]
+            assert np.allclose(got[s], ref, rtol=0, atol=1e-12), (k, s)
+
+
+def check_verify_causal(orc):
+    """Keys and values after a query's own position never change its row;
+    they do change the rows of the later queries that see them."""
+    ctx, q_len = [40, 21], 6
+    case, qv = _verify_case(41, 8, 2, 64, ctx, q_len)
+    base, rc = _verify(orc, case, qv)
+    assert rc == 0
+    for s, c in enumerate(ctx):
+        cut = c - q_len + 2            # query 2 sees tokens [0, cut]
+        kc, vc = w.gather_contiguous(case.k_pool, case.v_pool, case.tables, s)
+        kc2, vc2 = kc.copy(), vc.copy()
+        kc2[:, cut + 1:] = w.bf16_bits(-w.bf16_to_f32(kc[:, cut + 1:]) * 3)
+        vc2[:, cut + 1:] = w.bf16_bits(w.bf16_to_f32(vc[:, cut + 1:]) + 5)
+        k_pool, v_pool = case.k_pool.copy(), case.v_pool.copy()
+        w.scatter_contiguous(kc2, vc2, case.tables, s, k_pool, v_pool)
+        got, rc = orc.verify(qv, k_pool, v_pool, case.tables.block_tables,
+                             case.tables.context_lens, case.shape.n_kv, case.shape.scale)
+        assert rc == 0
+        assert np.array_equal(got[s, :3], base[s, :3]), s
+        assert not np.allclose(got[s, 3:], base[s, 3:]), s
+        other = 1 - s
+        assert np.array_equal(got[other], base[other])
+
+
+def check_verify_invalid(orc):
+    """Fewer cached tokens than query tokens is invalid: NaN rows, status -1,
+    the other sequences untouched."""
+    case, qv = _verify_case(43, 4, 1, 64, [3, 30], 4)
+    got, rc = _verify(orc, case, qv)
+    assert rc == -1
+    assert np.isnan(got[0]).all() and np.isfinite(got[1]).all()
+
+
 ALL_CHECKS = [check_kv_sizes, check_kv_linearity, check_append_golden, check_write_golden,
               check_write_equals_append, check_decode_golden,
               check_append_touches_only_its_slots, check_copy_blocks, check_single_token,
               check_constant_values, check_equal_keys, check_sdpa, check_large_logits,
               check_block_permutation, check_shared_prefix, check_group_equals_repeat,
-              check_invalid_inputs]
+              check_invalid_inputs, check_verify_one_token_is_decode, check_verify_sdpa,
+              check_verify_causal, check_verify_invalid]

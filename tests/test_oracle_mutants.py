@@ -35,6 +35,12 @@ MUTANTS = {
                             "    int slot = row % ORACLE_BLOCK;\n    for (int h = 0; h < n_kv; ++h) {\n      for (int i = 0; i < d; ++i) {\n        size_t src = ((size_t)tok"),
     "write_source_row": ("        size_t src = ((size_t)tok * n_kv + h) * d + i;", "        size_t src = ((size_t)row * n_kv + h) * d + i;"),
     "copy_k_only": ("      v_pool[(size_t)dst[p] * per_block + e] = v_pool[(size_t)src[p] * per_block + e];\n", ""),
+    "verify_no_causal": ("int seen = ctx - q_len + i + 1;", "int seen = ctx;"),
+    "verify_seen_off_by_one": ("int seen = ctx - q_len + i + 1;", "int seen = ctx - q_len + i + 2;"),
+    "verify_reversed_tokens": ("int seen = ctx - q_len + i + 1;", "int seen = ctx - i;"),
+    "verify_query_of_decode_layout": ("int rc = oracle_decode_row(row, q + row_index * d,",
+                                      "int rc = oracle_decode_row(row, q + ((size_t)s * n_q + j) * d,"),
+    "verify_short_context_accepted": ("int bad_ctx = ctx < q_len ||", "int bad_ctx ="),
     "kv_bytes_no_two": ("return (uint64_t)2 * (uint64_t)n_layers", "return (uint64_t)n_layers"),
     "kv_bytes_no_precision": (" *\n         (uint64_t)bytes_per_value;", ";"),
 }
