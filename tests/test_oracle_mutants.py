@@ -16,7 +16,8 @@ from oracle.build import SRC, build
 from oracle_pins import ALL_CHECKS
 
 MUTANTS = {
-    "kv_head_modulo": ("j / group", "j % n_kv"),
+    "kv_head_modulo": ("ctx, num_blocks, n_kv, j / group,", "ctx, num_blocks, n_kv, j % n_kv,"),
+    "verify_kv_head_modulo": ("seen, num_blocks, n_kv, j / group,", "seen, num_blocks, n_kv, j % n_kv,"),
     "dropped_scale": ("z[t] = scale * dot;", "z[t] = dot;"),
     "exp_sign": ("z[t] = exp(z[t] - zmax);", "z[t] = exp(zmax - z[t]);"),
     "max_not_subtracted": ("z[t] = exp(z[t] - zmax);", "z[t] = exp(z[t]);"),
