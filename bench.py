@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 import workload as w  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+VOCAB = 128256          # LLaMA-3 vocabulary: the acceptance rule's draw runs over it
 BLOCK = 16
 # counter summaries: profiles/pmc_<kernel>_<workload>.txt, ending in a JSON record
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_paged_attn_balanced_{workload}.txt")
@@ -406,6 +407,110 @@ def stored_traffic(workload, kernel):
     return per[kernel], None
 
 
+def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
+    """The verification pass of speculative decoding on the decode bench's
+    state: per layer, pkv_kv_write of the q_len new tokens of every sequence
+    (at positions ctx - q_len .. ctx - 1) and pkv_paged_attn_verify; then
+    once, pkv_spec_accept over a 128,256-token vocabulary. The contexts
+    stay fixed between steps (the tokens are rewritten in place); the KV
+    bytes per step are those of the decode at the same contexts."""
+    sh, L, B = S.shape, S.shape.n_layers, S.B
+    dev = torch.device("cuda")
+    base = 7000
+    q = w.device_normal_bf16_(torch.empty((L, B, q_len, sh.n_q, sh.d), dtype=torch.bfloat16,
+                                          device=dev), base + 1)
+    k_src = w.device_normal_bf16_(torch.empty((L, B * q_len, sh.n_kv, sh.d), dtype=torch.bfloat16,
+                                              device=dev), base + 2)
+    v_src = w.device_normal_bf16_(torch.empty_like(k_src), base + 3)
+    out = torch.empty((L, B, q_len, sh.n_q, sh.d), dtype=torch.float32, device=dev)
+    rows = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(q_len)
+    ctx = torch.from_numpy(S.ctx.copy()).to(dev)
+    pos = (ctx.repeat_interleave(q_len) - q_len +
+           torch.arange(q_len, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
+    S.cl.copy_(ctx)
+    ws = torch.empty(max(pkv.pkv_verify_workspace_bytes(B, q_len, sh.n_q, sh.n_kv, sh.d,
+                                                        S.max_ctx), 1),
+                     dtype=torch.uint8, device=dev)
+
+    # the acceptance rule once per step over a LLaMA-3 sized vocabulary:
+    # target probabilities for the q_len positions, draft probabilities for
+    # the q_len - 1 drafts (softmax of seeded N(0,1) logits), seeded drafts
+    # and uniforms
+    gamma = q_len - 1
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(base + 4)
+    p_t = torch.softmax(torch.randn((B, q_len, VOCAB), device=dev, generator=gen), dim=-1)
+    q_d = torch.softmax(torch.randn((B, max(gamma, 1), VOCAB), device=dev, generator=gen),
+                        dim=-1)[:, :gamma].contiguous()
+    drafts = torch.randint(0, VOCAB, (B, gamma), device=dev, generator=gen, dtype=torch.int32)
+    unif = torch.rand((B, q_len), device=dev, generator=gen)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def accept():
+        pkv.pkv_spec_accept(p_t, q_d, drafts, unif, n_acc, nxt, err_flag=S.err)
+
+    def write(l):
+        pkv.pkv_kv_write(S.k_pool[l], S.v_pool[l], k_src[l], v_src[l], S.bt, rows, pos,
+                         err_flag=S.err)
+
+    def verify(l):
+        pkv.pkv_paged_attn_verify(out[l], q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale,
+                                  S.max_ctx, workspace=ws, err_flag=S.err)
+
+    for _ in range(warmup):
+        for l in range(L):
+            write(l)
+            verify(l)
+        accept()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L * steps)]
+    eva = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for l in range(L):
+            e = ev[i * L + l]
+            e[0].record()
+            write(l)
+            e[1].record()
+            verify(l)
+            e[2].record()
+        eva[i][0].record()
+        accept()
+        eva[i][1].record()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    if int(S.err.item()):
+        raise RuntimeError(f"device error flag {int(S.err.item())}")
+    write_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    verify_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    accept_us = float(np.mean([e[0].elapsed_time(e[1]) for e in eva])) * 1e3
+    ms, mode = eager_ms, "eager"
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(L):
+                write(l)
+                verify(l)
+            accept()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms, mode = (time.perf_counter() - t0) * 1e3 / steps, "hip-graph"
+        if int(S.err.item()):
+            raise RuntimeError(f"device error flag {int(S.err.item())}")
+    kv_layer = kv_bytes(S, S.ctx)
+    alg = attn_alg_bytes(S, S.ctx) + B * (q_len - 1) * sh.n_q * sh.d * (2 + 4)
+    return {"ms_per_step": ms, "step_mode": mode, "eager_ms_per_step": eager_ms,
+            "kv_gbs": kv_layer * L / (ms * 1e-3) / 1e9, "write_us": write_us,
+            "verify_us": verify_us, "accept_us": accept_us, "verify_alg_bytes": alg,
+            "verify_gbs": alg / (verify_us * 1e-6) / 1e9,
+            "query_tokens_per_s": B * q_len / (ms * 1e-3)}
+
+
 def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
     """Continuous batching at a model shape: requests with prompts uniform in
     [prefix, ctx_hi - 256] tokens (all beginning with the shared prefix when
@@ -520,6 +625,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per layer (kv_append, partition, merge) instead of pkv_decode_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    ap.add_argument("--verify-tokens", type=int, default=0,
+                    help="speculative verification instead: this many query tokens per sequence")
     ap.add_argument("--loop", action="store_true",
                     help="continuous batching instead: the batcher's plans carried out step by step")
     ap.add_argument("--loop-steps", type=int, default=300)
@@ -546,6 +653,38 @@ def main():
         print(json.dumps(line), flush=True)
         return
     extra = args.warmup + 2 * args.steps + 1   # one token per step: eager, graph warm-up, graph
+    if args.verify_tokens > 0:
+        log(f"[bench] verification pass, {args.verify_tokens} query tokens, {WORKLOAD_NAMES[args.config]}")
+        share_v = shape.prefix_tokens > 0 and not args.no_share
+        S = build_state(pkv, torch, shape, args.seed, share_v, extra, 0)
+        dec = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
+        log(f"[bench] decode on the same state: {dec['ms_per_step']:.3f} ms/step")
+        vr = verify_bench(pkv, torch, S, args.verify_tokens, args.steps, args.warmup,
+                          graph=not args.no_graph)
+        log(f"[bench] verify: {vr['ms_per_step']:.3f} ms/step, write {vr['write_us']:.1f} us, "
+            f"verify {vr['verify_us']:.1f} us per layer")
+        line = {
+            "metric": "speculative verification pass: KV GB/s and time vs one decode step",
+            "value": vr["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": vr["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "verify-" + WORKLOAD_NAMES[args.config],
+                       "query_tokens": args.verify_tokens, "layers": shape.n_layers,
+                       "batch": S_batch(shape), "n_q_heads": shape.n_q, "n_kv_heads": shape.n_kv,
+                       "head_dim": shape.d, "shared_prefix_tokens": shape.prefix_tokens if share_v else 0},
+            "step_mode": vr["step_mode"], "decode_ms_per_step": dec["ms_per_step"],
+            "verify_over_decode": vr["ms_per_step"] / dec["ms_per_step"],
+            "query_tokens_per_s": vr["query_tokens_per_s"],
+            "kernels_us": {"kv_write": vr["write_us"], "paged_attn_verify": vr["verify_us"],
+                           "spec_accept": vr["accept_us"]},
+            "vocab": VOCAB,
+            "roofline": {"kernel": "paged_attn_verify", "bound": "hbm", "achieved": vr["verify_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": vr["verify_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "alg_bytes_per_launch": vr["verify_alg_bytes"]},
+        }
+        print(json.dumps(line), flush=True)
+        return
 
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")

@@ -101,6 +101,7 @@ enum {
 #define PKV_DEVERR_BLOCK_ID 1   /* a needed block-table entry outside [0, num_blocks) */
 #define PKV_DEVERR_CONTEXT 2    /* a context length outside [1, max_context_len] */
 #define PKV_DEVERR_COPY_PAIR 4  /* a copy_blocks id outside [0, num_blocks) */
+#define PKV_DEVERR_TOKEN 8      /* pkv_spec_accept: a drafted token outside [0, vocab) */
 
 /* Static string for a status code; never NULL. */
 const char* pkv_strerror(int status);
@@ -287,6 +288,72 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
                               int32_t max_context_len, int32_t partition_tokens,
                               void* workspace, size_t workspace_bytes,
                               int32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Verification pass of speculative decoding ([M23] 23.5: the target model
+ * checks all drafted tokens in one pass, at about the cost of one decode
+ * step since the pass is bound by memory reads; [SLS] "Speculative
+ * decoding"; [DSS] "Speculative decoding").
+ *
+ * Each sequence brings q_len query tokens (the last accepted token and the
+ * drafts): the last q_len of its context_lens[s] cached tokens, whose keys
+ * and values the caller has already written into the pools (pkv_kv_write).
+ * Query token i sits at position ctx - q_len + i and attends to positions
+ * 0 .. ctx - q_len + i (causal among the new tokens). Every K/V byte is read
+ * once for all q_len * (n_q/n_kv) rows of a KV head (up to 32 rows per read;
+ * more rows read the cache once per 32).
+ *   q:   device bf16 [num_seqs][q_len][n_q_heads][head_dim]
+ *   out: device fp32 [num_seqs][q_len][n_q_heads][head_dim]
+ * q_len in [1, 64]; q_len == 1 is pkv_paged_attn_decode (same kernels, same
+ * bits). Other arguments as for pkv_paged_attn_decode with the balanced
+ * split; workspace of at least pkv_verify_workspace_bytes, no initialisation
+ * needed. Device errors: a context length outside [q_len, max_context_len]
+ * sets PKV_DEVERR_CONTEXT, a bad block id PKV_DEVERR_BLOCK_ID; that
+ * sequence's rows are NaN. After the pass the caller keeps the accepted
+ * tokens by setting the context length; slots past it are overwritten by
+ * later appends. */
+size_t pkv_verify_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                  int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len);
+int pkv_paged_attn_verify(float* out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t q_len, int32_t max_blocks_per_seq,
+                          int32_t num_blocks, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, float scale,
+                          int32_t max_context_len, void* workspace,
+                          size_t workspace_bytes, int32_t* err_flag,
+                          void* stream);
+
+/* The acceptance rule of speculative decoding ([M23] 23.5 and Exercises;
+ * [SLS] "Speculative decoding"): for each sequence the gamma drafted tokens
+ * are checked in order, draft i kept with probability
+ * min(1, p_i(x_i) / q_i(x_i)), taken as the float32 decision
+ * u_i * q_i(x_i) < p_i(x_i). At the first rejection (draft n) the rest are
+ * discarded and one token is drawn from the leftover max(0, p_n - q_n)
+ * (from p_n itself if the leftover has no weight, which exact arithmetic
+ * rules out); with every draft kept, one token is drawn from p_gamma. A draw
+ * with weights w returns the smallest x whose running sum exceeds
+ * u_gamma * sum(w), sums in float64 (so a uniform within rounding of a
+ * boundary may land on either neighbour).
+ *   p_target:     device fp32 [num_seqs][gamma + 1][vocab] target probabilities
+ *   q_draft:      device fp32 [num_seqs][gamma][vocab] draft probabilities
+ *   draft_tokens: device int32 [num_seqs][gamma]
+ *   uniforms:     device fp32 [num_seqs][gamma + 1] in [0, 1): u_0 .. u_{gamma-1}
+ *                 for the keep tests, u_gamma for the draw (random numbers are
+ *                 the caller's)
+ *   n_accepted:   device int32 [num_seqs] out: drafts kept (0 .. gamma)
+ *   next_token:   device int32 [num_seqs] out: the drawn token
+ * A pass yields n_accepted + 1 tokens. gamma in [0, 64] (0: a plain draw
+ * from p_0; q_draft and draft_tokens may then be null); vocab in
+ * [1, 2097152]. A row with no positive weight draws token 0. Device errors: a
+ * draft outside [0, vocab) sets PKV_DEVERR_TOKEN and that sequence's
+ * outputs are -1. */
+int pkv_spec_accept(const float* p_target, const float* q_draft,
+                    const int32_t* draft_tokens, const float* uniforms,
+                    int32_t num_seqs, int32_t gamma, int32_t vocab,
+                    int32_t* n_accepted, int32_t* next_token, int32_t* err_flag,
+                    void* stream);
 
 /* Wavefronts of the balanced split on the current device for this shape:
  * one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4, -5
-PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT, PKV_DEVERR_COPY_PAIR = 1, 2, 4
+PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT, PKV_DEVERR_COPY_PAIR, PKV_DEVERR_TOKEN = 1, 2, 4, 8
 BLOCK_TOKENS = 16
 
 # every symbol include/pkv.h declares, with its ctypes signature
@@ -54,6 +54,10 @@ SIGNATURES = {
     "pkv_decode_step_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                                  _vp, _sz, _vp, _vp]),
+    "pkv_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_spec_accept": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp]),
@@ -319,6 +323,71 @@ def pkv_paged_attn_merge(out, q, k_pool, v_pool, block_tables, context_lens, sca
     args, _ = _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                            max_context_len, partition_tokens, workspace, err_flag, stream)
     _check(lib.pkv_paged_attn_merge(*args), "pkv_paged_attn_merge")
+
+
+def pkv_verify_workspace_bytes(num_seqs, q_len, n_q_heads, n_kv_heads, head_dim, max_context_len):
+    return int(lib.pkv_verify_workspace_bytes(num_seqs, q_len, n_q_heads, n_kv_heads, head_dim,
+                                              max_context_len))
+
+
+def pkv_paged_attn_verify(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, workspace=None, err_flag=None, stream=None):
+    """Verification pass: q bf16 [num_seqs, q_len, n_q, d] (the last q_len
+    cached tokens of each sequence, already written), out fp32 of the same
+    shape; query token i sees positions [0, ctx - q_len + i]. workspace: a
+    torch uint8 CUDA tensor of at least pkv_verify_workspace_bytes(...)
+    bytes, or None to have one allocated here. Returns the workspace."""
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(out, "out", torch.float32, 4)
+    B, q_len, n_q, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out: expected [num_seqs, q_len, n_q, head_dim], the same shape")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens: one row per sequence")
+    need = pkv_verify_workspace_bytes(B, q_len, n_q, n_kv, d, max_context_len) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_paged_attn_verify(_dev(out, "out", torch.float32), _dev(q, "q", torch.bfloat16),
+                                     _dev(k_pool, "k_pool", torch.bfloat16),
+                                     _dev(v_pool, "v_pool", torch.bfloat16), bt, cl, B, q_len,
+                                     block_tables.shape[1], nb, n_q, n_kv, d, float(scale),
+                                     int(max_context_len), ws, workspace.numel(), _flag(err_flag),
+                                     _stream(stream)), "pkv_paged_attn_verify")
+    return workspace
+
+
+def pkv_spec_accept(p_target, q_draft, draft_tokens, uniforms, n_accepted, next_token,
+                    err_flag=None, stream=None):
+    """The acceptance rule: p_target fp32 [B, gamma+1, V], q_draft fp32
+    [B, gamma, V], draft_tokens int32 [B, gamma], uniforms fp32 [B, gamma+1];
+    writes n_accepted and next_token (int32 [B])."""
+    torch = _torch()
+    _dev(p_target, "p_target", torch.float32, 3)
+    B, g1, V = p_target.shape
+    gamma = g1 - 1
+    if tuple(uniforms.shape) != (B, g1):
+        raise ValueError("uniforms: expected [num_seqs, gamma + 1]")
+    if gamma > 0:
+        _dev(q_draft, "q_draft", torch.float32, 3)
+        _dev(draft_tokens, "draft_tokens", torch.int32, 2)
+        if tuple(q_draft.shape) != (B, gamma, V) or tuple(draft_tokens.shape) != (B, gamma):
+            raise ValueError("q_draft / draft_tokens: expected [B, gamma, V] / [B, gamma]")
+    for name, t in (("n_accepted", n_accepted), ("next_token", next_token)):
+        _dev(t, name, torch.int32, 1)
+        if t.shape[0] != B:
+            raise ValueError(f"{name}: one entry per sequence")
+    _check(lib.pkv_spec_accept(_dev(p_target, "p_target", torch.float32),
+                               _dev(q_draft, "q_draft", torch.float32) if gamma > 0 else None,
+                               _dev(draft_tokens, "draft_tokens", torch.int32) if gamma > 0 else None,
+                               _dev(uniforms, "uniforms", torch.float32), B, gamma, V,
+                               _dev(n_accepted, "n_accepted", torch.int32),
+                               _dev(next_token, "next_token", torch.int32), _flag(err_flag),
+                               _stream(stream)), "pkv_spec_accept")
 
 
 def pkv_kv_write(k_pool, v_pool, k_src, v_src, block_tables, seq_rows, positions, err_flag=None,

@@ -1,4 +1,6 @@
-// Decode-phase attention over a paged KV cache, for gfx950 (MI355X).
+// Decode-phase attention over a paged KV cache, for gfx950 (MI355X), and
+// the verification pass of speculative decoding ("Module 23: Serving",
+// 23.5: the target model checks several drafted tokens in one pass).
 //
 // What is computed (include/pkv.h has the layouts): for every sequence s and
 // query head j, the softmax-weighted sum of the values of every cached token
@@ -13,13 +15,18 @@
 // (logical to physical block indirection).
 //
 // Work decomposition
-//   A unit is one (KV head h, query group qg, sequence s): the <= 16 query
-//   rows of head h's group (rows qg*16 .. qg*16+15) over the ceil(ctx/16)
-//   tiles of s. A segment is a run of consecutive tiles of one unit, and one
-//   wavefront processes a segment: for each 16-token block it loads the K
-//   tile (16 x D bf16, token-major) and the V tile (D x 16 bf16, dim-major),
-//   both contiguous, and serves all query rows of the group from them, so
-//   every KV byte is read from HBM once.
+//   The query rows of KV head h are the q_len * G pairs (query token i,
+//   head jj of h's group), row i*G + jj (decode: q_len = 1, the G heads).
+//   A unit is one (KV head h, row group qg, sequence s): rows
+//   qg*16*NG .. qg*16*NG + 16*NG - 1 (NG = 1 for the decode; the
+//   verification pass of speculative decoding takes NG = 2 when a head has
+//   more than 16 rows) over the ceil(ctx/16) tiles of s. A segment is a run
+//   of consecutive tiles of one unit, and one wavefront processes a segment:
+//   for each 16-token block it loads the K tile (16 x D bf16, token-major)
+//   and the V tile (D x 16 bf16, dim-major), both contiguous, and serves all
+//   rows of the unit from them, so every KV byte is read from HBM once per
+//   unit. In the verification pass row i sees positions up to
+//   ctx - q_len + i only (causal among the new tokens).
 //
 //   Balanced split (partition_tokens == 0): all tiles of the launch, in
 //   (KV head, query group, sequence, tile) order, are cut into n_waves equal
@@ -76,6 +83,7 @@ constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kXcds = 8;             // XCDs of an MI355X
 constexpr int kMaxSplitWaves = 8192; // cap of the balanced split's wave count
 constexpr int kMinTilesPerWave = 16; // balanced split: at least this much work per wave
+constexpr int kMaxQueryTokens = 64;  // verification pass: query tokens per sequence
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
@@ -93,7 +101,12 @@ struct DecodeArgs {
   int32_t* unit_info; // balanced split: per unit, first partial slot and partial count
   int32_t* err_flag;
   int num_seqs, max_blocks, num_blocks;
-  int n_q, n_kv, group, n_qgroups, rows;  // rows = min(group, 16) per slot
+  int n_q, n_kv, group;
+  int q_len;         // query tokens per sequence (1: decode)
+  int qrows;         // query rows per KV head: q_len * group
+  int group_rows;    // rows one wave serves per unit: 16 * NG
+  int n_qgroups;     // units per (KV head, sequence): ceil(qrows / group_rows)
+  int rows;          // rows per partial slot: min(qrows, group_rows)
   int max_ctx;
   int part_tokens;   // 0: balanced split
   int p_max;         // fixed partitions: partitions per unit
@@ -135,10 +148,11 @@ __device__ inline void flag_error(int32_t* err_flag, int bit) {
   if (err_flag) atomicOr(err_flag, bit);
 }
 
-// Tiles of a sequence for the work split: 0 for an invalid context length
-// (the merge kernel reports those and writes NaN rows).
-__device__ inline int seq_tiles(int ctx, int max_ctx) {
-  return (ctx >= 1 && ctx <= max_ctx) ? (ctx + 15) >> 4 : 0;
+// Tiles of a sequence for the work split: 0 for an invalid context length,
+// outside [q_len, max_ctx] (the merge kernel reports those and writes NaN
+// rows).
+__device__ inline int seq_tiles(int ctx, int q_len, int max_ctx) {
+  return (ctx >= q_len && ctx <= max_ctx) ? (ctx + 15) >> 4 : 0;
 }
 
 // Round-to-nearest-even float -> bf16 bits (finite inputs).
@@ -156,7 +170,7 @@ __device__ inline int total_seq_tiles(const DecodeArgs& a, int lane) {
   int sum = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int i = base + lane;
-    sum += wave_sum(i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0);
+    sum += wave_sum(i < a.num_seqs ? seq_tiles(a.context_lens[i], a.q_len, a.max_ctx) : 0);
   }
   return sum;
 }
@@ -168,7 +182,7 @@ __device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int i = base + lane;
-    const int n = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0;
+    const int n = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.q_len, a.max_ctx) : 0;
     const int incl = wave_inclusive_scan(n, lane) + carry;
     const uint64_t hit = __ballot(i < a.num_seqs && incl > r);
     if (hit) {
@@ -208,7 +222,7 @@ __device__ inline int tile_scan_total(const DecodeArgs& a, int lane, TileScan& t
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = lane + 64 * k;
-    ts.n[k] = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.max_ctx) : 0;
+    ts.n[k] = i < a.num_seqs ? seq_tiles(a.context_lens[i], a.q_len, a.max_ctx) : 0;
   }
   int total = 0;
 #pragma unroll
@@ -239,11 +253,47 @@ __device__ inline void tile_scan_locate(const DecodeArgs& a, int lane, const Til
   before_out = carry;
 }
 
-// One segment: tiles [ta, tb) of unit (h, qg, s). Leaves the running
-// reference max m (log2 units, per query row c, identical in the 4 lanes of
-// a column), the column's partial sum l (this lane's tokens only) and the
-// accumulator acc (dims 16m + 4r .. +3 of row c). Returns false if a block
-// id was out of range (nothing else is then meaningful).
+// The query rows one wave serves in a unit: NG groups of 16 lanes' rows,
+// row c of group g being row qg * 16 * NG + 16 * g + c of the unit's KV head.
+// A row stands for (query token i, head within the group jj) with
+// i = row / group, jj = row % group (decode: one token, i = 0). For each
+// group the lane keeps whether its row exists, the row's index into q and
+// out ([num_seqs][q_len][n_q] rows of D values), and with the causal mask
+// the last position the row may see (ctx - q_len + i).
+template <int NG>
+struct Rows {
+  bool valid[NG];
+  int64_t index[NG];
+  int lim[NG];
+};
+
+template <int NG, bool CAUSAL>
+__device__ inline Rows<NG> rows_of(const DecodeArgs& a, int lane, int s, int h, int qg, int ctx) {
+  Rows<NG> rw;
+  const int c = lane & 15;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int gr = qg * 16 * NG + 16 * g + c;
+    rw.valid[g] = gr < a.qrows;
+    if (CAUSAL) {
+      const int i = gr / a.group;
+      const int jj = gr - i * a.group;
+      rw.index[g] = ((int64_t)s * a.q_len + i) * a.n_q + h * a.group + jj;
+      rw.lim[g] = rw.valid[g] ? ctx - a.q_len + i : 0x7fffffff;
+    } else {
+      rw.index[g] = (int64_t)s * a.n_q + h * a.group + gr;
+      rw.lim[g] = 0x7fffffff;
+    }
+  }
+  return rw;
+}
+
+// One segment: tiles [ta, tb) of unit (h, qg, s). Leaves, per row group g,
+// the running reference max m_run[g] (log2 units, per query row c,
+// identical in the 4 lanes of a column), the column's partial sum l_run[g]
+// (this lane's tokens only) and the accumulator acc[g] (dims 16m + 4r .. +3
+// of row c). Returns false if a block id was out of range (nothing else is
+// then meaningful).
 //
 // With a.k_new set and the segment ending at the unit's last tile, the token
 // at position ctx - 1 is this step's new one: its key and value come from
@@ -254,29 +304,39 @@ __device__ inline void tile_scan_locate(const DecodeArgs& a, int lane, const Til
 //
 // STREAM selects non-temporal K/V loads (the tile is used once, so it is not
 // kept in cache at the expense of other data); without it the loads are
-// ordinary, for blocks that other sequences read too.
-template <int D, bool STREAM>
-__device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h, int j_row,
-                                       bool row_valid, int ctx, int ta, int tb, bool store_new,
-                                       f32x4_t* acc, float& m_run, float& l_run) {
+// ordinary, for blocks that other sequences read too. NG row groups share
+// every K/V tile. CAUSAL masks, per row, the positions after the row's own
+// (the verification pass); a row may then see nothing in a whole tile, so
+// its weights and rescale factors are guarded against -inf - (-inf).
+template <int D, bool STREAM, int NG, bool CAUSAL>
+__device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h,
+                                       const Rows<NG>& rw, int ctx, int ta, int tb, bool store_new,
+                                       f32x4_t (&acc)[NG][D / 16], float (&m_run)[NG],
+                                       float (&l_run)[NG]) {
   constexpr int KM = D / 32;   // score MFMAs per tile (k = 32 dims each)
   constexpr int VM = D / 16;   // value MFMAs per tile (16 dims each)
   const int c = lane & 15;
   const int r = lane >> 4;
 
 #pragma unroll
-  for (int m = 0; m < VM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  m_run = -__builtin_inff();
-  l_run = 0.f;
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int m = 0; m < VM; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[g] = -__builtin_inff();
+    l_run[g] = 0.f;
+  }
 
   // Q as the B operand of the score MFMA: lane (c, r) holds row c, dims
   // 32m + 8r .. +8. Rows past the group are zero.
-  bf16x8_t qv[KM];
-  const uint16_t* q_row = a.q + ((int64_t)s * a.n_q + (row_valid ? j_row : 0)) * D;
+  bf16x8_t qv[NG][KM];
 #pragma unroll
-  for (int m = 0; m < KM; ++m) {
-    const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
-    qv[m] = row_valid ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int g = 0; g < NG; ++g) {
+    const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
+      qv[g][m] = rw.valid[g] ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
 
   const int64_t tile_elems = 16 * D;
@@ -288,7 +348,8 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   const int last_tile = (ctx - 1) >> 4;
   const int last_valid = ctx - last_tile * 16;   // tokens in the sequence's last tile
   const int new_slot = last_valid - 1;           // slot of position ctx - 1
-  const bool has_new = a.k_new != nullptr && tb > last_tile;
+  const bool has_new = !CAUSAL && a.k_new != nullptr && tb > last_tile;   // decode only
+  const int first_masked = ctx - a.q_len + 1;    // causal: first position some row may not see
 
   bf16x8_t kA[KM], kB[KM];
   bf16x4_t vA[VM], vB[VM];
@@ -354,18 +415,23 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
           }
         }
       }
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float x[NG][4];
 #pragma unroll
-      for (int m = 0; m < KM; ++m)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[m], sc, 0, 0, 0);
-      float x[4];
+      for (int g = 0; g < NG; ++g) {
+        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = sc[e] * a.scale_log2;
+        for (int m = 0; m < KM; ++m)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[g][e] = sc[e] * a.scale_log2;
+      }
       if (cb + i == last_tile && last_valid < 16) {   // the partly filled last block
         const int valid = last_valid - 4 * r;         // tokens of this quad still inside
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e >= valid) x[e] = -__builtin_inff();
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e >= valid) x[g][e] = -__builtin_inff();
         // masked slots may hold anything (NaN included): zero their values
         const uint32_t keep0 = (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
         const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
@@ -377,34 +443,50 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
           vr[m] = __builtin_bit_cast(bf16x4_t, wv);
         }
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = wave_max_across_rows(mx);
-      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+      if (CAUSAL && (cb + i) * 16 + 15 >= first_masked) {
+        const int p0 = (cb + i) * 16 + 4 * r;   // position of this lane's first token
 #pragma unroll
-        for (int m = 0; m < VM; ++m) acc[m] *= alpha;
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (p0 + e > rw.lim[g]) x[g][e] = -__builtin_inff();
       }
-      float p[4];
+      bf16x8_t pb[NG];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      // P = hi + lo, both bf16: hi by truncation (exact remainder), lo rounded.
-      uint32_t hi[4], lo[4];
+      for (int g = 0; g < NG; ++g) {
+        float mx = fmaxf(fmaxf(x[g][0], x[g][1]), fmaxf(x[g][2], x[g][3]));
+        mx = wave_max_across_rows(mx);
+        if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_run[g], mx);
+          float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+          if (CAUSAL && m_new == -__builtin_inff()) alpha = 1.f;   // row still sees nothing
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
-        lo[e] = bf16_rne_bits(p[e] - __uint_as_float(hi[e]));
+          for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+        }
+        const float m_use = (CAUSAL && m_run[g] == -__builtin_inff()) ? 0.f : m_run[g];
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[g][e] - m_use);
+        l_run[g] += (p[0] + p[1]) + (p[2] + p[3]);
+        // P = hi + lo, both bf16: hi by truncation (exact remainder), lo rounded.
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
+          lo[e] = bf16_rne_bits(p[e] - __uint_as_float(hi[e]));
+        }
+        const u32x4_t pw = u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
+                                   lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        pb[g] = __builtin_bit_cast(bf16x8_t, pw);
       }
-      const u32x4_t pw = u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
-                                 lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int m = 0; m < VM; ++m) {
         const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[g], acc[g][m], 0, 0, 0);
       }
     };
 
@@ -423,22 +505,22 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   return true;
 }
 
-// Write a finished segment: out directly when it covers its whole unit,
-// else a partial into its workspace slot. Rows past the group write nothing.
+// Write a finished segment's row: out directly when the segment covers its
+// whole unit, else a partial into its workspace slot (row g_in_slot of the
+// slot). Rows past the group write nothing.
 template <int D>
 __device__ inline void finish_segment(const DecodeArgs& a, int lane, bool ok, bool whole,
-                                      int64_t slot, int s, int j_row, int g_in_slot,
+                                      int64_t slot, int64_t out_row, int g_in_slot,
                                       bool row_valid, const f32x4_t* acc, float m_run,
                                       float l_run) {
   constexpr int VM = D / 16;
   const int r = lane >> 4;
   const float l_tot = wave_sum_across_rows(l_run);
-  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
   if (!row_valid) return;
   const float nan = __builtin_nanf("");
   if (whole) {
     const float inv = ok ? 1.0f / l_tot : nan;
-    float* o = a.out + ((int64_t)s * a.n_q + j_row) * D + 4 * r;
+    float* o = a.out + out_row * D + 4 * r;
 #pragma unroll
     for (int m = 0; m < VM; ++m) *(f32x4_t*)(o + 16 * m) = acc[m] * inv;
   } else {
@@ -453,6 +535,18 @@ __device__ inline void finish_segment(const DecodeArgs& a, int lane, bool ok, bo
   }
 }
 
+template <int D, int NG>
+__device__ inline void finish_rows(const DecodeArgs& a, int lane, bool ok, bool whole,
+                                   int64_t slot, const Rows<NG>& rw,
+                                   const f32x4_t (&acc)[NG][D / 16], const float (&m_run)[NG],
+                                   const float (&l_run)[NG]) {
+  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    finish_segment<D>(a, lane, ok, whole, slot, rw.index[g], 16 * g + (lane & 15), rw.valid[g],
+                      acc[g], m_run[g], l_run[g]);
+}
+
 // First wave and last wave (inclusive) of the balanced split that touch
 // tiles [t0, t1) of the launch order, t1 > t0.
 __device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int n_waves,
@@ -462,12 +556,11 @@ __device__ inline void waves_of_range(int64_t t0, int64_t t1, int64_t total, int
   w1 = (int)((t1 * n_waves - 1) / total);
 }
 
-// Fixed partitions: one wave per (unit, partition).
+// Fixed partitions: one wave per (unit, partition). Decode only.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_fixed_kernel(DecodeArgs a) {
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15;
   const int unit_part = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
   if (unit_part >= a.n_units * a.p_max) return;
   const int part = unit_part % a.p_max;
@@ -476,36 +569,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int hq = u / a.num_seqs;
   const int h = hq / a.n_qgroups;
   const int qg = hq % a.n_qgroups;
-  const int g = qg * 16 + c;
-  const bool row_valid = g < a.group;
-  const int j = h * a.group + g;
 
   const int ctx = a.context_lens[s];
-  const int nt = seq_tiles(ctx, a.max_ctx);       // invalid: 0, reported by the merge
+  const int nt = seq_tiles(ctx, a.q_len, a.max_ctx);   // invalid: 0, reported by the merge
   const int tiles_per_part = a.part_tokens >> 4;
   const int ta = part * tiles_per_part;
   if (ta >= nt) return;
   const int tb = min(ta + tiles_per_part, nt);
 
-  f32x4_t acc[VM];
-  float m_run, l_run;
+  const Rows<1> rw = rows_of<1, false>(a, lane, s, h, qg, ctx);
+  f32x4_t acc[1][VM];
+  float m_run[1], l_run[1];
   const bool ok =
       shares_first_block(a, s)
-          ? process_segment<D, false>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run, l_run)
-          : process_segment<D, true>(a, lane, s, h, j, row_valid, ctx, ta, tb, false, acc, m_run, l_run);
-  finish_segment<D>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, s, j, c,
-                    row_valid, acc, m_run, l_run);
+          ? process_segment<D, false, 1, false>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run)
+          : process_segment<D, true, 1, false>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run);
+  finish_rows<D, 1>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, rw, acc, m_run,
+                    l_run);
 }
 
 // Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
 // (head, group, sequence, tile) order, T = all tiles of the launch. The
 // wave holding a unit's first tile records, for the merge kernel, the
 // unit's first partial slot and its number of partials (1: written here).
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_balanced_kernel(DecodeArgs a) {
+template <int D, int NG, bool CAUSAL>
+__device__ inline void balanced_body(const DecodeArgs& a) {
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15;
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
   if (w >= a.n_waves) return;
 
@@ -525,14 +615,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       int s, before;
       tile_scan_locate(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
       if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
-      const int g = (hq % a.n_qgroups) * 16 + c;
-      const int j = (hq / a.n_qgroups) * a.group + g;
       const int u = hq * a.num_seqs + s;
-      f32x4_t zero[VM];
+      const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups,
+                                              a.context_lens[s]);
+      f32x4_t zero[NG][VM];
+      float m0[NG], l0[NG];
 #pragma unroll
-      for (int m = 0; m < VM; ++m) zero[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      finish_segment<D>(a, lane, true, false, (int64_t)w + u, s, j, c, g < a.group, zero,
-                        -__builtin_inff(), 0.f);
+      for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int m = 0; m < VM; ++m) zero[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m0[g] = -__builtin_inff();
+        l0[g] = 0.f;
+      }
+      finish_rows<D, NG>(a, lane, true, false, (int64_t)w + u, rw, zero, m0, l0);
     }
     return;
   }
@@ -545,13 +640,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   int ctx = a.context_lens[s];
 
   while (true) {
-    const int nt = seq_tiles(ctx, a.max_ctx);
+    const int nt = seq_tiles(ctx, a.q_len, a.max_ctx);
     const int tb = (int)min((int64_t)nt, pos + (end - cur));
     const int h = hq / a.n_qgroups;
     const int qg = hq % a.n_qgroups;
-    const int g = qg * 16 + c;
-    const bool row_valid = g < a.group;
-    const int j = h * a.group + g;
     const int u = hq * a.num_seqs + s;
     const bool whole = pos == 0 && tb == nt;
 
@@ -561,15 +653,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       a.unit_info[2 * u] = w0 + u;
       a.unit_info[2 * u + 1] = w1 - w0 + 1;
     }
-    f32x4_t acc[VM];
-    float m_run, l_run;
+    const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, h, qg, ctx);
+    f32x4_t acc[NG][VM];
+    float m_run[NG], l_run[NG];
     const bool ok =
         shares_first_block(a, s)
-            ? process_segment<D, false>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
-                                        m_run, l_run)
-            : process_segment<D, true>(a, lane, s, h, j, row_valid, ctx, pos, tb, qg == 0, acc,
-                                       m_run, l_run);
-    finish_segment<D>(a, lane, ok, whole, (int64_t)w + u, s, j, c, row_valid, acc, m_run, l_run);
+            ? process_segment<D, false, NG, CAUSAL>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
+                                                    m_run, l_run)
+            : process_segment<D, true, NG, CAUSAL>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
+                                                   m_run, l_run);
+    finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
     cur += tb - pos;
     if (cur >= end) break;
     // next unit with work: following sequence, or the next (head, group)
@@ -580,8 +673,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (++hq >= n_hq) return;   // unreachable for consistent context lengths
       }
       ctx = a.context_lens[s];
-    } while (seq_tiles(ctx, a.max_ctx) == 0);
+    } while (seq_tiles(ctx, a.q_len, a.max_ctx) == 0);
   }
+}
+
+// The decode step's kernel: one query row per head, the append fused in.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_balanced_kernel(DecodeArgs a) {
+  balanced_body<D, 1, false>(a);
+}
+
+// The verification pass: q_len query tokens per sequence, causal among
+// them, NG groups of 16 rows per wave. Held to two waves per SIMD's
+// registers even with two groups (a couple of spilled values at head_dim
+// 128): measured faster than one wave with no spills, as the compiler then
+// schedules the loads of the next tile further ahead.
+template <int D, int NG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_verify_kernel(DecodeArgs a) {
+  balanced_body<D, NG, true>(a);
 }
 
 // Merge kernel: one wave per (unit, query row). With reference maxima m_p,
@@ -591,7 +700,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // lane i owns dims PER*i .. PER*i + PER - 1. A NaN maximum (a bad block id
 // met by the partition kernel) makes the row NaN; a sequence with an
 // invalid context length gets NaN rows and the error bit. Units one wave
-// covered were written by the partition kernel and are skipped.
+// covered were written by the partition kernel and are skipped. A partial
+// whose row saw nothing (maximum -inf, sum 0) has weight 0.
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
@@ -603,17 +713,19 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   const int s = u % a.num_seqs;
   const int hq = u / a.num_seqs;
   const int qg = hq % a.n_qgroups;
-  const int g = qg * 16 + g_in_slot;
-  if (g >= a.group) return;
-  const int j = (hq / a.n_qgroups) * a.group + g;
-  float* o = a.out + ((int64_t)s * a.n_q + j) * D + lane * PER;
+  const int gr = qg * a.group_rows + g_in_slot;
+  if (gr >= a.qrows) return;
+  const int i = gr / a.group;
+  const int64_t out_row =
+      ((int64_t)s * a.q_len + i) * a.n_q + (hq / a.n_qgroups) * a.group + (gr - i * a.group);
+  float* o = a.out + out_row * D + lane * PER;
   const float nan = __builtin_nanf("");
 
-  const int nt = seq_tiles(a.context_lens[s], a.max_ctx);
+  const int nt = seq_tiles(a.context_lens[s], a.q_len, a.max_ctx);
   if (nt == 0) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = nan;
-    if (hq == 0 && g == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
+    if (hq == 0 && gr == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
     return;
   }
   int64_t first;
@@ -685,35 +797,68 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 
-static int rows_per_slot(int n_q, int n_kv) { return (n_q / n_kv) < 16 ? (n_q / n_kv) : 16; }
+// Shape of one launch: decode (q_len 1, one 16-row group per wave, no mask)
+// or the verification pass (q_len query tokens, causal, one or two 16-row
+// groups per wave).
+struct Geom {
+  int num_seqs, n_q, n_kv, q_len, ng;
+  bool causal;
+  int qrows() const { return q_len * (n_q / n_kv); }
+  int group_rows() const { return 16 * ng; }
+  int rows() const { return qrows() < group_rows() ? qrows() : group_rows(); }
+  int64_t qgroups() const { return (qrows() + group_rows() - 1) / group_rows(); }
+  int64_t units() const { return (int64_t)n_kv * qgroups() * num_seqs; }
+};
 
-static int64_t n_units_of(int num_seqs, int n_q, int n_kv) {
-  const int64_t qgroups = (n_q / n_kv + 15) / 16;
-  return (int64_t)n_kv * qgroups * num_seqs;
+static Geom decode_geom(int num_seqs, int n_q, int n_kv) { return Geom{num_seqs, n_q, n_kv, 1, 1, false}; }
+
+// The verification pass serves up to 32 rows per KV head from each K/V
+// tile (two row groups); a decode with more than 16 query heads per KV
+// head uses 16-row groups.
+static Geom verify_geom(int num_seqs, int q_len, int n_q, int n_kv) {
+  const int qrows = q_len * (n_q / n_kv);
+  return Geom{num_seqs, n_q, n_kv, q_len, qrows > 16 ? 2 : 1, true};
 }
 
 // Upper bound of the balanced split's wave count: at most kMaxSplitWaves,
 // and no more than leaves kMinTilesPerWave tiles of the upper bound of the
 // tile count per wave. The launch uses min(this, resident_waves()).
-static int64_t split_wave_cap(int num_seqs, int n_q, int n_kv, int max_ctx) {
-  const int64_t tiles_ub = n_units_of(num_seqs, n_q, n_kv) * ((max_ctx + 15) / 16);
+static int64_t split_wave_cap(const Geom& g, int max_ctx) {
+  const int64_t tiles_ub = g.units() * ((max_ctx + 15) / 16);
   int64_t w = (tiles_ub + kMinTilesPerWave - 1) / kMinTilesPerWave;
   if (w > kMaxSplitWaves) w = kMaxSplitWaves;
   return w < 1 ? 1 : w;
 }
 
-static int resident_waves(int head_dim) {
-  static int cache[2][64];   // [head_dim == 128][device]
+template <typename K>
+static int occupancy_blocks(K kernel) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) != hipSuccess) return -1;
+  return blocks;
+}
+
+static int kernel_blocks_per_cu(const Geom& g, int head_dim) {
+  if (!g.causal)
+    return head_dim == 128 ? occupancy_blocks(paged_attn_balanced_kernel<128>)
+                           : occupancy_blocks(paged_attn_balanced_kernel<64>);
+  if (g.ng == 1)
+    return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 1>)
+                           : occupancy_blocks(paged_attn_verify_kernel<64, 1>);
+  return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 2>)
+                         : occupancy_blocks(paged_attn_verify_kernel<64, 2>);
+}
+
+static int resident_waves(const Geom& g, int head_dim) {
+  static int cache[3][2][64];   // [kernel: decode, verify 1 group, verify 2][head_dim == 128][device]
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  int& slot = cache[head_dim == 128][dev];
+  const int kind = !g.causal ? 0 : (g.ng == 1 ? 1 : 2);
+  int& slot = cache[kind][head_dim == 128][dev];
   if (slot > 0) return slot;
-  int cus = 0, blocks = 0;
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  hipError_t e = head_dim == 128
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<128>, 256, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, paged_attn_balanced_kernel<64>, 256, 0);
-  if (e != hipSuccess || blocks < 1 || cus < 1) return -1;
+  const int blocks = kernel_blocks_per_cu(g, head_dim);
+  if (blocks < 1 || cus < 1) return -1;
   // the split uses one wave per SIMD (4 per compute unit) for head_dim 128
   // and two for head_dim 64, whose tiles are half the bytes: enough loads in
   // flight, few per-wave start-up costs, and every wave resident
@@ -726,23 +871,22 @@ static int resident_waves(int head_dim) {
 // Workspace of the balanced split: per unit its first partial slot and
 // partial count (2 x int32, rounded up to 256 bytes), then the partial
 // slots. Fixed partitions: the partial slots only.
-static size_t unit_info_bytes(int num_seqs, int n_q, int n_kv) {
-  return (size_t)((n_units_of(num_seqs, n_q, n_kv) * 8 + 255) / 256 * 256);
+static size_t unit_info_bytes(const Geom& g) {
+  return (size_t)((g.units() * 8 + 255) / 256 * 256);
 }
 
-static int64_t slot_count(int num_seqs, int n_q, int n_kv, int max_ctx, int part) {
-  const int64_t units = n_units_of(num_seqs, n_q, n_kv);
+static int64_t slot_count(const Geom& g, int max_ctx, int part) {
   if (part > 0) {
     const int p_max = (max_ctx + part - 1) / part;
-    return p_max <= 1 ? 0 : units * p_max;
+    return p_max <= 1 ? 0 : g.units() * p_max;
   }
-  return split_wave_cap(num_seqs, n_q, n_kv, max_ctx) + units;
+  return split_wave_cap(g, max_ctx) + g.units();
 }
 
-static size_t workspace_bytes(int num_seqs, int n_q, int n_kv, int d, int max_ctx, int part) {
-  const size_t slots_bytes = (size_t)slot_count(num_seqs, n_q, n_kv, max_ctx, part) *
-                             rows_per_slot(n_q, n_kv) * (2 + d) * sizeof(float);
-  return (part > 0 ? 0 : unit_info_bytes(num_seqs, n_q, n_kv)) + slots_bytes;
+static size_t workspace_bytes(const Geom& g, int d, int max_ctx, int part) {
+  const size_t slots_bytes =
+      (size_t)slot_count(g, max_ctx, part) * g.rows() * (2 + d) * sizeof(float);
+  return (part > 0 ? 0 : unit_info_bytes(g)) + slots_bytes;
 }
 
 }  // namespace pkv
@@ -751,40 +895,55 @@ using namespace pkv;
 
 static bool valid_partition_arg(int32_t p) { return p >= 0 && p % 16 == 0 && p <= 1024; }
 
+static bool valid_heads(int32_t num_seqs, int32_t n_q, int32_t n_kv, int32_t d, int32_t max_ctx) {
+  return num_seqs > 0 && n_q > 0 && n_kv > 0 && d > 0 && max_ctx > 0 && n_q % n_kv == 0;
+}
+
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                              int32_t n_kv_heads, int32_t head_dim,
                                              int32_t max_context_len,
                                              int32_t partition_tokens) {
-  if (num_seqs <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
-    return 0;
-  if (n_q_heads % n_kv_heads != 0 || !valid_partition_arg(partition_tokens)) return 0;
-  return workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
+  if (!valid_heads(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len)) return 0;
+  if (!valid_partition_arg(partition_tokens)) return 0;
+  return workspace_bytes(decode_geom(num_seqs, n_q_heads, n_kv_heads), head_dim, max_context_len,
                          partition_tokens);
+}
+
+extern "C" size_t pkv_verify_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t n_q_heads,
+                                             int32_t n_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len) {
+  if (!valid_heads(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len)) return 0;
+  if (q_len < 1 || q_len > kMaxQueryTokens) return 0;
+  if (q_len == 1)
+    return workspace_bytes(decode_geom(num_seqs, n_q_heads, n_kv_heads), head_dim,
+                           max_context_len, 0);
+  return workspace_bytes(verify_geom(num_seqs, q_len, n_q_heads, n_kv_heads), head_dim,
+                         max_context_len, 0);
 }
 
 extern "C" int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
                                           int32_t head_dim, int32_t max_context_len) {
-  if (num_seqs <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_context_len <= 0 ||
-      n_q_heads % n_kv_heads != 0)
-    return PKV_EINVAL;
+  if (!valid_heads(num_seqs, n_q_heads, n_kv_heads, 1, max_context_len)) return PKV_EINVAL;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
-  const int res = resident_waves(head_dim);
+  const Geom g = decode_geom(num_seqs, n_q_heads, n_kv_heads);
+  const int res = resident_waves(g, head_dim);
   if (res < 1) return PKV_EHIP;
-  const int64_t cap = split_wave_cap(num_seqs, n_q_heads, n_kv_heads, max_context_len);
+  const int64_t cap = split_wave_cap(g, max_context_len);
   return (int32_t)(res < cap ? res : cap);
 }
 
-// Host-side checks and launch geometry shared by the three entry points.
-static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, const void* k_pool,
-                   const void* v_pool, const int32_t* block_tables, const int32_t* context_lens,
-                   int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
-                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                   int32_t max_context_len, int32_t partition_tokens, void* workspace,
-                   size_t workspace_bytes_given, int32_t* err_flag) {
-  if (num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || n_q_heads < 1 ||
-      n_kv_heads < 1 || max_context_len < 1)
+// Host-side checks and launch geometry shared by the entry points.
+static int prepare(DecodeArgs& a, int& head_dim_out, const Geom& g, float* out, const void* q,
+                   const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                   const int32_t* context_lens, int32_t max_blocks_per_seq, int32_t num_blocks,
+                   int32_t head_dim, float scale, int32_t max_context_len,
+                   int32_t partition_tokens, void* workspace, size_t workspace_bytes_given,
+                   int32_t* err_flag) {
+  const int32_t num_seqs = g.num_seqs;
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || g.n_q < 1 || g.n_kv < 1 ||
+      max_context_len < 1)
     return PKV_EINVAL;
-  if (n_q_heads % n_kv_heads != 0) return PKV_EINVAL;
+  if (g.n_q % g.n_kv != 0) return PKV_EINVAL;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   if ((int64_t)max_context_len > 16 * (int64_t)max_blocks_per_seq) return PKV_EINVAL;
   if (!valid_partition_arg(partition_tokens)) return PKV_EINVAL;
@@ -802,29 +961,31 @@ static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, 
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.n_q = n_q_heads;
-  a.n_kv = n_kv_heads;
-  a.group = n_q_heads / n_kv_heads;
-  a.n_qgroups = (a.group + 15) / 16;
-  a.rows = rows_per_slot(n_q_heads, n_kv_heads);
+  a.n_q = g.n_q;
+  a.n_kv = g.n_kv;
+  a.group = g.n_q / g.n_kv;
+  a.q_len = g.q_len;
+  a.qrows = g.qrows();
+  a.group_rows = g.group_rows();
+  a.n_qgroups = (int)g.qgroups();
+  a.rows = g.rows();
   a.max_ctx = max_context_len;
   a.part_tokens = partition_tokens;
   a.p_max = partition_tokens > 0 ? (max_context_len + partition_tokens - 1) / partition_tokens : 0;
   a.scale_log2 = scale * kLog2e;
   head_dim_out = head_dim;
 
-  const int64_t units = n_units_of(num_seqs, n_q_heads, n_kv_heads);
+  const int64_t units = g.units();
   if (units > (int64_t)INT32_MAX / 64) return PKV_EINVAL;
   // tiles of one (head, group) row of the split are counted in 32 bits
   if ((int64_t)num_seqs * ((max_context_len + 15) / 16) > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
   a.n_units = (int)units;
   if (num_seqs == 0) return PKV_OK;
 
-  const size_t need = workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
-                                      partition_tokens);
+  const size_t need = workspace_bytes(g, head_dim, max_context_len, partition_tokens);
   if (need > 0 && (workspace == nullptr || workspace_bytes_given < need)) return PKV_EWORKSPACE;
-  const int64_t slots = slot_count(num_seqs, n_q_heads, n_kv_heads, max_context_len, partition_tokens);
-  const size_t info = partition_tokens > 0 ? 0 : unit_info_bytes(num_seqs, n_q_heads, n_kv_heads);
+  const int64_t slots = slot_count(g, max_context_len, partition_tokens);
+  const size_t info = partition_tokens > 0 ? 0 : unit_info_bytes(g);
   a.unit_info = partition_tokens > 0 ? nullptr : (int32_t*)workspace;
   a.ws_ml = slots > 0 ? (float*)((char*)workspace + info) : nullptr;
   a.ws_acc = slots > 0 ? a.ws_ml + 2 * slots * a.rows : nullptr;
@@ -837,9 +998,9 @@ static int prepare(DecodeArgs& a, int& head_dim_out, float* out, const void* q, 
     if (waves > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
     a.n_waves = 0;
   } else {
-    const int res = resident_waves(head_dim);
+    const int res = resident_waves(g, head_dim);
     if (res < 1) return PKV_EHIP;
-    const int64_t cap = split_wave_cap(num_seqs, n_q_heads, n_kv_heads, max_context_len);
+    const int64_t cap = split_wave_cap(g, max_context_len);
     waves = res < cap ? res : cap;
     a.n_waves = (int)waves;
   }
@@ -864,6 +1025,23 @@ static int launch_partition(const DecodeArgs& a, int head_dim, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+static int launch_verify(const DecodeArgs& a, int head_dim, hipStream_t st) {
+  const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
+  const bool two = a.group_rows == 32;
+  if (head_dim == 128) {
+    if (two)
+      hipLaunchKernelGGL((paged_attn_verify_kernel<128, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((paged_attn_verify_kernel<128, 1>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    if (two)
+      hipLaunchKernelGGL((paged_attn_verify_kernel<64, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((paged_attn_verify_kernel<64, 1>), dim3(grid), dim3(256), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 static int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
   const unsigned mgrid = (unsigned)(((int64_t)a.n_units * a.rows + kWaves - 1) / kWaves);
   if (head_dim == 128)
@@ -879,15 +1057,15 @@ static int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
       int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, \
       int32_t head_dim, float scale, int32_t max_context_len, int32_t partition_tokens,      \
       void *workspace, size_t workspace_bytes_given, int32_t *err_flag, void *stream
-#define PKV_DECODE_ARGS                                                                      \
-  out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,          \
-      num_blocks, n_q_heads, n_kv_heads, head_dim, scale, max_context_len, partition_tokens, \
-      workspace, workspace_bytes_given, err_flag
+#define PKV_DECODE_PREP_ARGS                                                                  \
+  decode_geom(num_seqs, n_q_heads, n_kv_heads), out, q, k_pool, v_pool, block_tables,         \
+      context_lens, max_blocks_per_seq, num_blocks, head_dim, scale, max_context_len,        \
+      partition_tokens, workspace, workspace_bytes_given, err_flag
 
 extern "C" int pkv_paged_attn_partition(PKV_DECODE_PARAMS) {
   DecodeArgs a;
   int d = 0;
-  const int rc = prepare(a, d, PKV_DECODE_ARGS);
+  const int rc = prepare(a, d, PKV_DECODE_PREP_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return launch_partition(a, d, (hipStream_t)stream);
 }
@@ -895,7 +1073,7 @@ extern "C" int pkv_paged_attn_partition(PKV_DECODE_PARAMS) {
 extern "C" int pkv_paged_attn_merge(PKV_DECODE_PARAMS) {
   DecodeArgs a;
   int d = 0;
-  const int rc = prepare(a, d, PKV_DECODE_ARGS);
+  const int rc = prepare(a, d, PKV_DECODE_PREP_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return launch_merge(a, d, (hipStream_t)stream);
 }
@@ -909,7 +1087,7 @@ static int decode_launch(DecodeArgs& a, int d, hipStream_t st) {
 extern "C" int pkv_paged_attn_decode(PKV_DECODE_PARAMS) {
   DecodeArgs a;
   int d = 0;
-  const int rc = prepare(a, d, PKV_DECODE_ARGS);
+  const int rc = prepare(a, d, PKV_DECODE_PREP_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return decode_launch(a, d, (hipStream_t)stream);
 }
@@ -925,10 +1103,7 @@ extern "C" int pkv_paged_attn_decode(PKV_DECODE_PARAMS) {
 // split one launch (the append inside the partition kernel), with a fixed
 // partition size kv_append then the partition kernel.
 static int step_partition(DecodeArgs& a, int& d, PKV_STEP_PARAMS) {
-  const int rc = prepare(a, d, out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
-                         max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads, head_dim, scale,
-                         max_context_len, partition_tokens, workspace, workspace_bytes_given,
-                         err_flag);
+  const int rc = prepare(a, d, PKV_DECODE_PREP_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   if (!k_new || !v_new) return PKV_EINVAL;
   if (partition_tokens == 0) {
@@ -959,4 +1134,29 @@ extern "C" int pkv_decode_step(PKV_STEP_PARAMS) {
   const int rc = step_partition(a, d, PKV_STEP_ARGS);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return launch_merge(a, d, (hipStream_t)stream);
+}
+
+extern "C" int pkv_paged_attn_verify(float* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t q_len,
+                                     int32_t max_blocks_per_seq, int32_t num_blocks,
+                                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                     float scale, int32_t max_context_len, void* workspace,
+                                     size_t workspace_bytes_given, int32_t* err_flag,
+                                     void* stream) {
+  if (q_len < 1 || q_len > kMaxQueryTokens || n_kv_heads < 1) return PKV_EINVAL;
+  if (q_len == 1)   // one query token: the decode itself
+    return pkv_paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                                 max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads, head_dim,
+                                 scale, max_context_len, 0, workspace, workspace_bytes_given,
+                                 err_flag, stream);
+  DecodeArgs a;
+  int d = 0;
+  const int rc = prepare(a, d, verify_geom(num_seqs, q_len, n_q_heads, n_kv_heads), out, q,
+                         k_pool, v_pool, block_tables, context_lens, max_blocks_per_seq,
+                         num_blocks, head_dim, scale, max_context_len, 0, workspace,
+                         workspace_bytes_given, err_flag);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  const int vrc = launch_verify(a, d, (hipStream_t)stream);
+  return vrc != PKV_OK ? vrc : launch_merge(a, d, (hipStream_t)stream);
 }

@@ -138,3 +138,39 @@ def _decode_step_host_checks(pkv, f, dummy):
              256, 0, dummy, 1 << 30, None, None) == pkv.PKV_EINVAL
     assert f(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 0, 16, 64, 8, 2, 128, 0.1,
              256, 0, None, 0, None, None) == pkv.PKV_OK
+
+
+def test_verify_workspace_formula():
+    """The verification pass: q_len * G rows per KV head, served in groups
+    of 32 when there are more than 16 (else one group), one slot per wave
+    plus one per unit, (d + 2) floats per row."""
+    import paged_kv_cache_468_amd as pkv
+    cnt = lambda units: (units * 8 + 255) // 256 * 256
+    # LLaMA-3-8B shape, 5 query tokens: 20 rows -> one 32-row group per KV head
+    units = 64 * 8
+    assert pkv.pkv_verify_workspace_bytes(64, 5, 32, 8, 128, 8192) == cnt(units) + (units + 8192) * 20 * 130 * 4
+    # 3 tokens, G = 4: 12 rows, one 16-row group
+    assert pkv.pkv_verify_workspace_bytes(4, 3, 8, 2, 64, 256) == cnt(8) + (8 + 8) * 12 * 66 * 4
+    # 20 tokens, G = 4: 80 rows -> 3 groups of 32 per KV head
+    assert pkv.pkv_verify_workspace_bytes(2, 20, 4, 1, 128, 64) == cnt(6) + (6 + 2) * 32 * 130 * 4
+    # one token is the decode
+    assert pkv.pkv_verify_workspace_bytes(64, 1, 32, 8, 128, 8192) == \
+        pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 8192, 0)
+    # bad arguments
+    assert pkv.pkv_verify_workspace_bytes(4, 0, 8, 2, 64, 256) == 0
+    assert pkv.pkv_verify_workspace_bytes(4, 65, 8, 2, 64, 256) == 0
+    assert pkv.pkv_verify_workspace_bytes(4, 3, 9, 2, 64, 256) == 0
+
+
+def test_verify_host_checks():
+    import paged_kv_cache_468_amd as pkv
+    d = ctypes.c_void_p(0x1000)
+    f = pkv.lib.pkv_paged_attn_verify
+    #      out q  kp vp bt cl  B  qlen mb  nb  nq nkv hd  scale maxctx ws bytes err stream
+    assert f(d, d, d, d, d, d, 4, 0, 16, 64, 8, 2, 128, 0.1, 256, d, 1 << 30, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 65, 16, 64, 8, 2, 128, 0.1, 256, d, 1 << 30, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 5, 16, 64, 8, 2, 96, 0.1, 256, d, 1 << 30, None, None) == pkv.PKV_EUNSUPPORTED
+    assert f(d, d, d, d, d, d, 4, 5, 16, 64, 9, 2, 128, 0.1, 256, d, 1 << 30, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 5, 16, 64, 8, 2, 128, 0.1, 257, d, 1 << 30, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 0, 5, 16, 64, 8, 2, 128, 0.1, 256, None, 0, None, None) == pkv.PKV_OK
+    assert f(d, d, d, d, d, d, 4, 5, 16, 64, 8, 2, 128, 0.1, 256, d, 16, None, None) == pkv.PKV_EWORKSPACE

@@ -1,0 +1,162 @@
+"""The verification pass of speculative decoding on the GPU against the
+oracle: q_len query tokens per sequence, query token i at position
+ctx - q_len + i seeing positions [0, ctx - q_len + i].
+
+Cases span one and two 16-row groups per wave and several 32-row groups
+per KV head, d 64 and 128, contexts equal to q_len, drafts crossing a
+block boundary, tiny contexts (more waves than tiles, so partials of rows
+that see nothing in their range), NaN in every unused slot and block. The
+bar: max-abs error <= 1e-3 on fp32 outputs; q_len = 1 bitwise equal to the
+decode; invalid contexts flagged with NaN rows. At the LLaMA-3-8B shape
+(one layer, 64 sequences, contexts U[1024, 8192], shared prefix, 5 query
+tokens) sampled sequences are checked against the oracle.
+"""
+import numpy as np
+import pytest
+
+import workload as w
+from gpu_util import TOL, max_abs, to_dev_bf16, to_dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_468_amd as lib
+    return lib
+
+
+def _shape(n_q, n_kv, d):
+    return w.Shape(f"{n_q}/{n_kv} d{d}", 1, n_q, n_kv, d, 1, 1, 1)
+
+
+def _run(pkv, hc, qv, max_ctx=None, scale=None):
+    import torch
+    sh = hc.shape
+    scale = sh.scale if scale is None else scale
+    max_ctx = int(hc.tables.context_lens.max()) if max_ctx is None else max_ctx
+    kp, vp = to_dev_bf16(hc.k_pool), to_dev_bf16(hc.v_pool)
+    bt, cl = to_dev_i32(hc.tables.block_tables), to_dev_i32(hc.tables.context_lens)
+    q = to_dev_bf16(qv)
+    out = torch.full(qv.shape, float("nan"), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_attn_verify(out, q, kp, vp, bt, cl, scale, max_ctx, err_flag=err)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), int(err.item())
+
+
+CASES = [  # n_q, n_kv, d, contexts, q_len   (rows per KV head = q_len * G)
+    (32, 8, 128, [5, 17, 300, 1000, 4099], 5),      # 20 rows: two 16-row groups in one wave
+    (32, 8, 128, [3, 16, 33, 700], 3),              # 12 rows: one group
+    (32, 8, 128, [8, 64, 1500], 8),                 # 32 rows exactly
+    (8, 8, 128, [9, 31, 32, 33, 2000], 8),          # MHA, 8 rows
+    (20, 4, 64, [7, 18, 513, 2048], 7),             # G = 5: 35 rows -> two 32-row groups
+    (20, 4, 64, [2, 15, 16, 17, 129], 2),           # 10 rows, d 64
+    (64, 8, 128, [40, 8000], 4),                    # G = 8: 32 rows
+    (8, 1, 64, [20, 21, 47, 48, 49], 20),           # MQA, 160 rows -> five groups
+    (16, 1, 128, [64, 65, 300], 3),                 # G = 16: 48 rows -> two groups
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_verify_matches_oracle(pkv, orc, case):
+    n_q, n_kv, d, ctx, q_len = CASES[case]
+    hc = w.host_case(_shape(n_q, n_kv, d), 300 + case, context_lens=ctx)
+    qv = w.normal_bf16(w.rng(300 + case, 12), (len(ctx), q_len, n_q, d))
+    got, err = _run(pkv, hc, qv)
+    want, rc = orc.verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables, hc.tables.context_lens,
+                          n_kv, hc.shape.scale)
+    assert rc == 0 and err == 0
+    assert np.isfinite(got).all()
+    e = max_abs(got, want)
+    print(f"case {case}: q_len {q_len}, {q_len * n_q // n_kv} rows per KV head: max-abs {e:.2e}")
+    assert e <= TOL, e
+
+
+def test_one_token_is_the_decode(pkv):
+    """q_len = 1 runs the decode's kernels: the same bits."""
+    import torch
+    hc = w.host_case(_shape(32, 8, 128), 320, context_lens=[1, 17, 300, 2049])
+    dev_q = to_dev_bf16(hc.q)
+    kp, vp = to_dev_bf16(hc.k_pool), to_dev_bf16(hc.v_pool)
+    bt, cl = to_dev_i32(hc.tables.block_tables), to_dev_i32(hc.tables.context_lens)
+    a = torch.empty((4, 32, 128), dtype=torch.float32, device="cuda")
+    b = torch.empty((4, 1, 32, 128), dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attn_decode(a, dev_q, kp, vp, bt, cl, hc.shape.scale, 2049)
+    pkv.pkv_paged_attn_verify(b, dev_q.view(4, 1, 32, 128), kp, vp, bt, cl, hc.shape.scale, 2049)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy(), b[:, 0].cpu().numpy())
+
+
+def test_many_waves_few_tiles(pkv, orc):
+    """Contexts of a few tokens and a large max_context_len: more waves than
+    tiles, empty wave ranges inside units, and segments whose rows see
+    nothing at all (their partials must weigh nothing)."""
+    n_q, n_kv, d, q_len = 32, 8, 128, 6
+    ctx = [6, 7, 16, 17, 22, 6, 40]
+    hc = w.host_case(_shape(n_q, n_kv, d), 330, context_lens=ctx, max_blocks=512)
+    qv = w.normal_bf16(w.rng(330, 12), (len(ctx), q_len, n_q, d))
+    got, err = _run(pkv, hc, qv, max_ctx=8192)
+    want, rc = orc.verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables, hc.tables.context_lens,
+                          n_kv, hc.shape.scale)
+    assert rc == 0 and err == 0
+    assert max_abs(got, want) <= TOL
+
+
+def test_invalid_context_flagged(pkv, orc):
+    """A context shorter than q_len is invalid: error bit, NaN rows; the
+    other sequences are still right."""
+    import paged_kv_cache_468_amd as lib
+    n_q, n_kv, d, q_len = 8, 2, 64, 4
+    ctx = [30, 3, 50]
+    hc = w.host_case(_shape(n_q, n_kv, d), 340, context_lens=ctx)
+    qv = w.normal_bf16(w.rng(340, 12), (3, q_len, n_q, d))
+    got, err = _run(pkv, hc, qv)
+    assert err & lib.PKV_DEVERR_CONTEXT
+    assert np.isnan(got[1]).all()
+    want, rc = orc.verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables, hc.tables.context_lens,
+                          n_kv, hc.shape.scale)
+    assert rc == -1
+    assert max_abs(got[[0, 2]], want[[0, 2]]) <= TOL
+
+
+def test_llama3_shape_sampled(pkv, orc):
+    """One layer of the LLaMA-3-8B shape (64 sequences, contexts
+    U[1024, 8192], 2,048-token shared prefix) with 5 query tokens per
+    sequence, the launch the benchmark times; the shortest, the longest and
+    six random sequences checked against the oracle."""
+    import torch
+    shape = w.CONFIGS[4]
+    t = w.build_tables(shape, 4)
+    ks, vs = w.pool_shapes(t.num_blocks, shape.n_kv, shape.d)
+    kp = torch.empty(ks, dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty(vs, dtype=torch.bfloat16, device="cuda")
+    w.device_normal_bf16_(kp, 41)
+    w.device_normal_bf16_(vp, 42)
+    for dst, src in t.copies:
+        kp[int(dst)] = kp[int(src)]
+        vp[int(dst)] = vp[int(src)]
+    B, q_len = len(t.context_lens), 5
+    qv = w.normal_bf16(w.rng(4, 13), (B, q_len, shape.n_q, shape.d))
+    out = torch.full(qv.shape, float("nan"), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_attn_verify(out, to_dev_bf16(qv), kp, vp, to_dev_i32(t.block_tables),
+                              to_dev_i32(t.context_lens), shape.scale, int(t.context_lens.max()),
+                              err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    k_h = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    v_h = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    cl = t.context_lens
+    pick = sorted({int(np.argmin(cl)), int(np.argmax(cl))} |
+                  set(int(x) for x in w.rng(4, 14).choice(B, 6, replace=False)))
+    want, rc = orc.verify(qv[pick], k_h, v_h, t.block_tables[pick], cl[pick], shape.n_kv,
+                          shape.scale)
+    assert rc == 0
+    e = max_abs(got[pick], want)
+    print(f"llama3 shape, q_len 5, sequences {pick}: max-abs {e:.2e}")
+    assert e <= TOL
