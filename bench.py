@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 VOCAB = 128256          # LLaMA-3 vocabulary: the acceptance rule's draw runs over it
 BLOCK = 16
 # counter summaries: profiles/pmc_<kernel>_<workload>.txt, ending in a JSON record
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_paged_attn_balanced_{workload}.txt")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_{kernel}_{workload}.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_468_amd", "csrc", "attention.hip")
 
 WORKLOAD_NAMES = {
@@ -385,11 +385,11 @@ def cpu_baseline(torch, S, budget_s):
     }, worst, done
 
 
-def stored_traffic(workload, kernel):
-    """HBM bytes per launch of the roofline kernel from the committed counter
-    summary of this workload (profiles/pmc_*), if it was taken on the current
-    kernel source and the same entry point."""
-    path = PMC_FILE.format(workload=workload)
+def stored_traffic(workload, kernel, kernel_file="paged_attn_balanced"):
+    """HBM bytes per launch of the roofline kernel (entry `kernel`) from the
+    committed counter summary of this workload (profiles/pmc_*), if it was
+    taken on the current kernel source."""
+    path = PMC_FILE.format(kernel=kernel_file, workload=workload)
     if not os.path.exists(path):
         return None, "no counter summary"
     rec = None
@@ -611,6 +611,20 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
     }
 
 
+def copy_calibration(torch, mib):
+    """A plain device copy of mib MiB, three times: the reference the
+    counter runs scale FETCH_SIZE and WRITE_SIZE by."""
+    if mib <= 0:
+        return
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -663,6 +677,9 @@ def main():
                           graph=not args.no_graph)
         log(f"[bench] verify: {vr['ms_per_step']:.3f} ms/step, write {vr['write_us']:.1f} us, "
             f"verify {vr['verify_us']:.1f} us per layer")
+        vtraffic, vwhy = (stored_traffic(f"llama3-8b-verify{args.verify_tokens}", "paged_attn_verify",
+                                         "paged_attn_verify")
+                          if args.config == 4 and share_v else (None, "other workload"))
         line = {
             "metric": "speculative verification pass: KV GB/s and time vs one decode step",
             "value": vr["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -680,9 +697,14 @@ def main():
             "vocab": VOCAB,
             "roofline": {"kernel": "paged_attn_verify", "bound": "hbm", "achieved": vr["verify_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": vr["verify_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                         "alg_bytes_per_launch": vr["verify_alg_bytes"]},
+                         "frac": vr["verify_gbs"] / HBM_PEAK_GBS, "traffic": vtraffic,
+                         "traffic_note": vwhy, "alg_bytes_per_launch": vr["verify_alg_bytes"],
+                         "note": "events around each pkv_paged_attn_verify call (verify and merge "
+                                 "kernels); logical bytes with the shared prefix"},
         }
+        del S
+        torch.cuda.empty_cache()
+        copy_calibration(torch, args.copy_calibration_mib)
         print(json.dumps(line), flush=True)
         return
 
@@ -728,15 +750,7 @@ def main():
         del S2
         torch.cuda.empty_cache()
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        a.fill_(1)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    copy_calibration(torch, args.copy_calibration_mib)
 
     traffic, why = (stored_traffic("llama3-8b-shared" if share_main else "llama3-8b-no-share",
                                    main_r["dominant"]) if args.config == 4 else (None, "other workload"))

@@ -53,10 +53,15 @@ struct AcceptArgs {
 // Weight of entry x for the draw: the leftover max(0, p - q) after a
 // rejection at draft n < gamma (or p_n itself when the leftover is empty),
 // p_gamma when every draft was kept. Entries past the vocabulary weigh 0.
-__device__ inline float draw_weight(const float* prow, const float* qrow, bool leftover, int x,
-                                    int V) {
-  if (x >= V) return 0.f;
-  return leftover ? fmaxf(prow[x] - qrow[x], 0.f) : prow[x];
+// The loads are unconditional (the index clamped into the row) and the
+// kind of weight is a compile-time choice, so a thread's loads of several
+// entries are all in flight together.
+template <bool LEFTOVER>
+__device__ inline float draw_weight(const float* prow, const float* qrow, int x, int V) {
+  const int xc = x < V ? x : V - 1;
+  float w = prow[xc];
+  if (LEFTOVER) w = fmaxf(w - qrow[xc], 0.f);
+  return x < V ? w : 0.f;
 }
 
 __device__ inline double wave_sum_f64(double x) {
@@ -72,7 +77,8 @@ __device__ inline double wave_sum_f64(double x) {
 // sums in order, tile_start[k] = sum of tiles < k (non-decreasing: the
 // tiles' ranges [tile_start[k], tile_start[k+1]) cover [0, total) with no
 // gap or overlap).
-__device__ inline void tile_sums(const float* prow, const float* qrow, bool leftover, int V,
+template <bool LEFTOVER>
+__device__ inline void tile_sums(const float* prow, const float* qrow, int V,
                                  int n_tiles, double (*wave_part)[kWavesPerSeq],
                                  double* tile_start) {
   const int t = threadIdx.x;
@@ -82,7 +88,7 @@ __device__ inline void tile_sums(const float* prow, const float* qrow, bool left
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        wv[u][j] = draw_weight(prow, qrow, leftover, (k0 + u) * kTile + j * kThreads + t, V);
+        wv[u][j] = draw_weight<LEFTOVER>(prow, qrow, (k0 + u) * kTile + j * kThreads + t, V);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       double s = 0.0;
@@ -155,12 +161,12 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(AcceptArgs a) {
   const int n_tiles = (V + kTile - 1) / kTile;
 
   bool leftover = n < G;
-  tile_sums(prow, qrow, leftover, V, n_tiles, wave_part, tile_start);
-  if (leftover && !(tile_start[n_tiles] > 0.0)) {
+  if (leftover) {
+    tile_sums<true>(prow, qrow, V, n_tiles, wave_part, tile_start);
     // nothing is left (p = q up to rounding): draw from p_n instead
-    leftover = false;
-    tile_sums(prow, qrow, leftover, V, n_tiles, wave_part, tile_start);
+    if (!(tile_start[n_tiles] > 0.0)) leftover = false;
   }
+  if (!leftover) tile_sums<false>(prow, qrow, V, n_tiles, wave_part, tile_start);
   const double total = tile_start[n_tiles];
   const double target = (double)a.u[(int64_t)b * (G + 1) + G] * total;
 
@@ -194,8 +200,11 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(AcceptArgs a) {
   // range holds the target, or the target lies at or past the end, and that
   // thread walks its entries.
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    w_tile[j * kThreads + t] = draw_weight(prow, qrow, leftover, k * kTile + j * kThreads + t, V);
+  for (int j = 0; j < kPer; ++j) {
+    const int x = k * kTile + j * kThreads + t;
+    w_tile[j * kThreads + t] = leftover ? draw_weight<true>(prow, qrow, x, V)
+                                        : draw_weight<false>(prow, qrow, x, V);
+  }
   __syncthreads();
   double mine = 0.0;
 #pragma unroll
