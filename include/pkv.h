@@ -428,6 +428,47 @@ int pkv_seq_fork(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
 int pkv_seq_release(pkv_allocator* a, const int32_t* table, int32_t n_blocks);
 
 /* ------------------------------------------------------------------------
+ * Prefix cache ([SLS] "Reuse shared prefixes": requests that begin the
+ * same way share the KV cache of that start, kept in a tree so a new
+ * request picks it up instead of recomputing it; [SLS] "Caching and
+ * shortcuts": with paged attention this is block sharing; [DSS] "Paged
+ * attention").
+ *
+ * Host only, not thread-safe, over a caller's allocator (which must
+ * outlive the cache). A radix tree from token prefixes (int32 token ids) to
+ * the blocks holding their keys and values, at whole-block granularity:
+ * only full 16-token blocks are cached (their contents never change). The
+ * tree holds one reference to every block it caches.
+ *
+ * pkv_prefix_match: the longest cached prefix of tokens[0 .. n_tokens) of
+ *   whole blocks, at most max_blocks: writes its block ids to table[0 .. m)
+ *   and gives the caller one reference to each (release them with the
+ *   table, pkv_seq_release). Returns m (tokens matched: 16 m). A request
+ *   computes at least its last prompt token, so callers usually match
+ *   n_tokens - 1 tokens.
+ * pkv_prefix_insert: caches the first min(n_tokens / 16, n_blocks) blocks
+ *   of a sequence (table[i] holds tokens 16i .. 16i+15): prefixes already
+ *   cached keep their blocks; each newly cached block gets a reference
+ *   owned by the tree. Returns the number newly cached. Every table entry
+ *   used must be a live block (EINVAL otherwise).
+ * pkv_prefix_evict: frees up to n_blocks, one at a time, choosing the
+ *   block reached least recently (by match or insert) among the cached
+ *   blocks with no cached extension whose only reference is the tree's.
+ *   Returns the number freed (fewer if nothing else is evictable).
+ * Negative returns are PKV_E* codes. */
+typedef struct pkv_prefix_cache pkv_prefix_cache;
+
+int pkv_prefix_cache_create(pkv_allocator* alloc, pkv_prefix_cache** out);
+void pkv_prefix_cache_destroy(pkv_prefix_cache* pc); /* drops the tree's references */
+int32_t pkv_prefix_match(pkv_prefix_cache* pc, const int32_t* tokens,
+                         int32_t n_tokens, int32_t* table, int32_t max_blocks);
+int32_t pkv_prefix_insert(pkv_prefix_cache* pc, const int32_t* tokens,
+                          int32_t n_tokens, const int32_t* table,
+                          int32_t n_blocks);
+int32_t pkv_prefix_evict(pkv_prefix_cache* pc, int32_t n_blocks);
+int32_t pkv_prefix_cached_blocks(const pkv_prefix_cache* pc);
+
+/* ------------------------------------------------------------------------
  * Continuous batching ([DSS] "Continuous batching": before every token step
  * the scheduler releases the cache blocks of finished sequences, admits
  * waiting requests into the freed space and runs one decode step for what

@@ -61,6 +61,12 @@ SIGNATURES = {
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp]),
+    "pkv_prefix_cache_create": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+    "pkv_prefix_cache_destroy": (None, [_vp]),
+    "pkv_prefix_match": (_i32, [_vp, _i32p, _i32, _i32p, _i32]),
+    "pkv_prefix_insert": (_i32, [_vp, _i32p, _i32, _i32p, _i32]),
+    "pkv_prefix_evict": (_i32, [_vp, _i32]),
+    "pkv_prefix_cached_blocks": (_i32, [_vp]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
     "pkv_block_alloc": (ctypes.c_int, [_vp, _i32p]),
@@ -602,6 +608,51 @@ def _arr(ptr, n, dtype):
     if n == 0:
         return np.zeros(0, dtype)
     return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+
+class PrefixCache:
+    """Owner of a pkv_prefix_cache over an Allocator (kept alive here)."""
+
+    def __init__(self, alloc: Allocator):
+        h = ctypes.c_void_p()
+        _check(lib.pkv_prefix_cache_create(alloc._h, ctypes.byref(h)), "pkv_prefix_cache_create")
+        self._h = h
+        self.alloc = alloc
+
+    def close(self):
+        if self._h:
+            lib.pkv_prefix_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def match(self, tokens, max_blocks: int) -> np.ndarray:
+        """Block ids of the longest cached whole-block prefix (each with a
+        new reference for the caller)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        table = np.full(max(max_blocks, 1), -1, np.int32)
+        m = lib.pkv_prefix_match(self._h, _i32_host(t, "tokens"), len(t), _i32_host(table, "table"), max_blocks)
+        _check(min(m, 0), "pkv_prefix_match")
+        return table[:m].copy()
+
+    def insert(self, tokens, table) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        b = np.ascontiguousarray(table, dtype=np.int32)
+        r = lib.pkv_prefix_insert(self._h, _i32_host(t, "tokens"), len(t), _i32_host(b, "table"), len(b))
+        _check(min(r, 0), "pkv_prefix_insert")
+        return int(r)
+
+    def evict(self, n_blocks: int) -> int:
+        r = lib.pkv_prefix_evict(self._h, n_blocks)
+        _check(min(r, 0), "pkv_prefix_evict")
+        return int(r)
+
+    def cached_blocks(self) -> int:
+        return int(lib.pkv_prefix_cached_blocks(self._h))
 
 
 class Plan:
