@@ -40,6 +40,7 @@ import workload as w  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 VOCAB = 128256          # LLaMA-3 vocabulary: the acceptance rule's draw runs over it
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 BLOCK = 16
 # counter summaries: profiles/pmc_<kernel>_<workload>.txt, ending in a JSON record
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_{kernel}_{workload}.txt")
@@ -511,6 +512,102 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
             "query_tokens_per_s": B * q_len / (ms * 1e-3)}
 
 
+def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=True):
+    """Chunked prefill at a model shape: batch sequences each take a chunk
+    of `chunk` prompt tokens on top of 1,024..6,144 tokens already cached
+    (uniform), all layers. Per layer: pkv_kv_write of the chunk's keys and
+    values (batch * chunk tokens), then pkv_paged_prefill. Seeded N(0,1)
+    values drawn on the device, fragmented pool. Algorithmic flops of one
+    layer's prefill: for every (sequence, chunk token i, query head), 4 * d
+    per visible position (q.k and p.v, 2 flops per multiply-add), positions
+    0 .. ctx - chunk + i."""
+    L, n_q, n_kv, d = shape.n_layers, shape.n_q, shape.n_kv, shape.d
+    g = w.rng(seed, 20)
+    ctx = (g.integers(1024, 6145, batch) + chunk).astype(np.int32)
+    sh1 = w.Shape(shape.name, 1, n_q, n_kv, d, batch, 1, 1)
+    t = w.build_tables(sh1, seed, context_lens=ctx)
+    dev = torch.device("cuda")
+    ks, vs = w.pool_shapes(t.num_blocks, n_kv, d)
+    kp = [w.device_normal_bf16_(torch.empty(ks, dtype=torch.bfloat16, device=dev), seed * 100 + 2 * l)
+          for l in range(L)]
+    vp = [w.device_normal_bf16_(torch.empty(vs, dtype=torch.bfloat16, device=dev), seed * 100 + 2 * l + 1)
+          for l in range(L)]
+    q = w.device_normal_bf16_(torch.empty((L, batch, chunk, n_q, d), dtype=torch.bfloat16, device=dev), 31)
+    k_src = w.device_normal_bf16_(torch.empty((L, batch * chunk, n_kv, d), dtype=torch.bfloat16,
+                                              device=dev), 32)
+    v_src = w.device_normal_bf16_(torch.empty_like(k_src), 33)
+    out = torch.empty((L, batch, chunk, n_q, d), dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(t.block_tables).to(dev)
+    cl = torch.from_numpy(ctx).to(dev)
+    rows = torch.arange(batch, dtype=torch.int32, device=dev).repeat_interleave(chunk)
+    pos = (cl.repeat_interleave(chunk) - chunk +
+           torch.arange(chunk, dtype=torch.int32, device=dev).repeat(batch)).to(torch.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    max_ctx = int(ctx.max())
+
+    def write(l):
+        pkv.pkv_kv_write(kp[l], vp[l], k_src[l], v_src[l], bt, rows, pos, err_flag=err)
+
+    def prefill(l):
+        pkv.pkv_paged_prefill(out[l], q[l], kp[l], vp[l], bt, cl, shape.scale, max_ctx, err_flag=err)
+
+    for _ in range(warmup):
+        for l in range(L):
+            write(l)
+            prefill(l)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L * steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for l in range(L):
+            e = ev[i * L + l]
+            e[0].record()
+            write(l)
+            e[1].record()
+            prefill(l)
+            e[2].record()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    if int(err.item()):
+        raise RuntimeError(f"device error flag {int(err.item())}")
+    write_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    prefill_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    ms, mode = eager_ms, "eager"
+    if graph:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for l in range(L):
+                write(l)
+                prefill(l)
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        ms, mode = (time.perf_counter() - t0) * 1e3 / steps, "hip-graph"
+        if int(err.item()):
+            raise RuntimeError(f"device error flag {int(err.item())}")
+    seen = sum(int(c) - chunk + (chunk + 1) / 2 for c in ctx) * chunk   # visible positions, all rows of a head
+    flops_layer = 4.0 * d * n_q * seen
+    tflops = flops_layer / (prefill_us * 1e-6) / 1e12
+    return {
+        "metric": "chunked prefill against the paged cache: TFLOP/s of the attention",
+        "value": flops_layer * L / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill-{chunk}x{batch}-llama3-8b-gqa-32layer-ctx1024..6144",
+                   "layers": L, "batch": batch, "chunk_tokens": chunk, "n_q_heads": n_q,
+                   "n_kv_heads": n_kv, "head_dim": d, "cached_tokens": [1024, 6144], "seed": seed},
+        "step_mode": mode, "prompt_tokens_per_s": batch * chunk / (ms * 1e-3),
+        "kernels_us": {"kv_write": write_us, "paged_prefill": prefill_us},
+        "roofline": {"kernel": "paged_prefill", "bound": "mfma", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "alg_flops_per_launch": flops_layer},
+    }
+
+
 def prefix_cache_bench(pkv, seed, n_req=2000):
     """The prefix cache on the host, with a multi-turn chat workload at the
     LLaMA-3-8B context sizes. 64 conversations each share one of four
@@ -701,6 +798,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
     ap.add_argument("--verify-tokens", type=int, default=0,
                     help="speculative verification instead: this many query tokens per sequence")
+    ap.add_argument("--prefill-chunk", type=int, default=0,
+                    help="chunked prefill instead: chunk tokens per sequence on top of cached context")
+    ap.add_argument("--prefill-batch", type=int, default=8)
     ap.add_argument("--prefix-cache", action="store_true",
                     help="host benchmark of the prefix cache on a multi-turn chat workload")
     ap.add_argument("--loop", action="store_true",
@@ -730,6 +830,13 @@ def main():
     if args.loop:
         log(f"[bench] continuous batching, {WORKLOAD_NAMES[args.config]}")
         line = loop_bench(pkv, torch, shape, WORKLOAD_NAMES[args.config], args.seed, args.loop_steps, args.loop_warmup)
+        print(json.dumps(line), flush=True)
+        return
+    if args.prefill_chunk > 0:
+        log(f"[bench] chunked prefill, {args.prefill_chunk}-token chunks x {args.prefill_batch}")
+        line = prefill_bench(pkv, torch, shape, args.seed, args.prefill_chunk, args.prefill_batch,
+                             args.steps, args.warmup, graph=not args.no_graph)
+        copy_calibration(torch, args.copy_calibration_mib)
         print(json.dumps(line), flush=True)
         return
     extra = args.warmup + 2 * args.steps + 1   # one token per step: eager, graph warm-up, graph

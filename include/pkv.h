@@ -325,6 +325,35 @@ int pkv_paged_attn_verify(float* out, const void* q, const void* k_pool,
                           size_t workspace_bytes, int32_t* err_flag,
                           void* stream);
 
+/* ------------------------------------------------------------------------
+ * Chunked prefill against the paged cache ([SLS] "Split long prefills into
+ * chunks": a long prompt is taken a chunk per step beside the ongoing
+ * decodes; [DSS] "Scheduling: when prefill meets decode"; [M23] 23.2:
+ * prefill uses each weight for every prompt token, so it is bound by
+ * arithmetic).
+ *
+ * Each sequence's chunk is its last chunk_len cached tokens (the chunk's
+ * keys and values already written, pkv_kv_write); chunk token i, at position
+ * ctx - chunk_len + i, attends to positions 0 .. ctx - chunk_len + i: the
+ * earlier chunks and the prompt's cached prefix through the block table,
+ * and the chunk itself causally. The same computation as
+ * pkv_paged_attn_verify with q_len = chunk_len, organised for long chunks:
+ * one wavefront per (sequence, KV head, 32 query rows), scores and values
+ * on MFMA, no workspace.
+ *   q:   device bf16 [num_seqs][chunk_len][n_q_heads][head_dim]
+ *   out: device fp32 [num_seqs][chunk_len][n_q_heads][head_dim]
+ * chunk_len in [1, 16384]. Other arguments as for pkv_paged_attn_decode.
+ * Device errors: a context length outside [chunk_len, max_context_len] sets
+ * PKV_DEVERR_CONTEXT, a bad block id PKV_DEVERR_BLOCK_ID; that sequence's
+ * rows are NaN. */
+int pkv_paged_prefill(float* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs,
+                      int32_t chunk_len, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                      int32_t head_dim, float scale, int32_t max_context_len,
+                      int32_t* err_flag, void* stream);
+
 /* The acceptance rule of speculative decoding ([M23] 23.5 and Exercises;
  * [SLS] "Speculative decoding"): for each sequence the gamma drafted tokens
  * are checked in order, draft i kept with probability

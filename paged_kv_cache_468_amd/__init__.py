@@ -57,6 +57,8 @@ SIGNATURES = {
     "pkv_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _f32, _i32, _vp, _vp]),
     "pkv_spec_accept": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -365,6 +367,30 @@ def pkv_paged_attn_verify(out, q, k_pool, v_pool, block_tables, context_lens, sc
                                      int(max_context_len), ws, workspace.numel(), _flag(err_flag),
                                      _stream(stream)), "pkv_paged_attn_verify")
     return workspace
+
+
+def pkv_paged_prefill(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                      err_flag=None, stream=None):
+    """Chunked prefill: q bf16 [num_seqs, chunk_len, n_q, d] (the last
+    chunk_len cached tokens of each sequence, already written), out fp32 of
+    the same shape; chunk token i sees positions [0, ctx - chunk_len + i]."""
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(out, "out", torch.float32, 4)
+    B, C, n_q, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out: expected [num_seqs, chunk_len, n_q, head_dim], the same shape")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens: one row per sequence")
+    _check(lib.pkv_paged_prefill(_dev(out, "out", torch.float32), _dev(q, "q", torch.bfloat16),
+                                 _dev(k_pool, "k_pool", torch.bfloat16),
+                                 _dev(v_pool, "v_pool", torch.bfloat16), bt, cl, B, C,
+                                 block_tables.shape[1], nb, n_q, n_kv, d, float(scale),
+                                 int(max_context_len), _flag(err_flag), _stream(stream)),
+           "pkv_paged_prefill")
 
 
 def pkv_spec_accept(p_target, q_draft, draft_tokens, uniforms, n_accepted, next_token,
