@@ -338,8 +338,9 @@ int pkv_paged_attn_verify(float* out, const void* q, const void* k_pool,
  * earlier chunks and the prompt's cached prefix through the block table,
  * and the chunk itself causally. The same computation as
  * pkv_paged_attn_verify with q_len = chunk_len, organised for long chunks:
- * one wavefront per (sequence, KV head, 32 query rows), scores and values
- * on MFMA, no workspace.
+ * a workgroup of 8 wavefronts per (sequence, KV head, 256 query rows)
+ * stages 64-token K/V tiles in LDS for all its rows; scores and values on
+ * MFMA; no workspace.
  *   q:   device bf16 [num_seqs][chunk_len][n_q_heads][head_dim]
  *   out: device fp32 [num_seqs][chunk_len][n_q_heads][head_dim]
  * chunk_len in [1, 16384]. Other arguments as for pkv_paged_attn_decode.

@@ -85,12 +85,6 @@ constexpr int kMaxSplitWaves = 8192; // cap of the balanced split's wave count
 constexpr int kMinTilesPerWave = 16; // balanced split: at least this much work per wave
 constexpr int kMaxQueryTokens = 64;  // verification pass: query tokens per sequence
 constexpr int kMaxChunkTokens = 16384;  // chunked prefill: tokens per chunk
-// Chunked prefill: 16-row groups per wave, and waves per SIMD its registers
-// are held to. Measured on one LLaMA-3-8B layer (8 x 512-token chunks):
-// 2 groups at 2 waves 988 us, 4 at 1 wave 1234 us, 3 at 1 wave 1349 us,
-// 2 at 1 wave 1398 us, 1 at 2 waves 1953 us.
-constexpr int kPrefillGroups = 2;
-constexpr int kPrefillWavesPerEu = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
@@ -700,26 +694,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   balanced_body<D, NG, true>(a);
 }
 
-// Chunked prefill: q_len (the chunk) query tokens per sequence, causal,
-// NG groups of 16 rows per wave, one wave per unit (sequence, KV head, row
-// group) covering every tile its rows may see (tiles past its last row's
-// position are skipped): no split, no merge, the output written directly. Units are ordered (sequence, KV head, row
-// group), so a workgroup's four waves read the same K/V tiles.
-template <int D, int NG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerEu))) void paged_prefill_kernel(DecodeArgs a) {
+// Chunked prefill with the K/V tiles staged in LDS. A workgroup of
+// kPfWaves waves takes 32 * kPfWaves query rows of one (sequence, KV head)
+// (rows ordered (chunk token, head within the group), as everywhere); each
+// wave serves 32 of them as two 16-row MFMA groups. The workgroup walks the
+// cached context in tiles of kPfTile tokens (kPfTile / 16 blocks): all its
+// threads load the next tile's K and V from the pool into registers
+// (coalesced 16-byte loads) while the waves compute the current tile from
+// LDS, then store them into the other LDS buffer. Per tile and wave: for
+// each 16-token block, scores (K as A, q as B, as in the decode) for both
+// row groups; one running-max decision per tile; P split into bf16 hi + lo
+// for the P.V MFMAs (as in the decode). Causal: rows see positions up to
+// ctx - q_len + their token; tiles past the workgroup's last row are not
+// loaded; blocks of a tile past the limit of all rows are skipped.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kPfWaves = 8;                      // waves per workgroup
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRows = 32 * kPfWaves;           // query rows per workgroup
+constexpr int kPfTile = 64;                      // tokens per LDS tile
+constexpr int kPfSub = kPfTile / 16;             // blocks per tile
+constexpr int kPfKPad = 8;                       // bf16 of padding per K row in LDS
+constexpr int kPfVRow = 24;                      // bf16 per V dim row in LDS (16 tokens, padded)
+
+template <int D>
+struct PfSmem {
+  uint16_t k[2][kPfTile][D + kPfKPad];           // token-major, padded rows
+  uint16_t v[2][kPfSub][D][kPfVRow];             // per block, dim-major, padded rows
+};
+
+template <int D>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_prefill_lds_kernel(DecodeArgs a) {
+  constexpr int NG = 2;
+  constexpr int KM = D / 32;
   constexpr int VM = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int u = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
-  if (u >= a.n_units) return;
-  const int qg = u % a.n_qgroups;
-  const int sh = u / a.n_qgroups;
-  const int h = sh % a.n_kv;
-  const int s = sh / a.n_kv;
+  constexpr int KCH = D / 8;                     // 16-byte chunks per K row
+  constexpr int K_CHUNKS = kPfTile * KCH;        // per tile
+  constexpr int V_CHUNKS = kPfSub * D * 2;       // per tile (a dim row of a block: two chunks)
+  constexpr int K_PER = K_CHUNKS / kPfThreads;
+  constexpr int V_PER = V_CHUNKS / kPfThreads;
+  static_assert(K_PER * kPfThreads == K_CHUNKS && V_PER * kPfThreads == V_CHUNKS, "tile split");
+  __shared__ PfSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & 15;
+  const int r = lane >> 4;
+  const int n_rt = (a.qrows + kPfRows - 1) / kPfRows;   // row tiles per (sequence, KV head)
+  const int unit = logical_workgroup(a);
+  if (unit >= a.num_seqs * a.n_kv * n_rt) return;
+  const int rt = unit % n_rt;
+  const int h = (unit / n_rt) % a.n_kv;
+  const int s = unit / (n_rt * a.n_kv);
   const int ctx = a.context_lens[s];
+  const int qg = rt * kPfWaves + wave;              // this wave's 32-row group
   const Rows<NG> rw = rows_of<NG, true>(a, lane, s, h, qg, ctx);
+
   if (seq_tiles(ctx, a.q_len, a.max_ctx) == 0) {
-    if (h == 0 && qg == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
-    const int r = lane >> 4;
+    if (h == 0 && rt == 0 && tid == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -730,15 +764,207 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefillWav
     }
     return;
   }
-  // the last position any row of this unit may see
-  const int row_last = min((qg + 1) * 16 * NG, a.qrows) - 1;
+
+  // the positions the workgroup's rows may see: [0, visible)
+  const int row_last = min((rt + 1) * kPfRows, a.qrows) - 1;
   const int visible = ctx - a.q_len + row_last / a.group + 1;
-  const int tb = (visible + 15) >> 4;
+  const int n_blocks = (visible + 15) >> 4;          // blocks of the sequence to read
+  const int n_tiles = (n_blocks + kPfSub - 1) / kPfSub;
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  const int64_t tile_elems = 16 * D;
+  const int64_t head_off = (int64_t)h * tile_elems;
+  const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
+  const int last_block = (ctx - 1) >> 4;
+  const int last_valid = ctx - last_block * 16;
+  const int first_masked = ctx - a.q_len + 1;
+
+  // this wave's q rows, as the B operand of the score MFMA
+  bf16x8_t qv[NG][KM];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
+      qv[g][m] = rw.valid[g] ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // global -> registers for tile t. The tile's block ids are the same for
+  // the whole workgroup: loaded together first, checked, then every data
+  // load is issued with no wait in between. Blocks past n_blocks read a
+  // valid block and are zeroed (their positions lie past every valid row's
+  // limit, but 0 * NaN would not be 0).
+  bool bad = false;
+  u32x4_t kst[K_PER], vst[V_PER];
+  auto load_tile = [&](int t) {
+    int ids[kPfSub];
+#pragma unroll
+    for (int j = 0; j < kPfSub; ++j) {
+      const int b = t * kPfSub + j;
+      ids[j] = bt_row[b < n_blocks ? b : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < kPfSub; ++j) {
+      const bool in = t * kPfSub + j < n_blocks;
+      bad |= in && (ids[j] < 0 || ids[j] >= a.num_blocks);
+      ids[j] = (in && ids[j] >= 0 && ids[j] < a.num_blocks) ? ids[j] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < K_PER; ++i) {
+      const int ch = tid + i * kPfThreads;
+      const int tok = ch / KCH;                    // token within the tile
+      const int sb = tok / 16;
+      int blk = ids[0];
+#pragma unroll
+      for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
+      kst[i] = *(const u32x4_t*)(a.k_pool + blk * block_stride + head_off + (tok & 15) * D +
+                                 (ch % KCH) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int ch = tid + i * kPfThreads;
+      const int sb = ch / (2 * D);                 // block within the tile
+      int blk = ids[0];
+#pragma unroll
+      for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
+      vst[i] = *(const u32x4_t*)(a.v_pool + blk * block_stride + head_off + (ch % (2 * D)) * 8);
+    }
+  };
+  // registers -> LDS for tile t (the zeroing of blocks past n_blocks is
+  // done here, after the tile's compute, so the loads stay in flight)
+  auto store_tile = [&](int buf, int t) {
+#pragma unroll
+    for (int i = 0; i < K_PER; ++i) {
+      const int ch = tid + i * kPfThreads;
+      const bool in = t * kPfSub + (ch / KCH) / 16 < n_blocks;
+      *(u32x4_t*)&sm.k[buf][ch / KCH][(ch % KCH) * 8] = in ? kst[i] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int ch = tid + i * kPfThreads;
+      const int sb = ch / (2 * D);
+      const int within = ch % (2 * D);             // dim row (within / 2), half (within % 2)
+      const bool in = t * kPfSub + sb < n_blocks;
+      *(u32x4_t*)&sm.v[buf][sb][within >> 1][(within & 1) * 8] = in ? vst[i] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
   f32x4_t acc[NG][VM];
   float m_run[NG], l_run[NG];
-  const bool ok = process_segment<D, false, NG, true>(a, lane, s, h, rw, ctx, 0, tb, false, acc,
-                                                      m_run, l_run);
-  finish_rows<D, NG>(a, lane, ok, true, 0, rw, acc, m_run, l_run);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int m = 0; m < VM; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[g] = -__builtin_inff();
+    l_run[g] = 0.f;
+  }
+
+  load_tile(0);
+  store_tile(0, 0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    // Scores of all the tile's blocks, both row groups, with no branch
+    // between them. Blocks past those loaded hold zeros and lie past every
+    // valid row's limit; positions past a row's limit or the context are
+    // masked only in the tiles that reach them.
+    const bool edge = (t + 1) * kPfTile > first_masked;
+    float x[NG][kPfSub][4];
+#pragma unroll
+    for (int sb = 0; sb < kPfSub; ++sb) {
+      bf16x8_t kr[KM];
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * 16 + c][32 * m + 8 * r];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e] * a.scale_log2;
+      }
+    }
+    if (edge) {
+#pragma unroll
+      for (int sb = 0; sb < kPfSub; ++sb) {
+        const int p0 = (t * kPfSub + sb) * 16 + 4 * r;        // this lane's first position
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (p0 + e >= ctx || p0 + e > rw.lim[g]) x[g][sb][e] = -__builtin_inff();
+      }
+    }
+    // running max per row, one decision per tile; P = hi + lo in bf16
+    // (packed round-to-nearest conversions; hi + lo carries ~16 bits of P)
+    bf16x8_t pb[NG][kPfSub];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int sb = 0; sb < kPfSub; ++sb)
+        mx = fmaxf(mx, fmaxf(fmaxf(x[g][sb][0], x[g][sb][1]), fmaxf(x[g][sb][2], x[g][sb][3])));
+      mx = wave_max_across_rows(mx);
+      if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run[g], mx);
+        float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        if (m_new == -__builtin_inff()) alpha = 1.f;
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+      }
+      const float m_use = m_run[g] == -__builtin_inff() ? 0.f : m_run[g];
+#pragma unroll
+      for (int sb = 0; sb < kPfSub; ++sb) {
+        f32x2_t p01 = {__builtin_amdgcn_exp2f(x[g][sb][0] - m_use),
+                       __builtin_amdgcn_exp2f(x[g][sb][1] - m_use)};
+        f32x2_t p23 = {__builtin_amdgcn_exp2f(x[g][sb][2] - m_use),
+                       __builtin_amdgcn_exp2f(x[g][sb][3] - m_use)};
+        l_run[g] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+        const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+        const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+        const bf16x2_t l01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+        const bf16x2_t l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+        const u32x4_t pw = u32x4_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
+                                   __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+        pb[g][sb] = __builtin_bit_cast(bf16x8_t, pw);
+      }
+    }
+    // P.V per block; the slots of the sequence's last block past the
+    // context may hold anything (NaN included): their values are zeroed
+#pragma unroll
+    for (int sb = 0; sb < kPfSub; ++sb) {
+      const bool last = t * kPfSub + sb == last_block && last_valid < 16;
+      const int valid = last_valid - 4 * r;
+      const uint32_t keep0 = !last ? 0xFFFFFFFFu
+                                   : (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t keep1 = !last ? 0xFFFFFFFFu
+                                   : (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        u32x2_t wv = *(const u32x2_t*)&sm.v[buf][sb][16 * m + c][4 * r];
+        wv[0] &= keep0;
+        wv[1] &= keep1;
+        const bf16x4_t v4 = __builtin_bit_cast(bf16x4_t, wv);
+        const bf16x8_t vv = __builtin_shufflevector(v4, v4, 0, 1, 2, 3, 0, 1, 2, 3);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[g][sb], acc[g][m], 0, 0, 0);
+      }
+    }
+    if (t + 1 < n_tiles) {
+      // the other buffer was last read in the previous tile, before the
+      // barrier that ended it
+      store_tile(buf ^ 1, t + 1);
+      __syncthreads();
+    }
+  }
+  finish_rows<D, NG>(a, lane, !bad, true, 0, rw, acc, m_run, l_run);
 }
 
 // Merge kernel: one wave per (unit, query row). With reference maxima m_p,
@@ -868,9 +1094,9 @@ static Geom verify_geom(int num_seqs, int q_len, int n_q, int n_kv) {
   return Geom{num_seqs, n_q, n_kv, q_len, qrows > 16 ? 2 : 1, true};
 }
 
-// Chunked prefill: 16 * kPrefillGroups rows per wave, one wave per unit.
+// Chunked prefill: two 16-row groups per wave (32 rows).
 static Geom prefill_geom(int num_seqs, int chunk_len, int n_q, int n_kv) {
-  return Geom{num_seqs, n_q, n_kv, chunk_len, kPrefillGroups, true};
+  return Geom{num_seqs, n_q, n_kv, chunk_len, 2, true};
 }
 
 // Upper bound of the balanced split's wave count: at most kMaxSplitWaves,
@@ -1236,12 +1462,15 @@ extern "C" int pkv_paged_prefill(float* out, const void* q, const void* k_pool, 
                          num_blocks, head_dim, scale, max_context_len, 0, nullptr, 0, err_flag,
                          false);
   if (rc != PKV_OK || num_seqs == 0) return rc;
+  // one workgroup per (sequence, KV head, kPfRows rows)
+  const int64_t wgs = (int64_t)num_seqs * n_kv_heads * ((a.qrows + kPfRows - 1) / kPfRows);
+  a.wg_per_xcd = (int)((wgs + kXcds - 1) / kXcds);
   const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
   if (d == 128)
-    hipLaunchKernelGGL((paged_prefill_kernel<128, kPrefillGroups>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL(paged_prefill_lds_kernel<128>, dim3(grid), dim3(kPfThreads), 0,
                        (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((paged_prefill_kernel<64, kPrefillGroups>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL(paged_prefill_lds_kernel<64>, dim3(grid), dim3(kPfThreads), 0,
                        (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
