@@ -551,6 +551,7 @@ typedef struct {
   const int64_t* preempted_ids;
   int32_t num_free_blocks;       /* after this step's allocations (occupancy) */
   int32_t num_waiting;
+  int32_t n_cached_tokens;       /* prompt tokens admitted this step taken from the prefix cache */
 } pkv_step_plan;
 
 /* max_blocks_per_seq: the table width (longest request / 16, rounded up). */
@@ -568,6 +569,24 @@ int32_t pkv_batcher_prefix_table(const pkv_batcher* b, const int32_t** table);
 int pkv_batcher_submit(pkv_batcher* b, int64_t request_id, int32_t prompt_len,
                        int32_t gen_len, int32_t shares_prefix);
 int pkv_batcher_step(pkv_batcher* b, pkv_step_plan* plan);
+
+/* Prefix caching in the batcher ([SLS] "Reuse shared prefixes"): after
+ * pkv_batcher_enable_prefix_cache, requests submitted with their prompt's
+ * token ids (pkv_batcher_submit_tokens) are matched at admission against
+ * a prefix cache over the batcher's blocks (pkv_prefix_match on all but
+ * the last prompt token): the cached whole blocks are forked into the
+ * request's table and only the positions after them are in the plan's
+ * fill list. The prompt's full blocks join the cache at admission (this
+ * step's writes precede every read of them in each layer). Blocks only the
+ * cache holds are evicted (least recently used leaf first) before an
+ * admission is refused and before a resident request is preempted. A
+ * preempted request is matched again on its prompt tokens when it
+ * returns. pkv_batcher_cached_blocks: blocks the cache holds. */
+int pkv_batcher_enable_prefix_cache(pkv_batcher* b);
+int pkv_batcher_submit_tokens(pkv_batcher* b, int64_t request_id,
+                              const int32_t* tokens, int32_t prompt_len,
+                              int32_t gen_len);
+int32_t pkv_batcher_cached_blocks(const pkv_batcher* b);
 
 #ifdef __cplusplus
 }

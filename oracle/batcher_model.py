@@ -16,12 +16,17 @@ The policy details the pages leave open are the library's documented ones
 (include/pkv.h, pkv_batcher_step): growth of resident requests before
 admission, preemption of the most recently admitted request, first come
 first served admission with a reserve of one block per resident request.
+With a prefix cache ("Scaling LLM serving", "Reuse shared prefixes"): a
+request with token ids is matched at admission (all but its last prompt
+token), cached blocks are evicted before an admission is refused or a
+request preempted, and the prompt's full blocks are cached at admission.
 The model is compared with the library plan by plan (tests/test_batcher.py)
 and its invariants are checked separately.
 """
 from collections import deque
 
 from .allocator_model import AllocatorModel, OutOfBlocks
+from .prefix_cache_model import PrefixCacheModel
 
 BLOCK = 16
 
@@ -31,7 +36,7 @@ def _blocks(tokens):
 
 
 class _Req:
-    def __init__(self, rid, prompt_len, gen_len, shares):
+    def __init__(self, rid, prompt_len, gen_len, shares, tokens=None):
         self.id = rid
         self.prompt_len = prompt_len
         self.gen_len = gen_len
@@ -39,6 +44,7 @@ class _Req:
         self.shares = shares
         self.ctx = 0
         self.table = []
+        self.tokens = list(tokens) if tokens is not None else []
 
 
 class BatcherModel:
@@ -52,6 +58,14 @@ class BatcherModel:
             self.alloc.seq_grow(self.prefix_table, prefix_tokens, max_blocks)
         self.waiting = deque()
         self.running = []
+        self.cache = None
+
+    def enable_prefix_cache(self):
+        self.cache = PrefixCacheModel(self.alloc)
+
+    def submit_tokens(self, rid, tokens, gen_len):
+        self.submit(rid, len(tokens), gen_len, False)
+        self.waiting[-1].tokens = list(tokens)
 
     def submit(self, rid, prompt_len, gen_len, shares=False):
         if prompt_len < 1 or gen_len < 1:
@@ -94,6 +108,8 @@ class BatcherModel:
             try:
                 src, dst = self.alloc.seq_grow(r.table, r.ctx + 1, self.max_blocks)
             except OutOfBlocks:
+                if self.cache is not None and self.cache.evict(1) == 1:
+                    continue
                 self._preempt_last(preempted)
                 continue
             r.ctx += 1
@@ -102,14 +118,27 @@ class BatcherModel:
             i += 1
 
         prefix_full = self.prefix_tokens // BLOCK
+        cached_tokens = 0
         while self.waiting and len(self.running) < self.max_batch:
             w = self.waiting[0]
             ctx = w.prompt_len + 1
-            own = _blocks(ctx) - (prefix_full if w.shares else 0)
+            matched = []
+            if self.cache is not None and w.tokens:
+                known = min(len(w.tokens), w.prompt_len - 1)
+                matched = self.cache.match(w.tokens[:known], self.max_blocks)
+            own = _blocks(ctx) - (prefix_full if w.shares else 0) - len(matched)
+            short_by = own + len(self.running) - self.alloc.num_free()
+            if short_by > 0 and self.cache is not None:
+                self.cache.evict(short_by)
             if own + len(self.running) > self.alloc.num_free():
+                self.alloc.seq_release(list(matched))
                 break
             r = self.waiting.popleft()
             start = 0
+            if matched:
+                r.table = list(matched)
+                start = BLOCK * len(matched)
+                cached_tokens += start
             if r.shares:
                 self.alloc.seq_fork(self.prefix_table)
                 r.table = list(self.prefix_table)
@@ -124,6 +153,9 @@ class BatcherModel:
             r.ctx = ctx
             row = len(self.running)
             fill.extend((row, p) for p in range(start, r.prompt_len))
+            if self.cache is not None and r.tokens:
+                n = min(len(r.tokens), r.prompt_len)
+                self.cache.insert(r.tokens[:n], r.table)
             self.running.append(r)
 
         return {
@@ -136,4 +168,5 @@ class BatcherModel:
             "preempted": preempted,
             "num_free": self.alloc.num_free(),
             "num_waiting": len(self.waiting),
+            "cached_tokens": cached_tokens,
         }

@@ -63,6 +63,9 @@ SIGNATURES = {
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp]),
+    "pkv_batcher_enable_prefix_cache": (ctypes.c_int, [_vp]),
+    "pkv_batcher_submit_tokens": (ctypes.c_int, [_vp, _i64, _i32p, _i32, _i32]),
+    "pkv_batcher_cached_blocks": (_i32, [_vp]),
     "pkv_prefix_cache_create": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "pkv_prefix_cache_destroy": (None, [_vp]),
     "pkv_prefix_match": (_i32, [_vp, _i32p, _i32, _i32p, _i32]),
@@ -102,6 +105,7 @@ class StepPlan(ctypes.Structure):
         ("n_finished", ctypes.c_int32), ("finished_ids", ctypes.POINTER(ctypes.c_int64)),
         ("n_preempted", ctypes.c_int32), ("preempted_ids", ctypes.POINTER(ctypes.c_int64)),
         ("num_free_blocks", ctypes.c_int32), ("num_waiting", ctypes.c_int32),
+        ("n_cached_tokens", ctypes.c_int32),
     ]
 
 
@@ -698,6 +702,7 @@ class Plan:
         self.preempted_ids = _arr(c.preempted_ids, c.n_preempted, np.int64)
         self.num_free_blocks = c.num_free_blocks
         self.num_waiting = c.num_waiting
+        self.n_cached_tokens = c.n_cached_tokens
 
 
 class Batcher:
@@ -721,6 +726,17 @@ class Batcher:
             self.close()
         except Exception:
             pass
+
+    def enable_prefix_cache(self):
+        _check(lib.pkv_batcher_enable_prefix_cache(self._h), "pkv_batcher_enable_prefix_cache")
+
+    def submit_tokens(self, request_id: int, tokens, gen_len: int):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib.pkv_batcher_submit_tokens(self._h, int(request_id), _i32_host(t, "tokens"),
+                                             len(t), int(gen_len)), "pkv_batcher_submit_tokens")
+
+    def cached_blocks(self) -> int:
+        return int(lib.pkv_batcher_cached_blocks(self._h))
 
     def prefix_table(self):
         """(table int32 [max_blocks_per_seq], number of prefix blocks)."""

@@ -34,6 +34,7 @@
 // tokens of a preempted request).
 #include <stdint.h>
 
+#include <algorithm>
 #include <deque>
 #include <new>
 #include <vector>
@@ -51,6 +52,7 @@ struct Request {
   int32_t ctx;         // cached tokens including this step's one
   int32_t n_blocks;
   std::vector<int32_t> table;
+  std::vector<int32_t> tokens;   // the prompt's token ids, for the prefix cache (may be empty)
 };
 
 int32_t blocks_for(int32_t tokens) { return (tokens + PKV_BLOCK_TOKENS - 1) / PKV_BLOCK_TOKENS; }
@@ -63,6 +65,9 @@ struct pkv_batcher {
   std::vector<int32_t> prefix_table;
   std::deque<Request> waiting;
   std::vector<Request> running;   // admission order
+  pkv_prefix_cache* cache = nullptr;   // optional: prompts matched against cached blocks
+  std::vector<int32_t> match_table;
+  int32_t cached_tokens = 0;           // this step's prompt tokens served from the cache
   // plan buffers, valid until the next step
   std::vector<int32_t> tables, ctx, cow_src, cow_dst, fill_rows, fill_pos;
   std::vector<int64_t> ids, finished, preempted;
@@ -132,8 +137,24 @@ extern "C" int pkv_batcher_create(int32_t num_blocks, int32_t max_batch, int32_t
 
 extern "C" void pkv_batcher_destroy(pkv_batcher* b) {
   if (!b) return;
+  pkv_prefix_cache_destroy(b->cache);
   pkv_allocator_destroy(b->alloc);
   delete b;
+}
+
+extern "C" int pkv_batcher_enable_prefix_cache(pkv_batcher* b) {
+  if (!b || b->cache) return PKV_EINVAL;
+  try {
+    b->match_table.assign((size_t)b->max_blocks, -1);
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return pkv_prefix_cache_create(b->alloc, &b->cache);
+}
+
+extern "C" int32_t pkv_batcher_cached_blocks(const pkv_batcher* b) {
+  if (!b) return PKV_EINVAL;
+  return b->cache ? pkv_prefix_cached_blocks(b->cache) : 0;
 }
 
 extern "C" int32_t pkv_batcher_prefix_table(const pkv_batcher* b, const int32_t** table) {
@@ -162,6 +183,21 @@ extern "C" int pkv_batcher_submit(pkv_batcher* b, int64_t request_id, int32_t pr
     r.table.assign((size_t)b->max_blocks, -1);
     b->waiting.push_back(std::move(r));
   } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+extern "C" int pkv_batcher_submit_tokens(pkv_batcher* b, int64_t request_id,
+                                         const int32_t* tokens, int32_t prompt_len,
+                                         int32_t gen_len) {
+  if (!b || !tokens) return PKV_EINVAL;
+  const int rc = pkv_batcher_submit(b, request_id, prompt_len, gen_len, 0);
+  if (rc != PKV_OK) return rc;
+  try {
+    b->waiting.back().tokens.assign(tokens, tokens + prompt_len);
+  } catch (...) {
+    b->waiting.pop_back();
     return PKV_ENOMEM;
   }
   return PKV_OK;
@@ -204,20 +240,43 @@ extern "C" int pkv_batcher_step(pkv_batcher* b, pkv_step_plan* plan) {
         continue;
       }
       if (rc != PKV_ENOMEM) return rc;
-      // no free block: the newest resident request yields (possibly r itself)
+      // no free block: a block only the prefix cache holds goes first, then
+      // the newest resident request yields (possibly r itself)
+      if (b->cache && pkv_prefix_evict(b->cache, 1) == 1) continue;
       preempt_last(b);
     }
 
     // 3. admit first come first served
     const int32_t prefix_full = b->prefix_tokens / PKV_BLOCK_TOKENS;
+    b->cached_tokens = 0;
     while (!b->waiting.empty() && (int32_t)b->running.size() < b->max_batch) {
       Request& w = b->waiting.front();
       const int32_t ctx = w.prompt_len + 1;
-      const int32_t own = blocks_for(ctx) - (w.shares_prefix ? prefix_full : 0);
-      if (own + (int32_t)b->running.size() > pkv_num_free(b->alloc)) break;
+      // prompt blocks already cached (all but the last prompt token, which
+      // the request computes anyway)
+      int32_t matched = 0;
+      if (b->cache && !w.tokens.empty()) {
+        const int32_t known = std::min((int32_t)w.tokens.size(), w.prompt_len - 1);
+        matched = pkv_prefix_match(b->cache, w.tokens.data(), known, b->match_table.data(),
+                                   b->max_blocks);
+        if (matched < 0) return matched;
+      }
+      const int32_t own = blocks_for(ctx) - (w.shares_prefix ? prefix_full : 0) - matched;
+      const int32_t short_by = own + (int32_t)b->running.size() - pkv_num_free(b->alloc);
+      if (short_by > 0 && b->cache) pkv_prefix_evict(b->cache, short_by);
+      if (own + (int32_t)b->running.size() > pkv_num_free(b->alloc)) {
+        pkv_seq_release(b->alloc, b->match_table.data(), matched);
+        break;
+      }
       Request r = std::move(w);
       b->waiting.pop_front();
       int32_t start = 0;
+      if (matched > 0) {
+        for (int32_t k = 0; k < matched; ++k) r.table[k] = b->match_table[k];
+        r.n_blocks = matched;
+        start = matched * PKV_BLOCK_TOKENS;
+        b->cached_tokens += start;
+      }
       if (r.shares_prefix) {
         pkv_seq_fork(b->alloc, b->prefix_table.data(), b->prefix_blocks);
         for (int32_t k = 0; k < b->prefix_blocks; ++k) r.table[k] = b->prefix_table[k];
@@ -243,6 +302,14 @@ extern "C" int pkv_batcher_step(pkv_batcher* b, pkv_step_plan* plan) {
       for (int32_t p = start; p < r.prompt_len; ++p) {
         b->fill_rows.push_back(row);
         b->fill_pos.push_back(p);
+      }
+      // the prompt's full blocks join the cache now: in every layer this
+      // step's writes come before any request's attention reads them
+      if (b->cache && !r.tokens.empty()) {
+        const int32_t n = std::min((int32_t)r.tokens.size(), r.prompt_len);
+        const int32_t irc = pkv_prefix_insert(b->cache, r.tokens.data(), n, r.table.data(),
+                                              r.n_blocks);
+        if (irc < 0) return irc;
       }
       b->running.push_back(std::move(r));
     }
@@ -278,5 +345,6 @@ extern "C" int pkv_batcher_step(pkv_batcher* b, pkv_step_plan* plan) {
   plan->preempted_ids = b->preempted.data();
   plan->num_free_blocks = pkv_num_free(b->alloc);
   plan->num_waiting = (int32_t)b->waiting.size();
+  plan->n_cached_tokens = b->cached_tokens;
   return PKV_OK;
 }

@@ -77,6 +77,38 @@ class History:
         return ks, vs
 
 
+
+class TokenHistory(History):
+    """Keys/values of requests given by token ids: those of position p are
+    drawn from a seed that is a function of (layer, tokens[0..p]) only, as a
+    model's are of the tokens it has seen. Two requests that start with the
+    same tokens have the same keys and values there, so a block that one
+    caches holds exactly what the other would write."""
+
+    def __init__(self, d, tokens):
+        self.d = d
+        self.tokens = tokens            # {request id: prompt + generated tokens}
+        self.cache = {}
+
+    def _own(self, l, rid):
+        key = (l, rid)
+        if key not in self.cache:
+            t = self.tokens[rid]
+            ks = np.empty((len(t), N_KV, self.d), np.uint16)
+            vs = np.empty_like(ks)
+            for p in range(len(t)):
+                g = np.random.default_rng([l] + [int(x) for x in t[:p + 1]])
+                ks[p] = w.normal_bf16(g, (N_KV, self.d))
+                vs[p] = w.normal_bf16(g, (N_KV, self.d))
+            self.cache[key] = (ks, vs)
+        return self.cache[key]
+
+    def kv(self, l, rid, positions):
+        k, v = self._own(l, rid)
+        pos = np.asarray(positions, dtype=np.int64)
+        return k[pos].copy(), v[pos].copy()
+
+
 def mirror_step(orc, k_pool, v_pool, plan, fill, kn, vn, d):
     """The plan carried out on host pools with the oracle's operations, in
     the documented order: copies, prompt writes, append."""

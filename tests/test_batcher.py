@@ -232,3 +232,132 @@ def test_plans_carried_out_by_the_oracle_hold_every_token():
     assert sorted(finished) == sorted(reqs)
     assert all(seen[rid] == reqs[rid][2] for rid in reqs)
     assert preempted > 0
+
+
+def _chat_requests(rnd, n, vocab=40, max_gen=40):
+    """Token prompts: system prompts, chats that extend an earlier request's
+    prompt and generated tokens, unrelated prompts. Generated tokens are a
+    fixed function of the request id (the scheduler never sees them)."""
+    systems = [[rnd.randrange(vocab) for _ in range(rnd.randint(16, 60))] for _ in range(3)]
+    history, reqs = [], []
+    for rid in range(n):
+        r = rnd.random()
+        if r < 0.4:
+            prompt = rnd.choice(systems) + [rnd.randrange(vocab) for _ in range(rnd.randint(1, 30))]
+        elif r < 0.75 and history:
+            prompt = rnd.choice(history) + [rnd.randrange(vocab) for _ in range(rnd.randint(1, 20))]
+        else:
+            prompt = [rnd.randrange(vocab) for _ in range(rnd.randint(1, 70))]
+        prompt = prompt[:300]
+        gen = rnd.randint(1, max_gen)
+        gen_tokens = [(rid * 7 + i * 3) % vocab for i in range(gen)]
+        history.append(prompt + gen_tokens)
+        reqs.append((rid, prompt, gen, gen_tokens))
+    return reqs
+
+
+def _check_cache_invariants(model, ref):
+    a = model.alloc
+    refs = {}
+    for table in ref["tables"] + [model.prefix_table]:
+        for b in table:
+            refs[b] = refs.get(b, 0) + 1
+    for blk, _ in model.cache.entries.values():
+        refs[blk] = refs.get(blk, 0) + 1
+    assert refs == {b: c for b, c in enumerate(a.refcount) if c}
+    for table, ctx in zip(ref["tables"], ref["ctx"]):
+        assert len(table) == -(-ctx // BLOCK)
+        assert a.refcount[table[(ctx - 1) // BLOCK]] == 1     # the appended slot is private
+    for row, pos in ref["fill"]:
+        assert a.refcount[ref["tables"][row][pos // BLOCK]] >= 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_cache_library_matches_model(seed):
+    """The batcher with a prefix cache (token requests, tight pool: cache
+    evictions and preemptions) against the model, plan by plan, the cached
+    token counts included; every block's references accounted for."""
+    rnd = random.Random(100 + seed)
+    nb, mb = 32, 32
+    lib = pkv.Batcher(nb, 6, mb, 0)
+    model = BatcherModel(nb, 6, mb, 0)
+    lib.enable_prefix_cache()
+    model.enable_prefix_cache()
+    reqs = _chat_requests(rnd, 60, max_gen=100)
+    pending = list(reqs)
+    cached, pre = 0, 0
+    for step in range(5000):
+        for _ in range(rnd.randint(0, 2)):
+            if pending:
+                rid, prompt, gen, _ = pending.pop(0)
+                lib.submit_tokens(rid, prompt, gen)
+                model.submit_tokens(rid, prompt, gen)
+        plan = lib.step()
+        ref = model.step()
+        _same_plan(plan, ref)
+        assert plan.n_cached_tokens == ref["cached_tokens"]
+        assert lib.cached_blocks() == model.cache.cached_blocks()
+        _check_cache_invariants(model, ref)
+        cached += ref["cached_tokens"]
+        pre += len(ref["preempted"])
+        if not pending and not ref["ids"] and not ref["num_waiting"]:
+            break
+    assert cached > 200 and pre > 0, (cached, pre)
+
+
+def test_prefix_cache_plans_hold_every_token():
+    """The plans of a prefix-caching batcher, carried out on host pools with
+    the oracle's copy, write and append: keys and values of position p are
+    a function of the request's tokens up to p, and every resident
+    request's whole history, read through its table, is its own at every
+    step; cached blocks hold exactly the prefix they were cached under."""
+    import workload as w
+    from oracle import Oracle
+    orc = Oracle()
+    rnd = random.Random(7)
+    n_kv, d, nb, mb = 1, 64, 64, 32
+    reqs = {rid: (prompt, gen, gtoks) for rid, prompt, gen, gtoks in _chat_requests(rnd, 50)}
+    lib = pkv.Batcher(nb, 6, mb, 0)
+    lib.enable_prefix_cache()
+    sk, sv = w.pool_shapes(nb, n_kv, d)
+    k_pool = np.full(sk, w.BF16_NAN, np.uint16)
+    v_pool = np.full(sv, w.BF16_NAN, np.uint16)
+    memo = {}
+
+    def kv_of(tokens, p):
+        key = tuple(tokens[:p + 1])
+        if key not in memo:
+            g = np.random.default_rng(hash(key) & 0x7fffffff)
+            memo[key] = (w.normal_bf16(g, (n_kv, d)), w.normal_bf16(g, (n_kv, d)))
+        return memo[key]
+
+    pending = sorted(reqs)
+    cached = 0
+    for step in range(3000):
+        if pending and rnd.random() < 0.6:
+            rid = pending.pop(0)
+            lib.submit_tokens(rid, reqs[rid][0], reqs[rid][1])
+        p = lib.step()
+        ids = [int(x) for x in p.request_ids]
+        cached += p.n_cached_tokens
+        if not pending and p.num_seqs == 0 and p.num_waiting == 0:
+            break
+        full = {rid: reqs[rid][0] + reqs[rid][2] for rid in ids}
+        if len(p.cow_src):
+            assert orc.copy_blocks(k_pool, v_pool, p.cow_src, p.cow_dst, n_kv, d) == 0
+        if len(p.fill_rows):
+            ks = np.stack([kv_of(full[ids[r]], q)[0] for r, q in zip(p.fill_rows, p.fill_positions)])
+            vs = np.stack([kv_of(full[ids[r]], q)[1] for r, q in zip(p.fill_rows, p.fill_positions)])
+            assert orc.kv_write(k_pool, v_pool, ks, vs, p.block_tables, p.fill_rows,
+                                p.fill_positions) == 0
+        if p.num_seqs:
+            kn = np.stack([kv_of(full[rid], int(c) - 1)[0] for rid, c in zip(ids, p.context_lens)])
+            vn = np.stack([kv_of(full[rid], int(c) - 1)[1] for rid, c in zip(ids, p.context_lens)])
+            assert orc.kv_append(k_pool, v_pool, kn, vn, p.block_tables, p.context_lens) == 0
+        for row, rid in enumerate(ids):
+            for q in range(int(p.context_lens[row])):
+                blk = p.block_tables[row, q // BLOCK]
+                want_k, want_v = kv_of(full[rid], q)
+                assert np.array_equal(k_pool[blk, :, q % BLOCK, :], want_k), (step, rid, q)
+                assert np.array_equal(v_pool[blk, :, :, q % BLOCK], want_v), (step, rid, q)
+    assert cached > 100
