@@ -792,6 +792,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, choices=sorted(w.CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--shard", type=int, default=1,
+                    help="time one GPU's share of the shape split by KV head over this many GPUs")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-share", action="store_true", help="main run with private prefix copies")
     ap.add_argument("--skip-no-share", action="store_true", help="skip the second, unshared run")
@@ -829,10 +831,12 @@ def main():
         sys.exit(1)
     import paged_kv_cache_468_amd as pkv
     torch.cuda.set_device(0)
-    shape = w.CONFIGS[args.config]
+    shape = w.tp_shard(w.CONFIGS[args.config], args.shard)
+    wname = WORKLOAD_NAMES[args.config] + (f"-shard1of{args.shard}-by-kv-head" if args.shard > 1 else "")
+    stored = args.config == 4 and args.shard == 1     # the workload the counter records cover
     if args.loop:
-        log(f"[bench] continuous batching, {WORKLOAD_NAMES[args.config]}")
-        line = loop_bench(pkv, torch, shape, WORKLOAD_NAMES[args.config], args.seed, args.loop_steps, args.loop_warmup)
+        log(f"[bench] continuous batching, {wname}")
+        line = loop_bench(pkv, torch, shape, wname, args.seed, args.loop_steps, args.loop_warmup)
         print(json.dumps(line), flush=True)
         return
     if args.prefill_chunk > 0:
@@ -844,7 +848,7 @@ def main():
         return
     extra = args.warmup + 2 * args.steps + 1   # one token per step: eager, graph warm-up, graph
     if args.verify_tokens > 0:
-        log(f"[bench] verification pass, {args.verify_tokens} query tokens, {WORKLOAD_NAMES[args.config]}")
+        log(f"[bench] verification pass, {args.verify_tokens} query tokens, {wname}")
         share_v = shape.prefix_tokens > 0 and not args.no_share
         S = build_state(pkv, torch, shape, args.seed, share_v, extra, 0)
         dec = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
@@ -855,13 +859,13 @@ def main():
             f"verify {vr['verify_us']:.1f} us per layer")
         vtraffic, vwhy = (stored_traffic(f"llama3-8b-verify{args.verify_tokens}", "paged_attn_verify",
                                          "paged_attn_verify")
-                          if args.config == 4 and share_v else (None, "other workload"))
+                          if stored and share_v else (None, "other workload"))
         line = {
             "metric": "speculative verification pass: KV GB/s and time vs one decode step",
             "value": vr["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": vr["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "verify-" + WORKLOAD_NAMES[args.config],
+            "config": {"workload": "verify-" + wname,
                        "query_tokens": args.verify_tokens, "layers": shape.n_layers,
                        "batch": S_batch(shape), "n_q_heads": shape.n_q, "n_kv_heads": shape.n_kv,
                        "head_dim": shape.d, "shared_prefix_tokens": shape.prefix_tokens if share_v else 0},
@@ -885,7 +889,7 @@ def main():
         return
 
     share_main = (not args.no_share) and shape.prefix_tokens > 0
-    log(f"[bench] building {WORKLOAD_NAMES[args.config]} share={share_main}")
+    log(f"[bench] building {wname} share={share_main}")
     S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens,
                     fused=not args.unfused)
     log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
@@ -911,7 +915,7 @@ def main():
         log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step ({r2['step_mode']}), "
             f"{r2['kv_gbs']:.0f} GB/s; {r2['dominant']} {r2['dominant_us']:.1f} us = "
             f"{r2['dominant_gbs']:.0f} GB/s; kernels {r2['kernels_us']}")
-        t2, why2 = stored_traffic("llama3-8b-no-share", r2["dominant"]) if args.config == 4 else (None, "other workload")
+        t2, why2 = stored_traffic("llama3-8b-no-share", r2["dominant"]) if stored else (None, "other workload")
         extra_runs["no_share"] = {
             "value": r2["kv_gbs"], "unit": "GB/s", "ms_per_step": r2["ms_per_step"],
             "step_mode": r2["step_mode"], "eager_ms_per_step": r2["eager_ms_per_step"],
@@ -929,7 +933,7 @@ def main():
     copy_calibration(torch, args.copy_calibration_mib)
 
     traffic, why = (stored_traffic("llama3-8b-shared" if share_main else "llama3-8b-no-share",
-                                   main_r["dominant"]) if args.config == 4 else (None, "other workload"))
+                                   main_r["dominant"]) if stored else (None, "other workload"))
     line = {
         "metric": "paged decode-attention KV GB/s (% of HBM peak) + steps/s, Llama-3-8B shape",
         "value": main_r["kv_gbs"],
@@ -944,7 +948,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.config],
+            "workload": wname,
             "layers": shape.n_layers, "batch": S_batch(shape), "n_q_heads": shape.n_q,
             "n_kv_heads": shape.n_kv, "head_dim": shape.d, "block_tokens": BLOCK,
             "context": ([int(c) for c in shape.fixed_ctx] if shape.fixed_ctx else [shape.ctx_lo, shape.ctx_hi]),

@@ -157,7 +157,11 @@ int pkv_kv_append(void* k_pool, void* v_pool, const void* k_new,
  * k_src, v_src : device bf16 [n_tokens][n_kv_heads][head_dim].
  * seq_rows, positions : device int32 [n_tokens].
  * block_tables : device int32 [num_seqs][max_blocks_per_seq].
- * The blocks written must not be shared with another sequence. Device
+ * The blocks written must not be shared with another sequence. Two tokens
+ * for the same (row, position) leave one of them, unspecified which. The
+ * pools and k_src / v_src must be 16-byte aligned (PKV_EINVAL otherwise;
+ * every torch allocation is). Fastest when runs of 16 consecutive tokens
+ * are consecutive positions of one sequence, as a prompt is. Device
  * errors: a row outside [0, num_seqs) or a position outside
  * [0, 16*max_blocks_per_seq) -> PKV_DEVERR_CONTEXT; a table entry outside
  * [0, num_blocks) -> PKV_DEVERR_BLOCK_ID; that token is skipped. */

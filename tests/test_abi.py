@@ -95,6 +95,17 @@ def test_host_side_argument_checks():
     assert pkv.lib.pkv_kv_append(None, None, None, None, None, None, 4, 16, 64, 2, 80, None, None) == pkv.PKV_EUNSUPPORTED
     assert pkv.lib.pkv_copy_blocks(None, None, None, None, 0, 64, 2, 128, None, None) == pkv.PKV_OK
     assert pkv.lib.pkv_copy_blocks(None, None, None, None, 3, 64, 2, 128, None, None) == pkv.PKV_EINVAL
+    # kv_write: checks before any launch (fake device addresses are never touched)
+    A, idx = 0x10000, ctypes.c_void_p(0x20000)
+    kvw = lambda kp, ks, d=128, n=8: pkv.lib.pkv_kv_write(
+        ctypes.c_void_p(kp), ctypes.c_void_p(A), ctypes.c_void_p(ks), ctypes.c_void_p(A),
+        idx, idx, idx, n, 2, 16, 64, 2, d, None, None)
+    assert kvw(A, A, n=0) == pkv.PKV_OK                            # nothing to write
+    assert kvw(A, A, d=96) == pkv.PKV_EUNSUPPORTED
+    assert kvw(A + 2, A) == pkv.PKV_EINVAL                         # pools 16-byte aligned
+    assert kvw(A, A + 8) == pkv.PKV_EINVAL                         # sources 16-byte aligned
+    assert pkv.lib.pkv_kv_write(None, None, None, None, None, None, None, 8, 2, 16, 64, 2, 128,
+                                None, None) == pkv.PKV_EINVAL
 
 
 def test_split_waves_argument_checks():

@@ -2,7 +2,8 @@
 
 One layer of each shape is built at its real size (batch, heads, head
 size, context distribution, shared prefix), pools drawn on the GPU with a
-seeded generator and copied back for the oracle. The library runs the
+seeded generator and copied back for the oracle; the 80-layer shape also as
+one GPU's quarter of it split by KV head (16 q / 2 KV heads). The library runs the
 benchmark's calls in their launch configuration: pkv_decode_step as its two
 halves (pkv_decode_step_partition, the append inside the attention's
 partition kernel, then pkv_paged_attn_merge), the balanced
@@ -42,11 +43,12 @@ def _one_layer(shape):
                    shape.ctx_hi, prefix_tokens=shape.prefix_tokens)
 
 
-@pytest.mark.parametrize("cfg,fused", [(2, True), (3, True), (4, True), (5, True), (4, False)])
-def test_full_size_layer(pkv, orc, cfg, fused):
+@pytest.mark.parametrize("cfg,fused,shard", [(2, True, 1), (3, True, 1), (4, True, 1), (5, True, 1),
+                                             (4, False, 1), (5, True, 4)])
+def test_full_size_layer(pkv, orc, cfg, fused, shard):
     import torch
-    shape = _one_layer(w.CONFIGS[cfg])
-    seed = 40 + cfg
+    shape = _one_layer(w.tp_shard(w.CONFIGS[cfg], shard))
+    seed = 40 + cfg + 10 * (shard > 1)
     cl0 = w.context_lengths(shape, seed)
     max_ctx = int(cl0.max()) + BENCH_EXTRA_STEPS      # tables sized for the bench's growth
     t = w.build_tables(shape, seed, share=True, max_blocks=math.ceil(max_ctx / w.BLOCK))

@@ -68,6 +68,39 @@ def test_kv_write_bit_exact(pkv, orc, d, n_kv, n_tok):
     assert np.array_equal(to_host_u16(dk), hk)
     assert np.array_equal(to_host_u16(dv), hv)
 
+@pytest.mark.parametrize("d,n_kv", [(128, 8), (64, 4)])
+def test_kv_write_prompt_order_bit_exact(pkv, orc, d, n_kv):
+    """Prompts written in order, as after a prefill: per sequence a run of
+    consecutive positions starting anywhere in a block (so runs of 16 input
+    tokens straddle blocks and sequences), lengths 1 .. 200, one invalid
+    table entry. Bit for bit against the oracle's write."""
+    import torch
+    num_blocks, max_blocks = 400, 20
+    g = w.rng(77 + d, 8)
+    starts = [0, 5, 16, 31, 7, 100, 3]
+    lens = [200, 1, 16, 45, 90, 17, 60]
+    num_seqs = len(starts)
+    tables = g.permutation(num_blocks)[:num_seqs * max_blocks].astype(np.int32)
+    tables = tables.reshape(num_seqs, max_blocks)
+    tables[5, (100 + 10) // 16] = num_blocks + 3          # one bad entry: those tokens skipped
+    rows = np.concatenate([np.full(n, r, np.int32) for r, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(s0, s0 + n, dtype=np.int32) for s0, n in zip(starts, lens)])
+    n_tok = len(rows)
+    ks = w.normal_bf16(g, (n_tok, n_kv, d))
+    vs = w.normal_bf16(g, (n_tok, n_kv, d))
+    sk, sv = w.pool_shapes(num_blocks, n_kv, d)
+    hk = np.full(sk, w.BF16_NAN, np.uint16)
+    hv = np.full(sv, w.BF16_NAN, np.uint16)
+    dk, dv = to_dev_bf16(hk), to_dev_bf16(hv)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_kv_write(dk, dv, to_dev_bf16(ks), to_dev_bf16(vs), torch.from_numpy(tables).cuda(),
+                     torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda(), err_flag=err)
+    torch.cuda.synchronize()
+    assert orc.kv_write(hk, hv, ks, vs, tables, rows, pos) == -1
+    assert int(err.item()) == pkv.PKV_DEVERR_BLOCK_ID
+    assert np.array_equal(to_host_u16(dk), hk)
+    assert np.array_equal(to_host_u16(dv), hv)
+
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_continuous_batching_matches_contiguous_recompute(pkv, orc, d):

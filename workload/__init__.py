@@ -36,7 +36,7 @@ Recipe (every draw is seeded):
     ctx_s <= 2048). With share=False every sequence gets private copies of
     the same bytes.
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 import math
 
 import numpy as np
@@ -85,6 +85,18 @@ CONFIGS = {
     5: Shape("80-layer GQA: 80 layers, 64q/8kv, d128, B60, ctx 8000",
              80, 64, 8, 128, 60, 8000, 8000),
 }
+
+
+def tp_shard(shape: Shape, tp: int) -> Shape:
+    """One GPU's share of a shape split by KV head over tp GPUs: n_kv / tp
+    KV heads and the n_q / tp query heads that read them, everything else
+    (layers, batch, contexts) unchanged."""
+    if tp < 1 or shape.n_kv % tp:
+        raise ValueError(f"{shape.n_kv} KV heads do not split over {tp} GPUs")
+    if tp == 1:
+        return shape
+    return replace(shape, name=f"{shape.name}; one of {tp} shards by KV head",
+                   n_q=shape.n_q // tp, n_kv=shape.n_kv // tp)
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
