@@ -979,6 +979,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
+  constexpr int PRE = 8;   // partials whose accumulators are loaded with their (m, l)
   const int lane = threadIdx.x & 63;
   const int row_id = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row_id >= a.n_units * a.rows) return;
@@ -995,7 +996,14 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   float* o = a.out + out_row * D + lane * PER;
   const float nan = __builtin_nanf("");
 
-  const int nt = seq_tiles(a.context_lens[s], a.q_len, a.max_ctx);
+  // The context length and (balanced split) the unit's partial range are
+  // independent loads, issued together. The range is only used once the
+  // context is known to be valid: for an invalid one the partition kernel
+  // wrote nothing for the unit.
+  const int ctx = a.context_lens[s];
+  int2 info = make_int2(0, 0);
+  if (a.part_tokens == 0) info = *(const int2*)(a.unit_info + 2 * u);
+  const int nt = seq_tiles(ctx, a.q_len, a.max_ctx);
   if (nt == 0) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = nan;
@@ -1009,16 +1017,30 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     n = (nt + tiles_per_part - 1) / tiles_per_part;
     first = (int64_t)u * a.p_max;
   } else {
-    first = a.unit_info[2 * u];
-    n = a.unit_info[2 * u + 1];
+    first = info.x;
+    n = info.y;
   }
   if (n <= 1) return;   // written directly by the partition kernel
 
+  // One round trip for the first partials: lane p's (m, l), and the
+  // accumulators of partials 0 .. PRE-1 (indices past n read partial n-1
+  // again and get weight 0).
   const float* ml = a.ws_ml + (first * a.rows + g_in_slot) * 2;
   const int64_t mls = (int64_t)a.rows * 2;
-  float mx = -__builtin_inff();
-  bool bad = false;
-  for (int p = lane; p < n; p += 64) {
+  const float* acc = a.ws_acc + (first * a.rows + g_in_slot) * D + lane * PER;
+  const int64_t accs = (int64_t)a.rows * D;
+  float v0[PRE][PER];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int kk = k < n ? k : n - 1;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v0[k][e] = acc[kk * accs + e];
+  }
+  f32x2_t mine = lane < n ? *(const f32x2_t*)(ml + lane * mls) : f32x2_t{-__builtin_inff(), 0.f};
+
+  float mx = mine[0];
+  bool bad = mine[0] != mine[0];
+  for (int p = lane + 64; p < n; p += 64) {
     const float mp = ml[p * mls];
     bad |= mp != mp;
     mx = fmaxf(mx, mp);
@@ -1030,35 +1052,28 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) o[e] = nan;
     return;
   }
-  float lsum = 0.f;
-  for (int p = lane; p < n; p += 64) lsum += ml[p * mls + 1] * __builtin_amdgcn_exp2f(ml[p * mls] - mx);
+  const float my_w = lane < n ? __builtin_amdgcn_exp2f(mine[0] - mx) : 0.f;
+  float lsum = mine[1] * my_w;
+  for (int p = lane + 64; p < n; p += 64) lsum += ml[p * mls + 1] * __builtin_amdgcn_exp2f(ml[p * mls] - mx);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
 
   float res[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) res[e] = 0.f;
-  const float* acc = a.ws_acc + (first * a.rows + g_in_slot) * D + lane * PER;
-  const int64_t accs = (int64_t)a.rows * D;
-  for (int p0 = 0; p0 < n; p0 += 64) {
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const float wg = __shfl(my_w, k);   // 0 past n
+#pragma unroll
+    for (int e = 0; e < PER; ++e) res[e] += wg * v0[k][e];
+  }
+  // partials past the first PRE (many waves on few units)
+  for (int p0 = PRE; p0 < n; p0 += 64) {
     const int np = min(64, n - p0);
-    const float my_w = lane < np ? __builtin_amdgcn_exp2f(ml[(p0 + lane) * mls] - mx) : 0.f;
-    int p = 0;
-    for (; p + 8 <= np; p += 8) {   // eight independent loads in flight
-      float v[8][PER];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) v[k][e] = acc[(p0 + p + k) * accs + e];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float wg = __shfl(my_w, p + k);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) res[e] += wg * v[k][e];
-      }
-    }
-    for (; p < np; ++p) {
-      const float wg = __shfl(my_w, p);
+    const int pl = p0 + lane;
+    const float w_l = lane < np ? __builtin_amdgcn_exp2f(ml[pl * mls] - mx) : 0.f;
+    for (int p = 0; p < np; ++p) {
+      const float wg = __shfl(w_l, p);
 #pragma unroll
       for (int e = 0; e < PER; ++e) res[e] += wg * acc[(p0 + p) * accs + e];
     }
