@@ -1153,10 +1153,13 @@ static int resident_waves(const Geom& g, int head_dim) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   const int blocks = kernel_blocks_per_cu(g, head_dim);
   if (blocks < 1 || cus < 1) return -1;
-  // the split uses one wave per SIMD (4 per compute unit) for head_dim 128
-  // and two for head_dim 64, whose tiles are half the bytes: enough loads in
-  // flight, few per-wave start-up costs, and every wave resident
-  const int want = head_dim == 128 ? 4 : 8;
+  // the decode's split uses one wave per SIMD (4 per compute unit) for
+  // head_dim 128 and two for head_dim 64, whose tiles are half the bytes:
+  // enough loads in flight, few per-wave start-up costs, and every wave
+  // resident. The verification pass does q_len times the decode's matrix
+  // and softmax work per tile: two waves per SIMD, so one computes while
+  // the other's loads are in flight.
+  const int want = (head_dim == 128 && !g.causal) ? 4 : 8;
   const int per_cu = blocks * kWaves < want ? blocks * kWaves : want;
   slot = cus * per_cu;
   return slot;
