@@ -416,6 +416,12 @@ def cpu_baseline(torch, S, budget_s):
     }, worst, done
 
 
+def measured_gbs(traffic, us):
+    """HBM bytes per launch from the counter records over the launch's
+    duration: the rate HBM actually delivered (None without a record)."""
+    return None if traffic is None or not us else traffic / (us * 1e-6) / 1e9
+
+
 def stored_traffic(workload, kernel, kernel_file="paged_attn_balanced"):
     """HBM bytes per launch of the roofline kernel (entry `kernel`) from the
     committed counter summary of this workload (profiles/pmc_*), if it was
@@ -637,6 +643,7 @@ def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=Tr
         "roofline": {"kernel": "paged_prefill", "bound": "mfma", "achieved": tflops,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                     "traffic_gbs": measured_gbs(traffic, prefill_us),
                      "traffic_note": why, "alg_flops_per_launch": flops_layer},
     }
 
@@ -908,6 +915,7 @@ def main():
             "roofline": {"kernel": "paged_attn_verify", "bound": "hbm", "achieved": vr["verify_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": vr["verify_gbs"] / HBM_PEAK_GBS, "traffic": vtraffic,
+                         "traffic_gbs": measured_gbs(vtraffic, vr["verify_us"]),
                          "traffic_note": vwhy, "alg_bytes_per_launch": vr["verify_alg_bytes"],
                          "note": "events around each pkv_paged_attn_verify call (verify and merge "
                                  "kernels); logical bytes with the shared prefix"},
@@ -956,6 +964,7 @@ def main():
                          "us_per_launch_events_in_step": r2["dominant_us_per_launch_events"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": r2["dominant_gbs"] / HBM_PEAK_GBS, "traffic": t2,
+                         "traffic_gbs": measured_gbs(t2, r2["dominant_us"]),
                          "traffic_note": why2, "alg_bytes_per_launch": r2["dominant_alg_bytes"]},
             "num_blocks_per_layer": r2["num_blocks_per_layer"],
         }
@@ -1004,6 +1013,7 @@ def main():
             "unit": "GB/s",
             "frac": main_r["dominant_gbs"] / HBM_PEAK_GBS,
             "traffic": traffic,
+            "traffic_gbs": measured_gbs(traffic, main_r["dominant_us"]),
             "traffic_note": why,
             "alg_bytes_per_launch": main_r["dominant_alg_bytes"],
             "duration_us": main_r["dominant_us"],
