@@ -113,3 +113,70 @@ def test_full_size_layer(pkv, orc, cfg, fused, shard):
         worst = max(worst, max_abs(got[s, j], want))
     print(f"config {cfg}: {len(rows)} sampled rows, max-abs {worst:.2e}")
     assert worst <= TOL
+
+
+def test_very_long_context(pkv, orc):
+    """One sequence of 131,072 tokens beside two short ones, at the
+    LLaMA-3-8B heads. Each of its units spans on the order of a hundred
+    waves of the balanced split, so the merge combines more than 64
+    partials per row. On the same pools: the decode step (append inside),
+    the verification pass (4 query tokens) and chunked prefill (32-token
+    chunks). Sampled rows of every call, each recomputed by the oracle over
+    the pools after the append, within 1e-3; the short sequences' rows
+    included."""
+    import torch
+    shape = w.CONFIGS[4]
+    ctx = np.array([131072, 37, 700], np.int32)
+    B, G, D = len(ctx), shape.n_q // shape.n_kv, shape.d
+    sh1 = w.Shape(shape.name, 1, shape.n_q, shape.n_kv, D, B, 1, 1)
+    t = w.build_tables(sh1, 61, context_lens=ctx)
+    ks, vs = w.pool_shapes(t.num_blocks, shape.n_kv, D)
+    kp = w.device_normal_bf16_(torch.empty(ks, dtype=torch.bfloat16, device="cuda"), 611)
+    vp = w.device_normal_bf16_(torch.empty(vs, dtype=torch.bfloat16, device="cuda"), 612)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    bt, cl = to_dev_i32(t.block_tables), to_dev_i32(ctx)
+    max_ctx = int(ctx.max())
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = w.rng(61, 3)
+    nan = float("nan")
+
+    q1 = w.normal_bf16(g, (B, shape.n_q, D))
+    kn, vn = w.normal_bf16(g, (B, shape.n_kv, D)), w.normal_bf16(g, (B, shape.n_kv, D))
+    out1 = torch.full((B, shape.n_q, D), nan, dtype=torch.float32, device="cuda")
+    pkv.pkv_decode_step(out1, dev(q1), dev(kn), dev(vn), kp, vp, bt, cl, shape.scale, max_ctx,
+                        err_flag=err)
+    QV, QP = 4, 32
+    qv = w.normal_bf16(g, (B, QV, shape.n_q, D))
+    outv = torch.full((B, QV, shape.n_q, D), nan, dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attn_verify(outv, dev(qv), kp, vp, bt, cl, shape.scale, max_ctx, err_flag=err)
+    qp = w.normal_bf16(g, (B, QP, shape.n_q, D))
+    outp = torch.full((B, QP, shape.n_q, D), nan, dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_prefill(outp, dev(qp), kp, vp, bt, cl, shape.scale, max_ctx, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    waves = pkv.pkv_decode_split_waves(B, shape.n_q, shape.n_kv, D, max_ctx)
+    print(f"balanced split over {waves} waves for {B * shape.n_kv} units", flush=True)
+
+    k_h, v_h = to_host_u16(kp), to_host_u16(vp)
+    got1, gotv, gotp = (x.cpu().numpy().astype(np.float64) for x in (out1, outv, outp))
+    assert np.isfinite(got1).all() and np.isfinite(gotv).all() and np.isfinite(gotp).all()
+    pick = w.rng(61, 9)
+    worst = {"decode": 0.0, "verify": 0.0, "prefill": 0.0}
+    for s in range(B):
+        for _ in range(6 if s == 0 else 3):
+            j = int(pick.integers(shape.n_q))
+            row = lambda qr, seen: orc.decode_row(qr, k_h, v_h, t.block_tables[s], seen,
+                                                  shape.n_kv, j // G, shape.scale)
+            want, rc = row(q1[s, j], int(ctx[s]))
+            assert rc == 0
+            worst["decode"] = max(worst["decode"], max_abs(got1[s, j], want))
+            i = int(pick.integers(QV))
+            want, rc = row(qv[s, i, j], int(ctx[s]) - QV + i + 1)
+            assert rc == 0
+            worst["verify"] = max(worst["verify"], max_abs(gotv[s, i, j], want))
+            i = int(pick.integers(QP))
+            want, rc = row(qp[s, i, j], int(ctx[s]) - QP + i + 1)
+            assert rc == 0
+            worst["prefill"] = max(worst["prefill"], max_abs(gotp[s, i, j], want))
+    print(f"131,072-token context: max-abs {worst}")
+    assert max(worst.values()) <= TOL
