@@ -173,6 +173,24 @@ def test_verify_workspace_formula():
     assert pkv.pkv_verify_workspace_bytes(4, 3, 9, 2, 64, 256) == 0
 
 
+def test_prefill_host_checks():
+    """pkv_paged_prefill rejects bad shapes before any launch (fake device
+    addresses are never touched)."""
+    import paged_kv_cache_468_amd as pkv
+    d = ctypes.c_void_p(0x1000)
+    f = pkv.lib.pkv_paged_prefill
+    #      out q  kp vp bt cl  B  chunk   mb  nb  nq nkv hd  scale maxctx err stream
+    assert f(d, d, d, d, d, d, 4, 0, 16, 64, 8, 2, 128, 0.1, 256, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 16385, 2048, 64, 8, 2, 128, 0.1, 32768, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 16, 16, 64, 8, 2, 96, 0.1, 256, None, None) == pkv.PKV_EUNSUPPORTED
+    assert f(d, d, d, d, d, d, 4, 16, 16, 64, 9, 2, 128, 0.1, 256, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 16, 16, 64, 8, 0, 128, 0.1, 256, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 16, 16, 64, 8, 2, 128, 0.1, 257, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 4, 16, 16, 64, 8, 2, 128, float("nan"), 256, None, None) == pkv.PKV_EINVAL
+    assert f(None, d, d, d, d, d, 4, 16, 16, 64, 8, 2, 128, 0.1, 256, None, None) == pkv.PKV_EINVAL
+    assert f(d, d, d, d, d, d, 0, 16, 16, 64, 8, 2, 128, 0.1, 256, None, None) == pkv.PKV_OK
+
+
 def test_verify_host_checks():
     import paged_kv_cache_468_amd as pkv
     d = ctypes.c_void_p(0x1000)

@@ -123,3 +123,41 @@ def test_llama3_shape_sampled(pkv, orc):
         e = max(e, float(np.abs(got[s, i, j] - want).max()))
     print(f"llama3 shape, 8 x 512-token chunks, {len(picks)} sampled rows: max-abs {e:.2e}")
     assert e <= TOL
+
+
+def test_largest_chunk_sampled(pkv, orc):
+    """The largest chunk, 16,384 tokens, on top of 300 cached ones, at the
+    LLaMA-3-8B heads (65,536 rows per KV head): sampled rows, the chunk's
+    first and last token included, recomputed one by one."""
+    import torch
+    shape = w.CONFIGS[4]
+    C = 16384
+    ctx = np.array([C + 300], np.int32)
+    sh1 = w.Shape(shape.name, 1, shape.n_q, shape.n_kv, shape.d, 1, 1, 1)
+    t = w.build_tables(sh1, 47, context_lens=ctx)
+    ks, vs = w.pool_shapes(t.num_blocks, shape.n_kv, shape.d)
+    kp = w.device_normal_bf16_(torch.empty(ks, dtype=torch.bfloat16, device="cuda"), 471)
+    vp = w.device_normal_bf16_(torch.empty(vs, dtype=torch.bfloat16, device="cuda"), 472)
+    g = w.rng(47, 16)
+    qv = w.normal_bf16(g, (1, C, shape.n_q, shape.d))
+    out = torch.full(qv.shape, float("nan"), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_prefill(out, to_dev_bf16(qv), kp, vp, to_dev_i32(t.block_tables),
+                          to_dev_i32(ctx), shape.scale, int(ctx.max()), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    k_h = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    v_h = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    G = shape.n_q // shape.n_kv
+    picks = [(0, 0), (C - 1, shape.n_q - 1)] + [(int(g.integers(C)), int(g.integers(shape.n_q)))
+                                                for _ in range(30)]
+    e = 0.0
+    for i, j in picks:
+        want, rc = orc.decode_row(qv[0, i, j], k_h, v_h, t.block_tables[0], int(ctx[0]) - C + i + 1,
+                                  shape.n_kv, j // G, shape.scale)
+        assert rc == 0
+        e = max(e, float(np.abs(got[0, i, j] - want).max()))
+    print(f"16,384-token chunk, {len(picks)} sampled rows: max-abs {e:.2e}")
+    assert e <= TOL

@@ -57,6 +57,7 @@ CASES = [  # n_q, n_kv, d, contexts, q_len   (rows per KV head = q_len * G)
     (64, 8, 128, [40, 8000], 4),                    # G = 8: 32 rows
     (8, 1, 64, [20, 21, 47, 48, 49], 20),           # MQA, 160 rows -> five groups
     (16, 1, 128, [64, 65, 300], 3),                 # G = 16: 48 rows -> two groups
+    (32, 8, 128, [64, 65, 1000], 64),               # the most query tokens: 256 rows
 ]
 
 
