@@ -699,9 +699,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // (rows ordered (chunk token, head within the group), as everywhere); each
 // wave serves 32 of them as two 16-row MFMA groups. The workgroup walks the
 // cached context in tiles of kPfTile tokens (kPfTile / 16 blocks): all its
-// threads load the next tile's K and V from the pool into registers
-// (coalesced 16-byte loads) while the waves compute the current tile from
-// LDS, then store them into the other LDS buffer. Per tile and wave: for
+// threads load the next tile's K and V from the pool into registers while
+// the waves compute the current tile from LDS, then store them into the
+// other LDS buffer. LDS holds the tiles in MFMA operand order: for each
+// (block, MFMA step) the 64 lanes' operands one after another, so every
+// wave's LDS read is lane-linear and free of bank conflicts, and the
+// threads that stage a slot write consecutive addresses too (the pool
+// reads that feed them: whole 64-byte runs of a K row, whole 512-byte runs
+// of a V block). Per tile and wave: for
 // each 16-token block, scores (K as A, q as B, as in the decode) for both
 // row groups; one running-max decision per tile; P split into bf16 hi + lo
 // for the P.V MFMAs (as in the decode). Causal: rows see positions up to
@@ -714,13 +719,13 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 32 * kPfWaves;           // query rows per workgroup
 constexpr int kPfTile = 64;                      // tokens per LDS tile
 constexpr int kPfSub = kPfTile / 16;             // blocks per tile
-constexpr int kPfKPad = 8;                       // bf16 of padding per K row in LDS
-constexpr int kPfVRow = 24;                      // bf16 per V dim row in LDS (16 tokens, padded)
 
 template <int D>
 struct PfSmem {
-  uint16_t k[2][kPfTile][D + kPfKPad];           // token-major, padded rows
-  uint16_t v[2][kPfSub][D][kPfVRow];             // per block, dim-major, padded rows
+  // MFMA operand order: slot (block, step) holds, for lane i, the 16 bytes
+  // of K (8 bytes of V) that lane i feeds to that MFMA, at i * 16 (i * 8)
+  uint16_t k[2][kPfSub * (D / 32)][64][8];
+  uint16_t v[2][kPfSub * (D / 16)][64][4];
 };
 
 template <int D>
@@ -729,9 +734,8 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   constexpr int NG = 2;
   constexpr int KM = D / 32;
   constexpr int VM = D / 16;
-  constexpr int KCH = D / 8;                     // 16-byte chunks per K row
-  constexpr int K_CHUNKS = kPfTile * KCH;        // per tile
-  constexpr int V_CHUNKS = kPfSub * D * 2;       // per tile (a dim row of a block: two chunks)
+  constexpr int K_CHUNKS = kPfSub * KM * 64;     // 16-byte operand slots per tile
+  constexpr int V_CHUNKS = kPfSub * VM * 64;     // 8-byte operand slots per tile
   constexpr int K_PER = K_CHUNKS / kPfThreads;
   constexpr int V_PER = V_CHUNKS / kPfThreads;
   static_assert(K_PER * kPfThreads == K_CHUNKS && V_PER * kPfThreads == V_CHUNKS, "tile split");
@@ -796,7 +800,8 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   // valid block and are zeroed (their positions lie past every valid row's
   // limit, but 0 * NaN would not be 0).
   bool bad = false;
-  u32x4_t kst[K_PER], vst[V_PER];
+  u32x4_t kst[K_PER];
+  u32x2_t vst[V_PER];
   auto load_tile = [&](int t) {
     int ids[kPfSub];
 #pragma unroll
@@ -812,23 +817,29 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
+      // slot (sb, m, lane'): token sb*16 + c, dims 32m + 8r .. +7
       const int ch = tid + i * kPfThreads;
-      const int tok = ch / KCH;                    // token within the tile
-      const int sb = tok / 16;
+      const int sb = ch / (KM * 64);
+      const int m = (ch / 64) % KM;
+      const int ln = ch % 64;
       int blk = ids[0];
 #pragma unroll
       for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
-      kst[i] = *(const u32x4_t*)(a.k_pool + blk * block_stride + head_off + (tok & 15) * D +
-                                 (ch % KCH) * 8);
+      kst[i] = *(const u32x4_t*)(a.k_pool + blk * block_stride + head_off + (ln & 15) * D +
+                                 32 * m + 8 * (ln >> 4));
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
+      // slot (sb, m, lane'): dim 16m + c, tokens 4r .. 4r+3
       const int ch = tid + i * kPfThreads;
-      const int sb = ch / (2 * D);                 // block within the tile
+      const int sb = ch / (VM * 64);
+      const int m = (ch / 64) % VM;
+      const int ln = ch % 64;
       int blk = ids[0];
 #pragma unroll
       for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
-      vst[i] = *(const u32x4_t*)(a.v_pool + blk * block_stride + head_off + (ch % (2 * D)) * 8);
+      vst[i] = *(const u32x2_t*)(a.v_pool + blk * block_stride + head_off + (16 * m + (ln & 15)) * 16 +
+                                 4 * (ln >> 4));
     }
   };
   // registers -> LDS for tile t (the zeroing of blocks past n_blocks is
@@ -837,16 +848,14 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const bool in = t * kPfSub + (ch / KCH) / 16 < n_blocks;
-      *(u32x4_t*)&sm.k[buf][ch / KCH][(ch % KCH) * 8] = in ? kst[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const bool in = t * kPfSub + ch / (KM * 64) < n_blocks;
+      *(u32x4_t*)&sm.k[buf][ch / 64][ch % 64][0] = in ? kst[i] : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const int sb = ch / (2 * D);
-      const int within = ch % (2 * D);             // dim row (within / 2), half (within % 2)
-      const bool in = t * kPfSub + sb < n_blocks;
-      *(u32x4_t*)&sm.v[buf][sb][within >> 1][(within & 1) * 8] = in ? vst[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const bool in = t * kPfSub + ch / (VM * 64) < n_blocks;
+      *(u32x2_t*)&sm.v[buf][ch / 64][ch % 64][0] = in ? vst[i] : u32x2_t{0u, 0u};
     }
   };
 
@@ -877,7 +886,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
       bf16x8_t kr[KM];
 #pragma unroll
       for (int m = 0; m < KM; ++m)
-        kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * 16 + c][32 * m + 8 * r];
+        kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * KM + m][lane][0];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -947,7 +956,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
                                    : (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int m = 0; m < VM; ++m) {
-        u32x2_t wv = *(const u32x2_t*)&sm.v[buf][sb][16 * m + c][4 * r];
+        u32x2_t wv = *(const u32x2_t*)&sm.v[buf][sb * VM + m][lane][0];
         wv[0] &= keep0;
         wv[1] &= keep1;
         const bf16x4_t v4 = __builtin_bit_cast(bf16x4_t, wv);
