@@ -706,7 +706,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // wave's LDS read is lane-linear and free of bank conflicts, and the
 // threads that stage a slot write consecutive addresses too (the pool
 // reads that feed them: whole 64-byte runs of a K row, whole 512-byte runs
-// of a V block). Per tile and wave: for
+// of a V block). A lane's V operands of two consecutive MFMA steps sit
+// together, one 16-byte read for both; the V slots of the sequence's last
+// block past the context are zeroed there, once per workgroup. Per tile and wave: for
 // each 16-token block, scores (K as A, q as B, as in the decode) for both
 // row groups; one running-max decision per tile; P split into bf16 hi + lo
 // for the P.V MFMAs (as in the decode). Causal: rows see positions up to
@@ -725,7 +727,7 @@ struct PfSmem {
   // MFMA operand order: slot (block, step) holds, for lane i, the 16 bytes
   // of K (8 bytes of V) that lane i feeds to that MFMA, at i * 16 (i * 8)
   uint16_t k[2][kPfSub * (D / 32)][64][8];
-  uint16_t v[2][kPfSub * (D / 16)][64][4];
+  uint16_t v[2][kPfSub * (D / 32)][64][8];   // two MFMA steps' V per lane
 };
 
 template <int D>
@@ -854,8 +856,17 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const bool in = t * kPfSub + ch / (VM * 64) < n_blocks;
-      *(u32x2_t*)&sm.v[buf][ch / 64][ch % 64][0] = in ? vst[i] : u32x2_t{0u, 0u};
+      const int sb = ch / (VM * 64);
+      const int m = (ch / 64) % VM;
+      const int ln = ch % 64;
+      const int b = t * kPfSub + sb;
+      u32x2_t val = b < n_blocks ? vst[i] : u32x2_t{0u, 0u};
+      if (b == last_block && last_valid < 16) {   // slots past the context: zero (0 * NaN)
+        const int first = 4 * (ln >> 4);
+        val[0] &= (first < last_valid ? 0xFFFFu : 0u) | (first + 1 < last_valid ? 0xFFFF0000u : 0u);
+        val[1] &= (first + 2 < last_valid ? 0xFFFFu : 0u) | (first + 3 < last_valid ? 0xFFFF0000u : 0u);
+      }
+      *(u32x2_t*)&sm.v[buf][sb * (VM / 2) + m / 2][ln][(m & 1) * 4] = val;
     }
   };
 
@@ -944,26 +955,19 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
         pb[g][sb] = __builtin_bit_cast(bf16x8_t, pw);
       }
     }
-    // P.V per block; the slots of the sequence's last block past the
-    // context may hold anything (NaN included): their values are zeroed
+    // P.V per block (the V slots past the context were zeroed when stored)
 #pragma unroll
     for (int sb = 0; sb < kPfSub; ++sb) {
-      const bool last = t * kPfSub + sb == last_block && last_valid < 16;
-      const int valid = last_valid - 4 * r;
-      const uint32_t keep0 = !last ? 0xFFFFFFFFu
-                                   : (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
-      const uint32_t keep1 = !last ? 0xFFFFFFFFu
-                                   : (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        u32x2_t wv = *(const u32x2_t*)&sm.v[buf][sb * VM + m][lane][0];
-        wv[0] &= keep0;
-        wv[1] &= keep1;
-        const bf16x4_t v4 = __builtin_bit_cast(bf16x4_t, wv);
-        const bf16x8_t vv = __builtin_shufflevector(v4, v4, 0, 1, 2, 3, 0, 1, 2, 3);
+      for (int m = 0; m < VM; m += 2) {
+        const bf16x8_t w = *(const bf16x8_t*)&sm.v[buf][sb * (VM / 2) + m / 2][lane][0];
+        const bf16x8_t v0 = __builtin_shufflevector(w, w, 0, 1, 2, 3, 0, 1, 2, 3);
+        const bf16x8_t v1 = __builtin_shufflevector(w, w, 4, 5, 6, 7, 4, 5, 6, 7);
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[g][sb], acc[g][m], 0, 0, 0);
+        for (int g = 0; g < NG; ++g) {
+          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[g][sb], acc[g][m], 0, 0, 0);
+          acc[g][m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb[g][sb], acc[g][m + 1], 0, 0, 0);
+        }
       }
     }
     if (t + 1 < n_tiles) {
