@@ -24,6 +24,7 @@ that sample against the GPU output.
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -59,9 +60,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(path=KERNEL_SOURCE):
+    """Hash of the kernel source's code: comments and whitespace removed, so
+    that a counter record stays valid across edits that change no code."""
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------

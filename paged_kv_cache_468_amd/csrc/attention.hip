@@ -1,6 +1,9 @@
-// Decode-phase attention over a paged KV cache, for gfx950 (MI355X), and
-// the verification pass of speculative decoding ("Module 23: Serving",
-// 23.5: the target model checks several drafted tokens in one pass).
+// Decode-phase attention over a paged KV cache, for gfx950 (MI355X), the
+// verification pass of speculative decoding ("Module 23: Serving", 23.5:
+// the target model checks several drafted tokens in one pass) and chunked
+// prefill ("Scaling LLM serving", "Split long prefills into chunks": a chunk
+// of query tokens per sequence over its cached context; its own kernel, near
+// the end of this file).
 //
 // What is computed (include/pkv.h has the layouts): for every sequence s and
 // query head j, the softmax-weighted sum of the values of every cached token
