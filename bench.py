@@ -715,7 +715,7 @@ def prefix_cache_bench(pkv, seed, n_req=2000):
     }
 
 
-def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
+def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False):
     """Continuous batching at a model shape: requests with prompts uniform in
     [prefix, ctx_hi - 256] tokens (all beginning with the shared prefix when
     the shape has one) and 32..256 generated tokens, queued ahead; the
@@ -724,7 +724,11 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
     written (pkv_kv_write). Every step is the whole loop: the batcher's
     plan, its upload, per layer copies + prompt writes + pkv_decode_step,
     and a synchronisation (a server samples from the outputs before the
-    next step). Keys, values and queries are seeded N(0,1) on the device."""
+    next step). Keys, values and queries are seeded N(0,1) on the device,
+    in the loop's own input buffers. With graphs, the decode launches of a
+    step are replayed from a HIP graph cached per row count (the loop's
+    copies and prompt writes stay eager); measured slower than issuing them
+    eagerly, whose launches the host already queues ahead of the GPU."""
     from paged_kv_cache_468_amd.loop import ServingLoop
     L, B, n_kv, d = shape.n_layers, shape.batch, shape.n_kv, shape.d
     max_blocks = -(-shape.ctx_hi // BLOCK)
@@ -749,12 +753,9 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
     src_v = torch.empty_like(src_k)
     w.device_normal_bf16_(src_k, seed * 1000 + 900)
     w.device_normal_bf16_(src_v, seed * 1000 + 901)
-    q = torch.empty((L, B, shape.n_q, d), dtype=torch.bfloat16, device="cuda")
-    kn = torch.empty((L, B, n_kv, d), dtype=torch.bfloat16, device="cuda")
-    vn = torch.empty_like(kn)
-    for i, t in enumerate((q, kn, vn)):
+    loop = ServingLoop(b, kp, vp, shape.n_q, shape.scale, B, graphs=graphs)
+    for i, t in enumerate(loop.inputs()):
         w.device_normal_bf16_(t, seed * 1000 + 950 + i)
-    loop = ServingLoop(b, kp, vp, shape.n_q, shape.scale, B)
     if prefix:
         loop.write_prefix([src_k[:prefix]] * L, [src_v[:prefix]] * L)
     stream = loop.stream
@@ -765,7 +766,7 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
         p = loop.schedule()
         acc["host_s"] += time.perf_counter() - t
         n, n_fill = p.num_seqs, len(p.fill_rows)
-        loop.run(lambda l: (src_k[:n_fill], src_v[:n_fill]), q[:, :n], kn[:, :n], vn[:, :n])
+        loop.run(lambda l: (src_k[:n_fill], src_v[:n_fill]), None, None, None)
         stream.synchronize()
         acc["tokens"] += n
         acc["kv_bytes"] += per_token * int(p.context_lens.astype(np.int64).sum())
@@ -812,6 +813,8 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup):
         "admitted_per_step": acc["admitted"] / steps,
         "finished_per_step": acc["finished"] / steps,
         "cow_per_step": acc["cow"] / steps,
+        "decode_launches": "hip-graph, cached per row count" if graphs else "eager",
+        "graph_captures": loop.graph_captures, "graph_replays_from_cache": loop.graph_hits,
     }
 
 
@@ -854,6 +857,8 @@ def main():
                     help="host benchmark of the prefix cache on a multi-turn chat workload")
     ap.add_argument("--loop", action="store_true",
                     help="continuous batching instead: the batcher's plans carried out step by step")
+    ap.add_argument("--loop-graphs", action="store_true",
+                    help="continuous batching with the decode launches replayed from cached graphs")
     ap.add_argument("--loop-steps", type=int, default=300)
     ap.add_argument("--loop-warmup", type=int, default=300)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -880,7 +885,8 @@ def main():
     stored = args.config == 4 and args.shard == 1     # the workload the counter records cover
     if args.loop:
         log(f"[bench] continuous batching, {wname}")
-        line = loop_bench(pkv, torch, shape, wname, args.seed, args.loop_steps, args.loop_warmup)
+        line = loop_bench(pkv, torch, shape, wname, args.seed, args.loop_steps, args.loop_warmup,
+                          graphs=args.loop_graphs)
         print(json.dumps(line), flush=True)
         return
     if args.prefill_chunk > 0:

@@ -20,7 +20,18 @@ caller's: in a model they come from the layers' projections.
 
 The staging buffers are reused every step: schedule() waits until the
 previous step's uploads have left them (an event, not a device-wide sync).
+
+With graphs=True the decode launches of all layers are replayed from a HIP
+graph captured for the step's row count and input addresses (a few kept,
+the least recently used dropped): once the batch is full and the caller
+writes the step's queries and new keys/values into the loop's own input
+buffers (inputs()), every step replays the same graph. The copies and
+prompt writes of a step run first, eagerly (their counts change from step
+to step); each touches only its layer's pools, so running them before the
+decodes keeps every layer's order.
 """
+from collections import OrderedDict
+
 import numpy as np
 
 from . import (Batcher, _torch, pkv_copy_blocks, pkv_decode_step, pkv_decode_workspace_bytes,
@@ -32,7 +43,7 @@ class ServingLoop:
     tables, one workspace sized for the largest batch and context."""
 
     def __init__(self, batcher: Batcher, k_pools, v_pools, n_q: int, scale: float,
-                 max_batch: int, stream=None):
+                 max_batch: int, stream=None, graphs: bool = False, max_graphs: int = 4):
         torch = _torch()
         self.b = batcher
         self.k_pools, self.v_pools = k_pools, v_pools
@@ -62,6 +73,23 @@ class ServingLoop:
         self.uploaded = torch.cuda.Event()
         self.uploaded.record(self.stream)
         self.plan = None
+        self.graphs = OrderedDict() if graphs else None
+        self.max_graphs = max_graphs
+        self.graph_hits = self.graph_captures = 0
+        self._inputs = None
+
+    def inputs(self):
+        """The loop's own input buffers (q [L][max_batch, n_q, d], k_new and
+        v_new [L][max_batch, n_kv, d], bf16): write a step's rows 0 .. n-1
+        into them and call run() with q = k_new = v_new = None."""
+        if self._inputs is None:
+            torch = _torch()
+            bf = torch.bfloat16
+            L, B = self.n_layers, self.max_batch
+            self._inputs = (torch.zeros((L, B, self.n_q, self.d), dtype=bf, device=self.dev),
+                            torch.zeros((L, B, self.n_kv, self.d), dtype=bf, device=self.dev),
+                            torch.zeros((L, B, self.n_kv, self.d), dtype=bf, device=self.dev))
+        return self._inputs
 
     def _size_cow(self, n):
         if self.cow_h is None or self.cow_h.shape[1] < n:
@@ -127,19 +155,50 @@ class ServingLoop:
         torch = _torch()
         p = self.plan
         n, n_cow, n_fill = p.num_seqs, len(p.cow_src), len(p.fill_rows)
+        if q is None:
+            qb, kb, vb = self.inputs()
+            q, k_new, v_new = qb[:, :n], kb[:, :n], vb[:, :n]
+        if self.graphs is None:
+            with torch.cuda.stream(self.stream):
+                for l in range(self.n_layers):
+                    self._writes(l, n, n_cow, n_fill, fill_kv)
+                    if n:
+                        self._decode(l, n, q, k_new, v_new, self.stream)
+            return self.out[:, :n]
         with torch.cuda.stream(self.stream):
             for l in range(self.n_layers):
-                if n_cow:
-                    pkv_copy_blocks(self.k_pools[l], self.v_pools[l], self.cow[0, :n_cow],
-                                    self.cow[1, :n_cow], err_flag=self.err, stream=self.stream)
-                if n_fill:
-                    k_src, v_src = fill_kv(l)
-                    pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src, v_src, self.bt[:n],
-                                 self.fill[0, :n_fill], self.fill[1, :n_fill], err_flag=self.err,
-                                 stream=self.stream)
-                if n:
-                    pkv_decode_step(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
-                                    self.v_pools[l], self.bt[:n], self.cl[:n], self.scale,
-                                    self.max_ctx, 0, workspace=self.ws, err_flag=self.err,
-                                    stream=self.stream)
+                self._writes(l, n, n_cow, n_fill, fill_kv)
+            if n:
+                key = (n,) + tuple(t.data_ptr() for x in (q, k_new, v_new)
+                                   for t in (x[l] for l in range(self.n_layers)))
+                g = self.graphs.pop(key, None)
+                if g is None:
+                    g = torch.cuda.CUDAGraph()
+                    # the calls name the current stream, which is the capture
+                    # stream inside the capture
+                    with torch.cuda.graph(g):
+                        for l in range(self.n_layers):
+                            self._decode(l, n, q, k_new, v_new, None)
+                    self.graph_captures += 1
+                    while len(self.graphs) >= self.max_graphs:
+                        self.graphs.popitem(last=False)
+                else:
+                    self.graph_hits += 1
+                self.graphs[key] = g
+                g.replay()
         return self.out[:, :n]
+
+    def _writes(self, l, n, n_cow, n_fill, fill_kv):
+        if n_cow:
+            pkv_copy_blocks(self.k_pools[l], self.v_pools[l], self.cow[0, :n_cow],
+                            self.cow[1, :n_cow], err_flag=self.err, stream=self.stream)
+        if n_fill:
+            k_src, v_src = fill_kv(l)
+            pkv_kv_write(self.k_pools[l], self.v_pools[l], k_src, v_src, self.bt[:n],
+                         self.fill[0, :n_fill], self.fill[1, :n_fill], err_flag=self.err,
+                         stream=self.stream)
+
+    def _decode(self, l, n, q, k_new, v_new, stream):
+        pkv_decode_step(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
+                        self.v_pools[l], self.bt[:n], self.cl[:n], self.scale, self.max_ctx, 0,
+                        workspace=self.ws, err_flag=self.err, stream=stream)

@@ -239,3 +239,68 @@ def test_continuous_batching_with_prefix_cache(pkv, orc, d):
     assert all(steps_seen[rid] == reqs[rid][1] for rid in reqs)
     assert cached > 1000 and preempted > 0, (cached, preempted)
     print(f"d={d}: {cached} prompt tokens from the cache, {preempted} preemptions")
+
+
+def test_graph_replay_matches_eager_loop(pkv):
+    """The serving loop with its decode launches replayed from cached HIP
+    graphs, against the same loop issuing them eagerly. Two batchers fed the
+    same requests make the same plans; each step's queries and new keys and
+    values go into each loop's own input buffers. Every step's outputs, and
+    the pools at the end, are bit for bit the same; graphs are captured once
+    per row count and replayed from the cache otherwise (admissions,
+    preemptions and finishes change the row count between replays)."""
+    import torch
+    from paged_kv_cache_468_amd.loop import ServingLoop
+    d, L = 128, lu.L
+    reqs = lu.requests(d)
+    hist = lu.History(d, {rid: r[3] for rid, r in reqs.items()})
+    sk, sv = w.pool_shapes(lu.NUM_BLOCKS, lu.N_KV, d)
+    loops = []
+    for graphs in (False, True):
+        b = pkv.Batcher(lu.NUM_BLOCKS, lu.MAX_BATCH, lu.MAX_BLOCKS, lu.PREFIX)
+        kp = [to_dev_bf16(np.full(sk, w.BF16_NAN, np.uint16)) for _ in range(L)]
+        vp = [to_dev_bf16(np.full(sv, w.BF16_NAN, np.uint16)) for _ in range(L)]
+        loop = ServingLoop(b, kp, vp, lu.N_Q, 1.0 / np.sqrt(d), lu.MAX_BATCH, graphs=graphs)
+        loop.write_prefix([to_dev_bf16(hist.pk[l]) for l in range(L)],
+                          [to_dev_bf16(hist.pv[l]) for l in range(L)])
+        loops.append((b, loop, kp, vp))
+    steps = 0
+    for step in range(2000):
+        plans = []
+        for b, loop, _, _ in loops:
+            for rid, (arr, prompt, gen, shares) in reqs.items():
+                if arr == step:
+                    b.submit(rid, prompt, gen, shares)
+            plans.append(loop.schedule())
+        p = plans[0]
+        assert p.request_ids.tolist() == plans[1].request_ids.tolist()
+        assert p.context_lens.tolist() == plans[1].context_lens.tolist()
+        n = p.num_seqs
+        if n == 0 and p.num_waiting == 0 and step > 30:
+            break
+        ids = [int(x) for x in p.request_ids]
+        fill = [hist.fill(l, ids, p) for l in range(L)]
+        new = [hist.new_token(l, ids, p) for l in range(L)]
+        g = w.rng(70000 + step, 7)
+        q_h = [w.normal_bf16(g, (n, lu.N_Q, d)) for _ in range(L)]
+        outs = []
+        for b, loop, _, _ in loops:
+            qb, kb, vb = loop.inputs()
+            for l in range(L):
+                if n:
+                    qb[l, :n].copy_(to_dev_bf16(q_h[l]))
+                    kb[l, :n].copy_(to_dev_bf16(new[l][0]))
+                    vb[l, :n].copy_(to_dev_bf16(new[l][1]))
+            out = loop.run(lambda l: (to_dev_bf16(fill[l][0]), to_dev_bf16(fill[l][1])),
+                           None, None, None)
+            torch.cuda.synchronize()
+            assert int(loop.err.item()) == 0, f"step {step}"
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1]), f"step {step}: graph replay differs"
+        steps += 1
+    for l in range(L):
+        assert np.array_equal(to_host_u16(loops[0][2][l]), to_host_u16(loops[1][2][l]))
+        assert np.array_equal(to_host_u16(loops[0][3][l]), to_host_u16(loops[1][3][l]))
+    gl = loops[1][1]
+    print(f"{steps} steps: {gl.graph_captures} captures, {gl.graph_hits} replays from the cache")
+    assert gl.graph_hits > gl.graph_captures > 0
