@@ -99,3 +99,39 @@ def test_verify_sweep(pkv, orc, seed):
     e = max_abs(got, want)
     print(f"  max-abs {e:.2e}")
     assert np.isfinite(got).all() and e <= TOL
+
+
+@pytest.mark.parametrize("seed", range(200, 210))
+def test_prefill_sweep(pkv, orc, seed):
+    """Chunked prefill over random shapes: chunks of 1 .. 160 tokens (so
+    256-row workgroups from nearly empty to several per KV head), 1 .. 4
+    sequences with 0 .. 1,000 cached tokens before the chunk."""
+    import torch
+    g = np.random.default_rng([9300, seed])
+    while True:
+        n_kv = int(g.choice([1, 2, 4, 8]))
+        G = int(g.choice([1, 2, 3, 4, 5, 8]))
+        if n_kv * G <= 32:
+            break
+    n_q, d = n_kv * G, int(g.choice([64, 128]))
+    C = int(g.integers(1, 161))
+    B = int(g.integers(1, 5))
+    ctx = [C + int(g.integers(0, 1001)) for _ in range(B)]
+    slack = int(g.choice([0, 16, 300]))
+    print(f"seed {seed}: {n_q}/{n_kv} heads, d {d}, chunk {C}, contexts {ctx}, slack {slack}",
+          flush=True)
+    hc, max_ctx = _host(n_q, n_kv, d, ctx, slack, seed)
+    qv = w.normal_bf16(g, (B, C, n_q, d))
+    out = torch.full(qv.shape, float("nan"), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_prefill(out, to_dev_bf16(qv), to_dev_bf16(hc.k_pool), to_dev_bf16(hc.v_pool),
+                          to_dev_i32(hc.tables.block_tables), to_dev_i32(hc.tables.context_lens),
+                          hc.shape.scale, max_ctx, err_flag=err)
+    torch.cuda.synchronize()
+    want, rc = orc.verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables,
+                          hc.tables.context_lens, n_kv, hc.shape.scale)
+    assert rc == 0 and int(err.item()) == 0
+    got = out.cpu().numpy().astype(np.float64)
+    e = max_abs(got, want)
+    print(f"  max-abs {e:.2e}")
+    assert np.isfinite(got).all() and e <= TOL
