@@ -389,10 +389,11 @@ int pkv_spec_accept(const float* p_target, const float* q_draft,
                     int32_t* n_accepted, int32_t* next_token, int32_t* err_flag,
                     void* stream);
 
-/* Wavefronts of the balanced split on the current device for this shape:
- * one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the
+/* Wavefronts of the decode's balanced split on the current device for this
+ * shape: one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the
  * kernel's occupancy were lower), at most 8192, and at most one per 16 tiles of
- * units * ceil(max_context_len / 16). Queries the HIP runtime; returns
+ * units * ceil(max_context_len / 16). (The verification pass puts two per
+ * SIMD at both head sizes.) Queries the HIP runtime; returns
  * PKV_EINVAL / PKV_EUNSUPPORTED for bad shapes, PKV_EHIP without a device. */
 int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim,
