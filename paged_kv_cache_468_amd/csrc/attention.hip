@@ -89,6 +89,9 @@ constexpr int kMinTilesPerWave = 16; // balanced split: at least this much work 
 constexpr int kMaxQueryTokens = 64;  // verification pass: query tokens per sequence
 constexpr int kMaxChunkTokens = 16384;  // chunked prefill: tokens per chunk
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef PKV_DECODE_NBUF
+#define PKV_DECODE_NBUF 3
+#endif
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
 struct DecodeArgs {
@@ -158,6 +161,12 @@ __device__ inline void flag_error(int32_t* err_flag, int bit) {
 __device__ inline int seq_tiles(int ctx, int q_len, int max_ctx) {
   return (ctx >= q_len && ctx <= max_ctx) ? (ctx + 15) >> 4 : 0;
 }
+
+// A compile-time flag passed as a value (to a generic lambda).
+template <bool B>
+struct Flag {
+  constexpr operator bool() const { return B; }
+};
 
 // Round-to-nearest-even float -> bf16 bits (finite inputs).
 __device__ inline uint32_t bf16_rne_bits(float x) {
@@ -312,7 +321,9 @@ __device__ inline Rows<NG> rows_of(const DecodeArgs& a, int lane, int s, int h, 
 // every K/V tile. CAUSAL masks, per row, the positions after the row's own
 // (the verification pass); a row may then see nothing in a whole tile, so
 // its weights and rescale factors are guarded against -inf - (-inf).
-template <int D, bool STREAM, int NG, bool CAUSAL>
+// NBUF register sets hold tiles in flight (NBUF - 1 ahead of the one
+// being computed).
+template <int D, bool STREAM, int NG, bool CAUSAL, int NBUF>
 __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h,
                                        const Rows<NG>& rw, int ctx, int ta, int tb, bool store_new,
                                        f32x4_t (&acc)[NG][D / 16], float (&m_run)[NG],
@@ -348,165 +359,205 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
   const int k_lane_off = c * D + 8 * r;          // + 32m
   const int v_lane_off = c * 16 + 4 * r;         // + 256m (16 dims x 16 tokens)
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
   const int last_tile = (ctx - 1) >> 4;
   const int last_valid = ctx - last_tile * 16;   // tokens in the sequence's last tile
   const int new_slot = last_valid - 1;           // slot of position ctx - 1
   const bool has_new = !CAUSAL && a.k_new != nullptr && tb > last_tile;   // decode only
   const int first_masked = ctx - a.q_len + 1;    // causal: first position some row may not see
 
-  bf16x8_t kA[KM], kB[KM];
-  bf16x4_t vA[VM], vB[VM];
   bf16x8_t kn[KM];   // new token: key dims 32m + 8r .. +7
   short vn[VM];      // new token: value dim 16m + c
+  if (has_new) {
+    const int64_t row = ((int64_t)s * a.n_kv + h) * D;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) kn[m] = *(const bf16x8_t*)(a.k_new + row + 32 * m + 8 * r);
+#pragma unroll
+    for (int m = 0; m < VM; ++m) vn[m] = (short)a.v_new[row + 16 * m + c];
+  }
 
-  for (int cb = ta; cb < tb; cb += 64) {
-    const int nb = min(64, tb - cb);
-    // Physical block ids of this chunk: lane i holds entry cb + i.
-    const int my_id = lane < nb ? bt_row[cb + lane] : 0;
-    if (__ballot(lane < nb && (my_id < 0 || my_id >= a.num_blocks)) != 0) return false;
-    const bool new_here = has_new && last_tile < cb + nb;
-    if (new_here) {
-      const int64_t row = ((int64_t)s * a.n_kv + h) * D;
-#pragma unroll
-      for (int m = 0; m < KM; ++m) kn[m] = *(const bf16x8_t*)(a.k_new + row + 32 * m + 8 * r);
-#pragma unroll
-      for (int m = 0; m < VM; ++m) vn[m] = (short)a.v_new[row + 16 * m + c];
+  // Block ids: idw holds in lane l the id of tile j0 + NBUF - 1 + l of the
+  // segment (clamped to its last tile), the tiles whose loads iteration j0
+  // issues; it is loaded one iteration ahead, so no id waits on a round
+  // trip. An id outside the pool is never dereferenced: block 0 is read in
+  // its place, and the segment reports failure (its rows become NaN) and
+  // stores nothing.
+  const int n = tb - ta;
+  const int32_t* ids = a.block_tables + (int64_t)s * a.max_blocks + ta;
+  auto ids_from = [&](int j) { return ids[min(j + lane, n - 1)]; };
+  bool bad = false;
+
+  // NBUF register sets in a ring: tile j of the segment lives in set
+  // j % NBUF, and the loads of the next NBUF - 1 tiles are in flight while
+  // one is computed. blk_of[b]: the (checked) block id of set b's tile.
+  bf16x8_t kb[NBUF][KM];
+  bf16x4_t vb[NBUF][VM];
+  int blk_of[NBUF];
+
+  // Issue the loads of the tile in block blk into set b.
+  auto issue = [&](int blk, int b) {
+    if ((unsigned)blk >= (unsigned)a.num_blocks) {
+      bad = true;
+      blk = 0;
     }
-
-    auto load_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
-      const int blk = __builtin_amdgcn_readlane(my_id, i);
-      const int64_t base = (int64_t)blk * block_stride + head_off;
-      const uint16_t* kt = a.k_pool + base;
-      const uint16_t* vt = a.v_pool + base;
-      if (STREAM) {
+    blk_of[b] = blk;
+    const int64_t base = (int64_t)blk * block_stride + head_off;
+    const uint16_t* kt = a.k_pool + base;
+    const uint16_t* vt = a.v_pool + base;
+    if (STREAM) {
 #pragma unroll
-        for (int m = 0; m < KM; ++m)
-          kr[m] = __builtin_nontemporal_load((const bf16x8_t*)(kt + k_lane_off + 32 * m));
+      for (int m = 0; m < KM; ++m)
+        kb[b][m] = __builtin_nontemporal_load((const bf16x8_t*)(kt + k_lane_off + 32 * m));
+#pragma unroll
+      for (int m = 0; m < VM; ++m)
+        vb[b][m] = __builtin_nontemporal_load((const bf16x4_t*)(vt + v_lane_off + 256 * m));
+    } else {
+#pragma unroll
+      for (int m = 0; m < KM; ++m) kb[b][m] = *(const bf16x8_t*)(kt + k_lane_off + 32 * m);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) vb[b][m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
+    }
+  };
+
+  // Tile j of the segment, in set b. maybe_last: the tile may be the
+  // unit's last (new token, partly filled block); the steady loop below
+  // never computes the segment's last tile, so it passes false.
+  auto compute_tile = [&](int j, int b, auto maybe_last) {
+    bf16x8_t* kr = kb[b];
+    bf16x4_t* vr = vb[b];
+    const int tile = ta + j;
+    if (maybe_last && has_new && tile == last_tile) {
+      if (c == new_slot) {
+#pragma unroll
+        for (int m = 0; m < KM; ++m) kr[m] = kn[m];
+      }
+      if (r == (new_slot >> 2)) {
 #pragma unroll
         for (int m = 0; m < VM; ++m)
-          vr[m] = __builtin_nontemporal_load((const bf16x4_t*)(vt + v_lane_off + 256 * m));
-      } else {
 #pragma unroll
-        for (int m = 0; m < KM; ++m) kr[m] = *(const bf16x8_t*)(kt + k_lane_off + 32 * m);
-#pragma unroll
-        for (int m = 0; m < VM; ++m) vr[m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
+          for (int e = 0; e < 4; ++e)   // static indices keep the ring in registers
+            if (e == (new_slot & 3)) vr[m][e] = vn[m];
       }
-    };
-
-    auto compute_tile = [&](int i, bf16x8_t* kr, bf16x4_t* vr) {
-      if (new_here && cb + i == last_tile) {
+      // stored only while every id of the segment so far was valid
+      if (store_new && !bad) {
+        const int blk = blk_of[b];
+        const int64_t base = (int64_t)blk * block_stride + head_off;
+        uint16_t* kt = (uint16_t*)a.k_pool + base;
+        uint16_t* vt = (uint16_t*)a.v_pool + base;
         if (c == new_slot) {
 #pragma unroll
-          for (int m = 0; m < KM; ++m) kr[m] = kn[m];
+          for (int m = 0; m < KM; ++m) *(bf16x8_t*)(kt + new_slot * D + 32 * m + 8 * r) = kn[m];
         }
-        if (r == (new_slot >> 2)) {
+        if (r == 0) {
 #pragma unroll
-          for (int m = 0; m < VM; ++m) vr[m][new_slot & 3] = vn[m];
-        }
-        if (store_new) {
-          const int blk = __builtin_amdgcn_readlane(my_id, i);
-          const int64_t base = (int64_t)blk * block_stride + head_off;
-          uint16_t* kt = (uint16_t*)a.k_pool + base;
-          uint16_t* vt = (uint16_t*)a.v_pool + base;
-          if (c == new_slot) {
-#pragma unroll
-            for (int m = 0; m < KM; ++m) *(bf16x8_t*)(kt + new_slot * D + 32 * m + 8 * r) = kn[m];
-          }
-          if (r == 0) {
-#pragma unroll
-            for (int m = 0; m < VM; ++m) vt[(16 * m + c) * 16 + new_slot] = (uint16_t)vn[m];
-          }
+          for (int m = 0; m < VM; ++m) vt[(16 * m + c) * 16 + new_slot] = (uint16_t)vn[m];
         }
       }
-      float x[NG][4];
+    }
+    float x[NG][4];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) {
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < KM; ++m)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
+      for (int m = 0; m < KM; ++m)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[g][e] = sc[e] * a.scale_log2;
-      }
-      if (cb + i == last_tile && last_valid < 16) {   // the partly filled last block
-        const int valid = last_valid - 4 * r;         // tokens of this quad still inside
+      for (int e = 0; e < 4; ++e) x[g][e] = sc[e] * a.scale_log2;
+    }
+    if (maybe_last && tile == last_tile && last_valid < 16) {   // the partly filled last block
+      const int valid = last_valid - 4 * r;         // tokens of this quad still inside
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e >= valid) x[g][e] = -__builtin_inff();
-        // masked slots may hold anything (NaN included): zero their values
-        const uint32_t keep0 = (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
-        const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int m = 0; m < VM; ++m) {
-          u32x2_t wv = __builtin_bit_cast(u32x2_t, vr[m]);
-          wv[0] &= keep0;
-          wv[1] &= keep1;
-          vr[m] = __builtin_bit_cast(bf16x4_t, wv);
-        }
-      }
-      if (CAUSAL && (cb + i) * 16 + 15 >= first_masked) {
-        const int p0 = (cb + i) * 16 + 4 * r;   // position of this lane's first token
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (p0 + e > rw.lim[g]) x[g][e] = -__builtin_inff();
-      }
-      bf16x8_t pb[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        float mx = fmaxf(fmaxf(x[g][0], x[g][1]), fmaxf(x[g][2], x[g][3]));
-        mx = wave_max_across_rows(mx);
-        if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run[g], mx);
-          float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-          if (CAUSAL && m_new == -__builtin_inff()) alpha = 1.f;   // row still sees nothing
-          m_run[g] = m_new;
-          l_run[g] *= alpha;
-#pragma unroll
-          for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
-        }
-        const float m_use = (CAUSAL && m_run[g] == -__builtin_inff()) ? 0.f : m_run[g];
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[g][e] - m_use);
-        l_run[g] += (p[0] + p[1]) + (p[2] + p[3]);
-        // P = hi + lo, both bf16: hi by truncation (exact remainder), lo rounded.
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
-          lo[e] = bf16_rne_bits(p[e] - __uint_as_float(hi[e]));
-        }
-        const u32x4_t pw = u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
-                                   lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-        pb[g] = __builtin_bit_cast(bf16x8_t, pw);
-      }
+        for (int e = 0; e < 4; ++e)
+          if (e >= valid) x[g][e] = -__builtin_inff();
+      // masked slots may hold anything (NaN included): zero their values
+      const uint32_t keep0 = (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int m = 0; m < VM; ++m) {
-        const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[g], acc[g][m], 0, 0, 0);
+        u32x2_t wv = __builtin_bit_cast(u32x2_t, vr[m]);
+        wv[0] &= keep0;
+        wv[1] &= keep1;
+        vr[m] = __builtin_bit_cast(bf16x4_t, wv);
       }
-    };
-
-    // Two register sets: the next tile's loads are in flight while the
-    // current one is computed.
-    load_tile(0, kA, vA);
-    int i = 0;
-    for (; i + 1 < nb; i += 2) {
-      load_tile(i + 1, kB, vB);
-      compute_tile(i, kA, vA);
-      if (i + 2 < nb) load_tile(i + 2, kA, vA);
-      compute_tile(i + 1, kB, vB);
     }
-    if (i < nb) compute_tile(i, kA, vA);
+    if (CAUSAL && tile * 16 + 15 >= first_masked) {
+      const int p0 = tile * 16 + 4 * r;   // position of this lane's first token
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (p0 + e > rw.lim[g]) x[g][e] = -__builtin_inff();
+    }
+    bf16x8_t pb[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float mx = fmaxf(fmaxf(x[g][0], x[g][1]), fmaxf(x[g][2], x[g][3]));
+      mx = wave_max_across_rows(mx);
+      if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run[g], mx);
+        float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        if (CAUSAL && m_new == -__builtin_inff()) alpha = 1.f;   // row still sees nothing
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+      }
+      const float m_use = (CAUSAL && m_run[g] == -__builtin_inff()) ? 0.f : m_run[g];
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[g][e] - m_use);
+      l_run[g] += (p[0] + p[1]) + (p[2] + p[3]);
+      // P = hi + lo, both bf16: hi by truncation (exact remainder), lo rounded.
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = __float_as_uint(p[e]) & 0xFFFF0000u;
+        lo[e] = bf16_rne_bits(p[e] - __uint_as_float(hi[e]));
+      }
+      const u32x4_t pw = u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
+                                 lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      pb[g] = __builtin_bit_cast(bf16x8_t, pw);
+    }
+#pragma unroll
+    for (int m = 0; m < VM; ++m) {
+      const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[g], acc[g][m], 0, 0, 0);
+    }
+  };
+
+  // The steady loop runs while every load it issues is inside the segment,
+  // so its loads are unconditional and the compiler's waits on them stay
+  // exact; the last (at most 2 NBUF - 2) tiles are computed after it.
+  const int id0 = ids_from(0);
+  int idw = ids_from(NBUF - 1);
+  int j0 = 0;
+  if (n >= 2 * NBUF - 1) {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) issue(__builtin_amdgcn_readlane(id0, b), b);
+    do {
+      const int idnext = ids_from(j0 + 2 * NBUF - 1);
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        issue(__builtin_amdgcn_readlane(idw, b), (b + NBUF - 1) % NBUF);
+        compute_tile(j0 + b, b, Flag<false>{});
+      }
+      idw = idnext;
+      j0 += NBUF;
+    } while (j0 + 2 * NBUF - 2 < n);
+  } else {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b)
+      if (b < n) issue(__builtin_amdgcn_readlane(id0, b), b);
   }
-  return true;
+#pragma unroll
+  for (int b = 0; b < 2 * NBUF - 2; ++b) {
+    if (j0 + b + NBUF - 1 < n) issue(__builtin_amdgcn_readlane(idw, b), (b + NBUF - 1) % NBUF);
+    if (j0 + b < n) compute_tile(j0 + b, b % NBUF, Flag<true>{});
+  }
+  return !bad;
 }
 
 // Write a finished segment's row: out directly when the segment covers its
@@ -586,8 +637,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   float m_run[1], l_run[1];
   const bool ok =
       shares_first_block(a, s)
-          ? process_segment<D, false, 1, false>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run)
-          : process_segment<D, true, 1, false>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run);
+          ? process_segment<D, false, 1, false, 2>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run)
+          : process_segment<D, true, 1, false, 2>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run);
   finish_rows<D, 1>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, rw, acc, m_run,
                     l_run);
 }
@@ -596,7 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // (head, group, sequence, tile) order, T = all tiles of the launch. The
 // wave holding a unit's first tile records, for the merge kernel, the
 // unit's first partial slot and its number of partials (1: written here).
-template <int D, int NG, bool CAUSAL>
+template <int D, int NG, bool CAUSAL, int NBUF>
 __device__ inline void balanced_body(const DecodeArgs& a) {
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
@@ -662,9 +713,9 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     float m_run[NG], l_run[NG];
     const bool ok =
         shares_first_block(a, s)
-            ? process_segment<D, false, NG, CAUSAL>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
+            ? process_segment<D, false, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
                                                     m_run, l_run)
-            : process_segment<D, true, NG, CAUSAL>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
+            : process_segment<D, true, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, pos, tb, qg == 0, acc,
                                                    m_run, l_run);
     finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
     cur += tb - pos;
@@ -683,8 +734,8 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
 
 // The decode step's kernel: one query row per head, the append fused in.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_balanced_kernel(DecodeArgs a) {
-  balanced_body<D, 1, false>(a);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void paged_attn_balanced_kernel(DecodeArgs a) {
+  balanced_body<D, 1, false, D == 128 ? PKV_DECODE_NBUF : 2>(a);
 }
 
 // The verification pass: q_len query tokens per sequence, causal among
@@ -694,7 +745,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // schedules the loads of the next tile further ahead.
 template <int D, int NG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_verify_kernel(DecodeArgs a) {
-  balanced_body<D, NG, true>(a);
+  balanced_body<D, NG, true, 2>(a);
 }
 
 // Chunked prefill with the K/V tiles staged in LDS. A workgroup of
