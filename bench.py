@@ -78,7 +78,8 @@ class State:
     pass
 
 
-def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, fused=True):
+def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, fused=True,
+                prefix_kernel=False):
     """Block tables from the refcounted allocator, pools filled on the
     device, every layer's buffers, and pre-marshalled library calls."""
     cl = w.context_lengths(shape, seed).astype(np.int32)
@@ -154,6 +155,13 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
     S.partition = partition_tokens
     S.split_waves = pkv.pkv_decode_split_waves(B, n_q, n_kv, d, S.max_ctx) if partition_tokens == 0 else 0
     ws_bytes = pkv.pkv_decode_workspace_bytes(B, n_q, n_kv, d, S.max_ctx, S.partition)
+    # the shared prefix read once for all sequences (pkv_decode_step_prefix)
+    S.prefix_blocks = n_prefix if (prefix_kernel and fused and partition_tokens == 0) else 0
+    S.prefix_table = None
+    if S.prefix_blocks:
+        S.prefix_table = torch.from_numpy(prefix[:n_prefix].copy()).to(dev)
+        ws_bytes = max(ws_bytes, pkv.pkv_decode_prefix_workspace_bytes(B, n_q, n_kv, d, S.max_ctx,
+                                                                       n_prefix, B))
     S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     S.fused = fused
     S.calls = layer_calls(pkv, S)
@@ -169,7 +177,15 @@ def layer_calls(pkv, S):
     kv_append + partition + merge."""
     sh, calls = S.shape, []
     for l in range(sh.n_layers):
-        if S.fused:
+        if S.prefix_blocks:
+            # the shared prefix read once for all sequences: prefix,
+            # partition and merge kernels in one call
+            calls.append([
+                ("decode_step_prefix", pkv.prepare_decode_step_prefix(
+                    S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt,
+                    S.cl, sh.scale, S.max_ctx, S.prefix_table, 0, S.B, workspace=S.ws,
+                    err_flag=S.err))])
+        elif S.fused:
             # pkv_decode_step as its two launches, so that events can time each
             calls.append([
                 ("decode_step_partition", pkv.prepare_decode_step_partition(
@@ -228,6 +244,24 @@ def attn_alg_bytes(S, ctx):
     B = len(ctx)
     tbl = 4 * int(np.ceil(ctx / BLOCK).astype(np.int64).sum())
     return kv_bytes(S, ctx) + B * sh.n_q * sh.d * (2 + 4) + tbl + 4 * B
+
+
+def prefix_call_alg_bytes(S, ctx):
+    """Algorithmic bytes of one pkv_decode_step_prefix call: the bytes it
+    must move when the prefix is read once. K and V of the prefix once, of
+    every sequence's tokens outside the prefix (a sequence whose context
+    ends inside the prefix reads its own blocks), q, the fp32 outputs, the
+    table entries, the context lengths and the appended rows."""
+    sh = S.shape
+    B = len(ctx)
+    per_tok = 2 * sh.n_kv * sh.d * 2
+    pre = S.prefix_blocks * BLOCK
+    reads = (ctx - 1) // BLOCK >= S.prefix_blocks
+    own = int(np.where(reads, ctx - pre, ctx).astype(np.int64).sum())
+    tiles = int(np.where(reads, np.ceil(ctx / BLOCK) - S.prefix_blocks,
+                         np.ceil(ctx / BLOCK)).astype(np.int64).sum())
+    return (per_tok * (own + pre) + B * sh.n_q * sh.d * (2 + 4) + 4 * (tiles + S.prefix_blocks)
+            + 4 * B + append_alg_bytes(S, B))
 
 
 def append_alg_bytes(S, B):
@@ -323,9 +357,15 @@ def run(pkv, torch, S, steps, warmup, graph=True):
 
     # the roofline kernel: the partition kernel, which reads the KV cache
     # (with the append inside when fused); the merge reads only partials
-    dom = "decode_step_partition" if S.fused else "paged_attn_partition"
-    dom_bytes = sum(attn_alg_bytes(S, c) + (append_alg_bytes(S, S.B) if S.fused else 0)
-                    for c in eager_ctx) / steps
+    if S.prefix_blocks:
+        # the prefix call as a whole: its three kernels against the bytes
+        # it must move (the prefix counted once)
+        dom = "decode_step_prefix"
+        alg = lambda c: prefix_call_alg_bytes(S, c)
+    else:
+        dom = "decode_step_partition" if S.fused else "paged_attn_partition"
+        alg = lambda c: attn_alg_bytes(S, c) + (append_alg_bytes(S, S.B) if S.fused else 0)
+    dom_bytes = sum(alg(c) for c in eager_ctx) / steps
     # Its launch duration without the per-launch event overhead: its
     # launches alone, one per layer, back to back from a graph, replayed
     # between two events. The kernel only reads the cache and rewrites its
@@ -351,7 +391,7 @@ def run(pkv, torch, S, steps, warmup, graph=True):
             raise RuntimeError(f"device error flag {int(S.err.item())}")
         b2b_launches = reps * L
         b2b_us = t0.elapsed_time(t1) * 1e3 / b2b_launches
-        b2b_bytes = attn_alg_bytes(S, S.ctx) + (append_alg_bytes(S, S.B) if S.fused else 0)
+        b2b_bytes = alg(S.ctx)
     kvb = sum(kv_bytes(S, c) * L for c in step_ctx)           # all layers, all timed steps
     return {
         "ms_per_step": ms_per_step,
@@ -845,6 +885,9 @@ def main():
     ap.add_argument("--no-share", action="store_true", help="main run with private prefix copies")
     ap.add_argument("--skip-no-share", action="store_true", help="skip the second, unshared run")
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-prefix-kernel", action="store_true",
+                    help="shared prefix: pkv_decode_step (every sequence reads the prefix through "
+                         "its own table) instead of pkv_decode_step_prefix")
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per layer (kv_append, partition, merge) instead of pkv_decode_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
@@ -942,7 +985,7 @@ def main():
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {wname} share={share_main}")
     S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens,
-                    fused=not args.unfused)
+                    fused=not args.unfused, prefix_kernel=not args.no_prefix_kernel)
     log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
     main_r = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
     log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step ({main_r['step_mode']}), "
@@ -1032,7 +1075,12 @@ def main():
             "duration_us": main_r["dominant_us"],
             "timing": main_r["dominant_timing"],
             "us_per_launch_events_in_step": main_r["dominant_us_per_launch_events"],
-            "note": ("with a shared prefix the algorithmic bytes count every sequence's whole "
+            "note": ("decode_step_prefix: the whole call (prefix, partition and merge kernels) "
+                     "against the bytes it must move, the shared prefix counted once; value "
+                     "counts every sequence's whole context (logical KV bytes). no_share gives "
+                     "the partition kernel alone with every byte unique"
+                     if main_r["dominant"] == "decode_step_prefix" else
+                     "with a shared prefix the algorithmic bytes count every sequence's whole "
                      "context while the shared blocks are re-read from cache, so achieved can "
                      "exceed HBM peak (no_share gives the all-unique case)"),
         },

@@ -293,6 +293,59 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
                               void* workspace, size_t workspace_bytes,
                               int32_t* err_flag, void* stream);
 
+/* A decode step whose batch shares a prompt prefix held once in the pools
+ * ([SLS] "Reuse shared prefixes": requests that begin with the same prompt
+ * share its cached blocks; [DSS] "Paged attention": shared blocks are
+ * reference-counted and written only after a copy). The result is that of
+ * pkv_decode_step on the same arguments, to fp32 rounding (the softmax is
+ * merged in another order); the pools are bitwise the same.
+ *
+ * Sequences prefix_first_seq .. prefix_first_seq + prefix_num_seqs - 1 are
+ * the candidates. A candidate whose first prefix_blocks table entries are
+ * prefix_table's ids (checked on the device at every call) and whose
+ * context extends past the prefix (context_lens[s] > 16 * prefix_blocks)
+ * reads its first prefix_blocks tiles through the prefix kernel, which
+ * serves the query rows of all candidates from each prefix tile (16 rows
+ * per K/V read where the decode serves n_q/n_kv); the partition kernel
+ * covers only its later tiles. Every other sequence (a context that ends
+ * inside the prefix, other blocks there such as a copy of a block it
+ * wrote, or outside the range) runs as in pkv_decode_step. So the result
+ * never depends on which sequences the range names, only the speed.
+ *   prefix_table    : device int32 [prefix_blocks], the prefix's block ids
+ *   prefix_blocks   : whole 16-token blocks of the prefix, in
+ *                     [0, max_blocks_per_seq]; 0 (or prefix_num_seqs = 0)
+ *                     is pkv_decode_step with the balanced split
+ *   workspace       : at least pkv_decode_prefix_workspace_bytes(...) bytes
+ *                     (the decode's workspace, then the prefix kernel's
+ *                     partials and one membership flag per candidate); no
+ *                     initialisation needed
+ * Other arguments as for pkv_decode_step with partition_tokens = 0. Three
+ * launches on the stream: prefix kernel, partition kernel (with the
+ * append), merge kernel. Host-checked errors: PKV_EINVAL for a member range
+ * outside [0, num_seqs), a negative count or prefix_blocks >
+ * max_blocks_per_seq, a null prefix_table with a non-empty prefix, and
+ * everything pkv_decode_step checks; PKV_EWORKSPACE. Device errors as for
+ * pkv_decode_step; an id in prefix_table outside the pool sets
+ * PKV_DEVERR_BLOCK_ID and makes the rows of every member that reads the
+ * prefix NaN (never read out of bounds). */
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len,
+                                         int32_t prefix_blocks,
+                                         int32_t prefix_num_seqs);
+int pkv_decode_step_prefix(float* out, const void* q, const void* k_new,
+                           const void* v_new, void* k_pool, void* v_pool,
+                           const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, float scale,
+                           int32_t max_context_len,
+                           const int32_t* prefix_table, int32_t prefix_blocks,
+                           int32_t prefix_first_seq, int32_t prefix_num_seqs,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* err_flag, void* stream);
+
 /* ------------------------------------------------------------------------
  * Verification pass of speculative decoding ([M23] 23.5: the target model
  * checks all drafted tokens in one pass, at about the cost of one decode

@@ -54,6 +54,10 @@ SIGNATURES = {
     "pkv_decode_step_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                                  _vp, _sz, _vp, _vp]),
+    "pkv_decode_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_step_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32,
+                                              _i32, _vp, _sz, _vp, _vp]),
     "pkv_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
@@ -305,6 +309,46 @@ def pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_
     args, _ = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
                          max_context_len, partition_tokens, workspace, err_flag, stream)
     _check(lib.pkv_decode_step(*args), "pkv_decode_step")
+
+
+def pkv_decode_prefix_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
+                                      prefix_blocks, prefix_num_seqs):
+    return int(lib.pkv_decode_prefix_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim,
+                                                     max_context_len, prefix_blocks,
+                                                     prefix_num_seqs))
+
+
+def _prefix_step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                      max_context_len, prefix_table, prefix_first_seq, prefix_num_seqs, workspace,
+                      err_flag, stream):
+    torch = _torch()
+    pt = _dev(prefix_table, "prefix_table", torch.int32, 1)
+    n_pre = prefix_table.shape[0]
+    _, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16, 3)
+    if workspace is None:
+        need = pkv_decode_prefix_workspace_bytes(q.shape[0], q.shape[1], n_kv, d, max_context_len,
+                                                 n_pre, prefix_num_seqs)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, 0, workspace, err_flag, stream)
+    # C order: the step's arguments up to max_context_len, then the prefix
+    # (table, blocks, first member, member count) in place of partition_tokens
+    return args[:16] + (pt, n_pre, int(prefix_first_seq), int(prefix_num_seqs)) + args[17:], ws
+
+
+def pkv_decode_step_prefix(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                           max_context_len, prefix_table, prefix_first_seq, prefix_num_seqs,
+                           workspace=None, err_flag=None, stream=None):
+    """pkv_decode_step for a batch whose sequences prefix_first_seq ..
+    prefix_first_seq + prefix_num_seqs - 1 share the blocks prefix_table
+    (device int32 [prefix_blocks]) as the start of their tables: the
+    prefix's tiles are read once for all members. workspace: at least
+    pkv_decode_prefix_workspace_bytes(...) bytes, or None."""
+    args, _ = _prefix_step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                                scale, max_context_len, prefix_table, prefix_first_seq,
+                                prefix_num_seqs, workspace, err_flag, stream)
+    _check(lib.pkv_decode_step_prefix(*args), "pkv_decode_step_prefix")
 
 
 def pkv_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
@@ -603,6 +647,17 @@ def prepare_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, block_ta
     return PreparedCall("pkv_decode_step_partition", args,
                         (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
                          err_flag))
+
+
+def prepare_decode_step_prefix(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                               scale, max_context_len, prefix_table, prefix_first_seq,
+                               prefix_num_seqs, workspace=None, err_flag=None, stream=None):
+    args, ws = _prefix_step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                                 scale, max_context_len, prefix_table, prefix_first_seq,
+                                 prefix_num_seqs, workspace, err_flag, stream)
+    return PreparedCall("pkv_decode_step_prefix", args,
+                        (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                         prefix_table, ws, err_flag))
 
 
 def prepare_paged_attn_decode(*a, **k):
