@@ -83,6 +83,11 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
     """Block tables from the refcounted allocator, pools filled on the
     device, every layer's buffers, and pre-marshalled library calls."""
     cl = w.context_lengths(shape, seed).astype(np.int32)
+    if shape.prefix_tokens:
+        # the sequences longer than the prefix first: with sharing they hold
+        # all of its blocks (the shorter ones copy the block they write), so
+        # they are pkv_decode_step_prefix's member range
+        cl = cl[np.argsort(cl <= shape.prefix_tokens, kind="stable")]
     B = len(cl)
     L, n_q, n_kv, d = shape.n_layers, shape.n_q, shape.n_kv, shape.d
     final_ctx = cl + extra_tokens
@@ -158,10 +163,11 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
     # the shared prefix read once for all sequences (pkv_decode_step_prefix)
     S.prefix_blocks = n_prefix if (prefix_kernel and fused and partition_tokens == 0) else 0
     S.prefix_table = None
+    S.prefix_members = int((cl > shape.prefix_tokens).sum()) if S.prefix_blocks else 0
     if S.prefix_blocks:
         S.prefix_table = torch.from_numpy(prefix[:n_prefix].copy()).to(dev)
         ws_bytes = max(ws_bytes, pkv.pkv_decode_prefix_workspace_bytes(B, n_q, n_kv, d, S.max_ctx,
-                                                                       n_prefix, B))
+                                                                       n_prefix, S.prefix_members))
     S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     S.fused = fused
     S.calls = layer_calls(pkv, S)
@@ -183,7 +189,7 @@ def layer_calls(pkv, S):
             calls.append([
                 ("decode_step_prefix", pkv.prepare_decode_step_prefix(
                     S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt,
-                    S.cl, sh.scale, S.max_ctx, S.prefix_table, 0, S.B, workspace=S.ws,
+                    S.cl, sh.scale, S.max_ctx, S.prefix_table, 0, S.prefix_members, workspace=S.ws,
                     err_flag=S.err))])
         elif S.fused:
             # pkv_decode_step as its two launches, so that events can time each
@@ -249,14 +255,15 @@ def attn_alg_bytes(S, ctx):
 def prefix_call_alg_bytes(S, ctx):
     """Algorithmic bytes of one pkv_decode_step_prefix call: the bytes it
     must move when the prefix is read once. K and V of the prefix once, of
-    every sequence's tokens outside the prefix (a sequence whose context
-    ends inside the prefix reads its own blocks), q, the fp32 outputs, the
+    every member's tokens after the prefix and of every other sequence's
+    whole context (a member whose context ends inside the prefix reads its
+    own blocks), q, the fp32 outputs, the
     table entries, the context lengths and the appended rows."""
     sh = S.shape
     B = len(ctx)
     per_tok = 2 * sh.n_kv * sh.d * 2
     pre = S.prefix_blocks * BLOCK
-    reads = (ctx - 1) // BLOCK >= S.prefix_blocks
+    reads = ((ctx - 1) // BLOCK >= S.prefix_blocks) & (np.arange(B) < S.prefix_members)
     own = int(np.where(reads, ctx - pre, ctx).astype(np.int64).sum())
     tiles = int(np.where(reads, np.ceil(ctx / BLOCK) - S.prefix_blocks,
                          np.ceil(ctx / BLOCK)).astype(np.int64).sum())

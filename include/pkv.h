@@ -102,6 +102,7 @@ enum {
 #define PKV_DEVERR_CONTEXT 2    /* a context length outside [1, max_context_len] */
 #define PKV_DEVERR_COPY_PAIR 4  /* a copy_blocks id outside [0, num_blocks) */
 #define PKV_DEVERR_TOKEN 8      /* pkv_spec_accept: a drafted token outside [0, vocab) */
+#define PKV_DEVERR_PREFIX 16    /* pkv_decode_step_prefix: a member's table does not start with the prefix */
 
 /* Static string for a status code; never NULL. */
 const char* pkv_strerror(int status);
@@ -301,27 +302,31 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
  * merged in another order); the pools are bitwise the same.
  *
  * Sequences prefix_first_seq .. prefix_first_seq + prefix_num_seqs - 1 are
- * the candidates. A candidate whose first prefix_blocks table entries are
- * prefix_table's ids (checked on the device at every call) and whose
- * context extends past the prefix (context_lens[s] > 16 * prefix_blocks)
- * reads its first prefix_blocks tiles through the prefix kernel, which
- * serves the query rows of all candidates from each prefix tile (16 rows
- * per K/V read where the decode serves n_q/n_kv); the partition kernel
- * covers only its later tiles. Every other sequence (a context that ends
- * inside the prefix, other blocks there such as a copy of a block it
- * wrote, or outside the range) runs as in pkv_decode_step. So the result
- * never depends on which sequences the range names, only the speed.
+ * the members. A member whose context extends past the prefix
+ * (context_lens[s] > 16 * prefix_blocks) must hold prefix_table's ids as
+ * its first prefix_blocks table entries; its first prefix_blocks tiles are
+ * read through the prefix kernel, which serves the query rows of all
+ * members from each prefix tile (16 rows per K/V read where the decode
+ * serves n_q/n_kv), and the partition kernel covers only its later tiles.
+ * The device checks the claim at every call: a member whose table differs
+ * there gets NaN rows and sets PKV_DEVERR_PREFIX (never a wrong finite
+ * result). A member whose context ends inside the prefix, and every
+ * sequence outside the range, runs as in pkv_decode_step. The prefix
+ * kernel runs on a second stream of the library's (one per host thread and
+ * device, default priority, created on first use), forked from and joined
+ * back into `stream`, so it overlaps the partition kernel; inside a stream
+ * capture this records a fork and a join.
  *   prefix_table    : device int32 [prefix_blocks], the prefix's block ids
  *   prefix_blocks   : whole 16-token blocks of the prefix, in
  *                     [0, max_blocks_per_seq]; 0 (or prefix_num_seqs = 0)
  *                     is pkv_decode_step with the balanced split
  *   workspace       : at least pkv_decode_prefix_workspace_bytes(...) bytes
  *                     (the decode's workspace, then the prefix kernel's
- *                     partials and one membership flag per candidate); no
+ *                     partials and one check flag per member); no
  *                     initialisation needed
  * Other arguments as for pkv_decode_step with partition_tokens = 0. Three
- * launches on the stream: prefix kernel, partition kernel (with the
- * append), merge kernel. Host-checked errors: PKV_EINVAL for a member range
+ * launches: the prefix kernel (second stream), the partition kernel with
+ * the append, then the merge kernel (both on `stream`). Host-checked errors: PKV_EINVAL for a member range
  * outside [0, num_seqs), a negative count or prefix_blocks >
  * max_blocks_per_seq, a null prefix_table with a non-empty prefix, and
  * everything pkv_decode_step checks; PKV_EWORKSPACE. Device errors as for

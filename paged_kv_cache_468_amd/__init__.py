@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4, -5
 PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT, PKV_DEVERR_COPY_PAIR, PKV_DEVERR_TOKEN = 1, 2, 4, 8
+PKV_DEVERR_PREFIX = 16
 BLOCK_TOKENS = 16
 
 # every symbol include/pkv.h declares, with its ctypes signature

@@ -67,8 +67,9 @@
 //   Shared prefix (pkv_decode_step_prefix): the prefix kernel serves the
 //   rows of all member sequences of a common prompt prefix from each prefix
 //   tile, 16 rows per read (the decode serves group rows), and leaves
-//   partials per row; the partition kernel's split then counts only each
-//   member's tiles after the prefix, and the merge kernel takes both lists.
+//   partials per row; the partition kernel's split counts only each
+//   member's tiles after the prefix. The two run side by side on two
+//   streams, and the merge kernel takes both lists.
 //
 //   Grid: workgroups of 4 waves; the workgroup index is remapped so that
 //   consecutive work (same KV head, neighbouring sequences) lands on the
@@ -141,7 +142,7 @@ struct DecodeArgs {
   int pre_parts;     // tile ranges per (KV head, row group)
   float* pre_ml;     // [n_kv * pre_qgroups * pre_parts][16][2]
   float* pre_acc;    // [n_kv * pre_qgroups * pre_parts][16][D]
-  int32_t* pre_member;  // [pre_count]: 1 if the sequence's table starts with pre_table
+  int32_t* pre_member;  // [pre_count]: 1 if the candidate's table starts with pre_table
 };
 
 __device__ inline float wave_max_across_rows(float x) {
@@ -184,16 +185,16 @@ __device__ inline int seq_tiles(int ctx, int q_len, int max_ctx) {
 }
 
 // Tiles of sequence s read through the shared prefix (the prefix kernel's
-// partials): all of them for a candidate whose table starts with the
-// prefix's blocks (checked by the prefix kernel) and whose last tile lies
-// after the prefix; none otherwise (its context ends inside the prefix, or
-// it holds other blocks there, e.g. a copy of the block it wrote).
+// partials): all of them for a candidate whose last tile lies after the
+// prefix (such a candidate holds the prefix's blocks as its first table
+// entries; the prefix kernel checks that, and the merge turns a candidate
+// that does not into NaN rows), none otherwise (its context ends inside the
+// prefix, so the block it writes is not a prefix block).
 __device__ inline int prefix_skip(const DecodeArgs& a, int s, int ctx) {
-  if (a.pre_tiles == 0) return 0;
-  const unsigned m = (unsigned)(s - a.pre_first);
-  if (m >= (unsigned)a.pre_count) return 0;
-  const int member = a.pre_member[m];   // issued before ctx is needed
-  return (member != 0 && ((ctx - 1) >> 4) >= a.pre_tiles) ? a.pre_tiles : 0;
+  return (a.pre_tiles > 0 && (unsigned)(s - a.pre_first) < (unsigned)a.pre_count &&
+          ((ctx - 1) >> 4) >= a.pre_tiles)
+             ? a.pre_tiles
+             : 0;
 }
 
 // Tiles of sequence s in the partition kernel's split: its tiles after the
@@ -795,7 +796,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // Shared prefix: the tiles every member sequence reads from the same
 // blocks, computed once for all of them. Candidates are the sequences
 // pre_first .. pre_first + pre_count - 1; this kernel also records which of
-// them are members (their tables start with the prefix's blocks). The query rows of KV head h are
+// them hold the prefix's blocks as the start of their tables, for the merge
+// to check. It runs beside the partition kernel (another stream): neither
+// reads what the other writes. The query rows of KV head h are
 // the pairs (member i, head jj of h's group), row i * group + jj, in groups
 // of 16; one wave per (KV head, row group, part) takes part p of the
 // prefix's tiles, serves its 16 rows from each tile (the decode serves
@@ -1206,6 +1209,14 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   int np = 0;
   int64_t pre_row = 0;
   if (prefix_skip(a, s, ctx) > 0) {
+    // the partition kernel skipped the prefix's tiles of this sequence: its
+    // table must start with the prefix's blocks, else the row is NaN
+    if (a.pre_member[s - a.pre_first] == 0) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = nan;
+      if (hq == 0 && gr == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_PREFIX);
+      return;
+    }
     const int tpp = (a.pre_tiles + a.pre_parts - 1) / a.pre_parts;
     np = (a.pre_tiles + tpp - 1) / tpp;
     const int pr = (s - a.pre_first) * a.group + gr;
@@ -1685,6 +1696,31 @@ extern "C" int pkv_decode_step(PKV_STEP_PARAMS) {
   return launch_merge(a, d, (hipStream_t)stream);
 }
 
+// A second stream (default priority) and two events per host thread and
+// device, created on first use and kept until the process ends: the shared
+// prefix's kernel runs there beside the partition kernel.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static SideStream* side_stream() {
+  thread_local SideStream per_device[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& s = per_device[dev];
+  if (!s.stream) {
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+      hipStreamDestroy(s.stream);
+      s.stream = nullptr;
+      return nullptr;
+    }
+  }
+  return &s;
+}
+
 static bool valid_prefix_args(int32_t num_seqs, int32_t max_blocks_per_seq,
                               const int32_t* prefix_table, int32_t prefix_blocks,
                               int32_t prefix_first_seq, int32_t prefix_num_seqs) {
@@ -1752,11 +1788,23 @@ extern "C" int pkv_decode_step_prefix(float* out, const void* q, const void* k_n
     const int64_t wgs = (waves + kWaves - 1) / kWaves;
     pa.wg_per_xcd = (int)((wgs + kXcds - 1) / kXcds);
     const unsigned grid = (unsigned)pa.wg_per_xcd * kXcds;
+    // The prefix kernel on this thread's side stream, beside the partition
+    // kernel: forked after the caller's earlier work, joined before the
+    // merge (also inside a stream capture, as a fork and a join).
+    SideStream* side = side_stream();
+    if (!side) return PKV_EHIP;
+    if (hipEventRecord(side->fork, st) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return PKV_EHIP;
     if (d == 128)
-      hipLaunchKernelGGL(paged_attn_prefix_kernel<128>, dim3(grid), dim3(256), 0, st, pa);
+      hipLaunchKernelGGL(paged_attn_prefix_kernel<128>, dim3(grid), dim3(256), 0, side->stream, pa);
     else
-      hipLaunchKernelGGL(paged_attn_prefix_kernel<64>, dim3(grid), dim3(256), 0, st, pa);
+      hipLaunchKernelGGL(paged_attn_prefix_kernel<64>, dim3(grid), dim3(256), 0, side->stream, pa);
     if (hipGetLastError() != hipSuccess) return PKV_EHIP;
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return PKV_EHIP;
+    const int prc = launch_partition(a, d, st);
+    if (hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return PKV_EHIP;
+    return prc != PKV_OK ? prc : launch_merge(a, d, st);
   }
   const int prc = launch_partition(a, d, st);
   return prc != PKV_OK ? prc : launch_merge(a, d, st);

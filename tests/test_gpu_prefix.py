@@ -8,7 +8,8 @@ table), within 1e-5 of pkv_decode_step on the same inputs (only the order of
 the softmax merge differs), and the pools bitwise equal to pkv_decode_step's
 (the append is the same). Members whose context ends inside the prefix,
 sequences outside the member range, head groups above 16 and both head
-sizes are covered; an empty prefix is pkv_decode_step bit for bit.
+sizes are covered; an empty prefix is pkv_decode_step bit for bit; a member
+whose table does not start with the prefix is caught on the device.
 """
 import math
 
@@ -16,7 +17,8 @@ import numpy as np
 import pytest
 
 import workload as w
-from gpu_util import TOL, DevCase, gpu_step, max_abs, oracle_step, to_dev_i32, to_host_u16
+from gpu_util import (TOL, DevCase, gpu_step, max_abs, oracle_step, to_dev_bf16, to_dev_i32,
+                      to_host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,10 +86,11 @@ def test_prefix_step_parity(pkv, orc, case, members):
     assert np.array_equal(to_host_u16(a.v_pool), v_ref)
 
 
-def test_non_member_table_takes_normal_path(pkv, orc):
-    """A candidate whose table holds another block inside the prefix range
-    (here a block of another sequence with different values) is not a
-    member: it reads its own table, and matches the oracle."""
+def test_member_table_mismatch_flagged(pkv, orc):
+    """A member past the prefix whose table holds another block inside the
+    prefix range (here a block of another sequence, other values): the
+    device check catches it, its rows are NaN and PKV_DEVERR_PREFIX is set;
+    every other row is unaffected (oracle on the same tables)."""
     n_q, n_kv, d, prefix, ctx = CASES[0]
     hc = w.host_case(_shape(n_q, n_kv, d, prefix), 313, context_lens=ctx, share=True)
     bt = hc.tables.block_tables
@@ -96,13 +99,16 @@ def test_non_member_table_takes_normal_path(pkv, orc):
     assert bt[s, 2] != hc.tables.prefix_phys[2]
     dc = DevCase(hc)
     got = _prefix_step(pkv, dc)
-    assert int(dc.err.item()) == 0
+    assert int(dc.err.item()) == pkv.PKV_DEVERR_PREFIX
+    assert np.isnan(got[s]).all()
+    others = np.arange(len(ctx)) != s
+    assert np.isfinite(got[others]).all()
     want, rc, _, _ = oracle_step(orc, hc)
     assert rc == 0
-    print(f"non-member: row error {max_abs(got[s], want[s]):.2e}, all {max_abs(got, want):.2e}")
-    assert max_abs(got, want) <= TOL
+    print(f"mismatch: other rows vs oracle {max_abs(got[others], want[others]):.2e}")
+    assert max_abs(got[others], want[others]) <= TOL
     ref = gpu_step(pkv, DevCase(hc), fused=True)
-    assert max_abs(got, ref) <= 1e-5
+    assert max_abs(got[others], ref[others]) <= 1e-5
 
 
 def test_empty_prefix_is_decode_step(pkv):
@@ -236,3 +242,46 @@ def test_prefix_llama3_shape(pkv, orc):
     print(f"llama3 shape: vs pkv_decode_step {err_d:.2e}, {len(seqs)} oracle rows {worst:.2e}")
     assert err_d <= 1e-5
     assert worst <= TOL
+
+
+def test_prefix_step_in_graph(pkv):
+    """The call captured in a HIP graph (its second stream becomes a fork and
+    a join of the capture) and replayed with new inputs between replays:
+    every replay equals an eager call on the same state, bit for bit."""
+    import torch
+    n_q, n_kv, d, prefix, ctx = CASES[0]
+    hc = w.host_case(_shape(n_q, n_kv, d, prefix), 314, context_lens=ctx, share=True)
+    dc = DevCase(hc)
+    B = len(ctx)
+    pt = to_dev_i32(hc.tables.prefix_phys)
+    ws = torch.zeros(pkv.pkv_decode_prefix_workspace_bytes(B, n_q, n_kv, d, dc.max_ctx, len(pt), B),
+                     dtype=torch.uint8, device="cuda")
+    out_ref = torch.empty_like(dc.out)
+    assert pkv.pkv_decode_split_waves(B, n_q, n_kv, d, dc.max_ctx) > 0
+    # one eager call first: the library's second stream exists before capture
+    pkv.pkv_decode_step_prefix(out_ref, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt,
+                               dc.cl, hc.shape.scale, dc.max_ctx, pt, 0, B, workspace=ws,
+                               err_flag=dc.err)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.prepare_decode_step_prefix(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool,
+                                       dc.bt, dc.cl, hc.shape.scale, dc.max_ctx, pt, 0, B,
+                                       workspace=ws, err_flag=dc.err)()
+    rng = w.rng(315, 0)
+    for rep in range(4):
+        dc.q.copy_(to_dev_bf16(w.normal_bf16(rng, tuple(dc.q.shape))))
+        dc.k_new.copy_(to_dev_bf16(w.normal_bf16(rng, tuple(dc.k_new.shape))))
+        dc.v_new.copy_(to_dev_bf16(w.normal_bf16(rng, tuple(dc.v_new.shape))))
+        dc.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dc.out.cpu().numpy()
+        pkv.pkv_decode_step_prefix(out_ref, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt,
+                                   dc.cl, hc.shape.scale, dc.max_ctx, pt, 0, B, workspace=ws,
+                                   err_flag=dc.err)
+        torch.cuda.synchronize()
+        assert int(dc.err.item()) == 0
+        assert np.isfinite(got).all(), f"replay {rep}"
+        assert np.array_equal(got, out_ref.cpu().numpy()), f"replay {rep} differs from eager"
