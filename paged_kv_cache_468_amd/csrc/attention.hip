@@ -198,9 +198,12 @@ __device__ inline int prefix_skip(const DecodeArgs& a, int s, int ctx) {
 }
 
 // Tiles of sequence s in the partition kernel's split: its tiles after the
-// prefix (0 for an invalid context length).
+// prefix (0 for an invalid context length). PREFIX = false: a kernel that
+// never runs with a shared prefix (the verification pass).
+template <bool PREFIX = true>
 __device__ inline int unit_tiles(const DecodeArgs& a, int s, int ctx) {
   const int nt = seq_tiles(ctx, a.q_len, a.max_ctx);
+  if (!PREFIX) return nt;
   return nt > 0 ? nt - prefix_skip(a, s, ctx) : 0;
 }
 
@@ -220,24 +223,26 @@ __device__ inline int logical_workgroup(const DecodeArgs& a) {
   return (blockIdx.x % kXcds) * a.wg_per_xcd + blockIdx.x / kXcds;
 }
 
-// Sum over all sequences of seq_tiles (identical in every lane).
+// Sum over all sequences of unit_tiles (identical in every lane).
+template <bool PREFIX>
 __device__ inline int total_seq_tiles(const DecodeArgs& a, int lane) {
   int sum = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int i = base + lane;
-    sum += wave_sum(i < a.num_seqs ? unit_tiles(a, i, a.context_lens[i]) : 0);
+    sum += wave_sum(i < a.num_seqs ? unit_tiles<PREFIX>(a, i, a.context_lens[i]) : 0);
   }
   return sum;
 }
 
 // The sequence holding tile r (0 <= r < total) of the per-unit-row tile
 // order, and the number of tiles of the sequences before it.
+template <bool PREFIX>
 __device__ inline void locate_tile(const DecodeArgs& a, int lane, int r, int& s_out,
                                    int& before_out) {
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int i = base + lane;
-    const int n = i < a.num_seqs ? unit_tiles(a, i, a.context_lens[i]) : 0;
+    const int n = i < a.num_seqs ? unit_tiles<PREFIX>(a, i, a.context_lens[i]) : 0;
     const int incl = wave_inclusive_scan(n, lane) + carry;
     const uint64_t hit = __ballot(i < a.num_seqs && incl > r);
     if (hit) {
@@ -272,12 +277,13 @@ struct TileScan {
   int n[4];   // tiles of sequences lane, lane + 64, lane + 128, lane + 192
 };
 
+template <bool PREFIX>
 __device__ inline int tile_scan_total(const DecodeArgs& a, int lane, TileScan& ts) {
-  if (a.num_seqs > 256) return total_seq_tiles(a, lane);
+  if (a.num_seqs > 256) return total_seq_tiles<PREFIX>(a, lane);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = lane + 64 * k;
-    ts.n[k] = i < a.num_seqs ? unit_tiles(a, i, a.context_lens[i]) : 0;
+    ts.n[k] = i < a.num_seqs ? unit_tiles<PREFIX>(a, i, a.context_lens[i]) : 0;
   }
   int total = 0;
 #pragma unroll
@@ -285,10 +291,11 @@ __device__ inline int tile_scan_total(const DecodeArgs& a, int lane, TileScan& t
   return total;
 }
 
+template <bool PREFIX>
 __device__ inline void tile_scan_locate(const DecodeArgs& a, int lane, const TileScan& ts, int r,
                                         int& s_out, int& before_out) {
   if (a.num_seqs > 256) {
-    locate_tile(a, lane, r, s_out, before_out);
+    locate_tile<PREFIX>(a, lane, r, s_out, before_out);
     return;
   }
   int carry = 0;
@@ -570,6 +577,26 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
     }
   };
 
+  if constexpr (CAUSAL) {
+    // The verification pass (two row groups, two waves per SIMD): chunks of
+    // 64 tiles, two register sets, the next tile's loads in flight. The
+    // ring below keeps more values live, and at this kernel's register
+    // budget they spill (measured 3 % slower per call).
+    for (int cb = 0; cb < n; cb += 64) {
+      const int nb = min(64, n - cb);
+      const int my_id = lane < nb ? ids[cb + lane] : 0;
+      issue(__builtin_amdgcn_readlane(my_id, 0), 0);
+      int i = 0;
+      for (; i + 1 < nb; i += 2) {
+        issue(__builtin_amdgcn_readlane(my_id, i + 1), 1);
+        compute_tile(cb + i, 0, Flag<true>{});
+        if (i + 2 < nb) issue(__builtin_amdgcn_readlane(my_id, i + 2), 0);
+        compute_tile(cb + i + 1, 1, Flag<true>{});
+      }
+      if (i < nb) compute_tile(cb + i, 0, Flag<true>{});
+    }
+    return !bad;
+  }
   // The steady loop runs while every load it issues is inside the segment,
   // so its loads are unconditional and the compiler's waits on them stay
   // exact; the last (at most 2 NBUF - 2) tiles are computed after it.
@@ -697,7 +724,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
   if (w >= a.n_waves) return;
 
   TileScan ts;
-  const int per_row = tile_scan_total(a, lane, ts);   // tiles of one (head, group)
+  const int per_row = tile_scan_total<!CAUSAL>(a, lane, ts);   // tiles of one (head, group)
   const int n_hq = a.n_kv * a.n_qgroups;
   const int64_t total = (int64_t)n_hq * per_row;
   int64_t cur = total * w / a.n_waves;
@@ -710,7 +737,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     if (cur < total) {
       const int hq = (int)(cur / per_row);
       int s, before;
-      tile_scan_locate(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
+      tile_scan_locate<!CAUSAL>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
       if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
       const int u = hq * a.num_seqs + s;
       const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups,
@@ -731,14 +758,14 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
 
   int hq = (int)(cur / per_row);
   int s, before;
-  tile_scan_locate(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
+  tile_scan_locate<!CAUSAL>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
   if (s >= a.num_seqs) return;   // unreachable for consistent context lengths
   int pos = (int)(cur - (int64_t)hq * per_row) - before;   // tile within the unit
   int ctx = a.context_lens[s];
 
   while (true) {
-    const int nt = unit_tiles(a, s, ctx);
-    const int skip = prefix_skip(a, s, ctx);   // tiles before the unit's first
+    const int nt = unit_tiles<!CAUSAL>(a, s, ctx);
+    const int skip = CAUSAL ? 0 : prefix_skip(a, s, ctx);   // tiles before the unit's first
     const int tb = (int)min((int64_t)nt, pos + (end - cur));
     const int h = hq / a.n_qgroups;
     const int qg = hq % a.n_qgroups;
@@ -773,7 +800,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
         if (++hq >= n_hq) return;   // unreachable for consistent context lengths
       }
       ctx = a.context_lens[s];
-    } while (unit_tiles(a, s, ctx) == 0);
+    } while (unit_tiles<!CAUSAL>(a, s, ctx) == 0);
   }
 }
 
