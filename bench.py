@@ -78,16 +78,21 @@ class State:
     pass
 
 
+def members_first(cl, prefix_tokens):
+    """The batch order: sequences longer than the prefix first, each group
+    in its drawn order. With sharing those hold all of the prefix's blocks
+    (a shorter one copies the block it writes), so they are
+    pkv_decode_step_prefix's member range [0, count)."""
+    if not prefix_tokens:
+        return cl
+    return cl[np.argsort(cl <= prefix_tokens, kind="stable")]
+
+
 def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, fused=True,
                 prefix_kernel=False):
     """Block tables from the refcounted allocator, pools filled on the
     device, every layer's buffers, and pre-marshalled library calls."""
-    cl = w.context_lengths(shape, seed).astype(np.int32)
-    if shape.prefix_tokens:
-        # the sequences longer than the prefix first: with sharing they hold
-        # all of its blocks (the shorter ones copy the block they write), so
-        # they are pkv_decode_step_prefix's member range
-        cl = cl[np.argsort(cl <= shape.prefix_tokens, kind="stable")]
+    cl = members_first(w.context_lengths(shape, seed).astype(np.int32), shape.prefix_tokens)
     B = len(cl)
     L, n_q, n_kv, d = shape.n_layers, shape.n_q, shape.n_kv, shape.d
     final_ctx = cl + extra_tokens
