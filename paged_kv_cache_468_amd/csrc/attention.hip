@@ -64,12 +64,12 @@
 //            gives the same softmax, since it cancels between sum and
 //            accumulator; the merge kernel uses the same convention.
 //
-//   Shared prefix (pkv_decode_step_prefix): the prefix kernel serves the
-//   rows of all member sequences of a common prompt prefix from each prefix
-//   tile, 16 rows per read (the decode serves group rows), and leaves
-//   partials per row; the partition kernel's split counts only each
-//   member's tiles after the prefix. The two run side by side on two
-//   streams, and the merge kernel takes both lists.
+//   Shared prefix (pkv_decode_step_prefix): the prefix's tiles become
+//   prefix units, one per (KV head, 16 member rows), placed after every
+//   sequence's tiles in the split; a prefix unit serves the rows of several
+//   member sequences from each tile (the decode serves group rows), and a
+//   member's own unit covers only its tiles after the prefix. The merge
+//   kernel takes both partial lists.
 //
 //   Grid: workgroups of 4 waves; the workgroup index is remapped so that
 //   consecutive work (same KV head, neighbouring sequences) lands on the
@@ -132,17 +132,19 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e)
   // Shared prefix (pkv_decode_step_prefix): sequences pre_first ..
   // pre_first + pre_count - 1 whose last tile lies after the prefix read its
-  // pre_tiles tiles (blocks pre_table[0 .. pre_tiles - 1]) through the prefix
-  // kernel, which serves the rows of all of them from each tile and leaves
-  // pre_parts partials per row in pre_ml / pre_acc; the partition kernel
-  // covers only the tiles after the prefix. pre_tiles = 0: no prefix.
+  // pre_tiles tiles (blocks pre_table[0 .. pre_tiles - 1]) through prefix
+  // units: one per (KV head, 16 member rows), pre_tiles tiles each, placed
+  // after every sequence's tiles in the split. A prefix unit serves 16
+  // rows of several members from each tile, and its partials (16 rows per
+  // slot) go to pre_ml / pre_acc; pre_info holds each prefix unit's first
+  // slot and partial count. pre_tiles = 0: no prefix.
   const int32_t* pre_table;
   int pre_first, pre_count, pre_tiles;
   int pre_qgroups;   // 16-row groups per KV head: ceil(pre_count * group / 16)
-  int pre_parts;     // tile ranges per (KV head, row group)
-  float* pre_ml;     // [n_kv * pre_qgroups * pre_parts][16][2]
-  float* pre_acc;    // [n_kv * pre_qgroups * pre_parts][16][D]
-  int32_t* pre_member;  // [pre_count]: 1 if the candidate's table starts with pre_table
+  int pre_units;     // n_kv * pre_qgroups
+  int32_t* pre_info; // [pre_units][2]
+  float* pre_ml;     // [slots][16][2]
+  float* pre_acc;    // [slots][16][D]
 };
 
 __device__ inline float wave_max_across_rows(float x) {
@@ -712,60 +714,148 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     l_run);
 }
 
+// A prefix unit's partial (16 rows per slot): reference max, sum and
+// accumulator of the rows this wave served, NaN after a bad block id.
+template <int D>
+__device__ inline void write_prefix_partial(const DecodeArgs& a, int lane, bool ok, int64_t slot,
+                                            bool valid, const f32x4_t* acc, float m_run,
+                                            float l_run) {
+  constexpr int VM = D / 16;
+  const int r = lane >> 4;
+  const float l_tot = wave_sum_across_rows(l_run);
+  if (!valid) return;
+  const float nan = __builtin_nanf("");
+  const int64_t row = slot * 16 + (lane & 15);
+  if (r == 0) {
+    a.pre_ml[2 * row] = ok ? m_run : nan;
+    a.pre_ml[2 * row + 1] = ok ? l_tot : nan;
+  }
+  float* o = a.pre_acc + row * D + 4 * r;
+#pragma unroll
+  for (int m = 0; m < VM; ++m) *(f32x4_t*)(o + 16 * m) = acc[m];
+}
+
+// The rows of prefix unit pu: (member i, head jj of KV head h's group),
+// row i * group + jj, rows qg * 16 .. qg * 16 + 15 of KV head h.
+__device__ inline Rows<1> prefix_rows(const DecodeArgs& a, int lane, int h, int qg) {
+  Rows<1> rw;
+  const int gr = qg * 16 + (lane & 15);
+  rw.valid[0] = gr < a.pre_count * a.group;
+  const int member = gr / a.group;
+  rw.index[0] = (int64_t)(a.pre_first + member) * a.n_q + h * a.group + (gr - member * a.group);
+  rw.lim[0] = 0x7fffffff;
+  return rw;
+}
+
+// Tiles [ta, tb) of prefix unit pu, through the prefix's own table: every
+// block is full, none is written, and the tiles are read by the other
+// prefix units of the KV head too (so through the caches).
+template <int D, int NBUF>
+__device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int ta, int tb,
+                                      int64_t slot) {
+  constexpr int VM = D / 16;
+  const int h = pu / a.pre_qgroups;
+  const Rows<1> rw = prefix_rows(a, lane, h, pu % a.pre_qgroups);
+  DecodeArgs pa = a;
+  pa.block_tables = a.pre_table;
+  pa.max_blocks = a.pre_tiles;
+  pa.k_new = nullptr;
+  pa.v_new = nullptr;
+  f32x4_t acc[1][VM];
+  float m_run[1], l_run[1];
+  const bool ok = process_segment<D, false, 1, false, NBUF>(pa, lane, 0, h, rw, a.pre_tiles * 16, ta,
+                                                            tb, false, acc, m_run, l_run);
+  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
+  write_prefix_partial<D>(a, lane, ok, slot, rw.valid[0], acc[0], m_run[0], l_run[0]);
+}
+
 // Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
-// (head, group, sequence, tile) order, T = all tiles of the launch. The
-// wave holding a unit's first tile records, for the merge kernel, the
-// unit's first partial slot and its number of partials (1: written here).
+// (head, group, sequence, tile) order, T = all tiles of the launch, and
+// after them (shared prefix) the prefix units' tiles in (KV head, row
+// group, tile) order. The wave holding a unit's first tile records, for
+// the merge kernel, the unit's first partial slot and its number of
+// partials (1: written here).
 template <int D, int NG, bool CAUSAL, int NBUF>
 __device__ inline void balanced_body(const DecodeArgs& a) {
   constexpr int VM = D / 16;
+  constexpr bool PREFIX = !CAUSAL;   // the verification pass never has one
   const int lane = threadIdx.x & 63;
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
   if (w >= a.n_waves) return;
 
   TileScan ts;
-  const int per_row = tile_scan_total<!CAUSAL>(a, lane, ts);   // tiles of one (head, group)
+  const int per_row = tile_scan_total<PREFIX>(a, lane, ts);   // tiles of one (head, group)
   const int n_hq = a.n_kv * a.n_qgroups;
-  const int64_t total = (int64_t)n_hq * per_row;
+  const int64_t t_seq = (int64_t)n_hq * per_row;
+  const int64_t total = t_seq + (PREFIX ? (int64_t)a.pre_units * a.pre_tiles : 0);
   int64_t cur = total * w / a.n_waves;
   const int64_t end = total * (w + 1) / a.n_waves;
+
+  // Prefix segments from tile c (at or after t_seq) up to end.
+  auto prefix_walk = [&](int64_t c) {
+    int pu = (int)((c - t_seq) / a.pre_tiles);
+    int pos = (int)((c - t_seq) - (int64_t)pu * a.pre_tiles);
+    while (c < end) {
+      const int tb = (int)min((int64_t)a.pre_tiles, pos + (end - c));
+      if (pos == 0 && lane == 0) {
+        int w0, w1;
+        waves_of_range(c, c + a.pre_tiles, total, a.n_waves, w0, w1);
+        a.pre_info[2 * pu] = w0 + pu;
+        a.pre_info[2 * pu + 1] = w1 - w0 + 1;
+      }
+      prefix_segment<D, NBUF>(a, lane, pu, pos, tb, (int64_t)w + pu);
+      c += tb - pos;
+      pos = 0;
+      ++pu;
+    }
+  };
+
   if (cur >= end) {
     // An empty range (fewer tiles than waves). If it sits strictly inside a
     // unit (after the unit's first tile), the merge of that unit counts
     // this wave: leave a neutral partial (weight 2^-inf, sum 0, accumulator
     // 0) in its slot. At a unit's first tile it belongs to no unit.
-    if (cur < total) {
+    f32x4_t zero[NG][VM];
+    float m0[NG], l0[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int m = 0; m < VM; ++m) zero[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m0[g] = -__builtin_inff();
+      l0[g] = 0.f;
+    }
+    if (cur < t_seq) {
       const int hq = (int)(cur / per_row);
       int s, before;
-      tile_scan_locate<!CAUSAL>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
+      tile_scan_locate<PREFIX>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
       if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
       const int u = hq * a.num_seqs + s;
       const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups,
                                               a.context_lens[s]);
-      f32x4_t zero[NG][VM];
-      float m0[NG], l0[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-#pragma unroll
-        for (int m = 0; m < VM; ++m) zero[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        m0[g] = -__builtin_inff();
-        l0[g] = 0.f;
-      }
       finish_rows<D, NG>(a, lane, true, false, (int64_t)w + u, rw, zero, m0, l0);
+    } else if (PREFIX && cur < total) {
+      const int pu = (int)((cur - t_seq) / a.pre_tiles);
+      if (cur - t_seq == (int64_t)pu * a.pre_tiles) return;
+      const Rows<1> rw = prefix_rows(a, lane, pu / a.pre_qgroups, pu % a.pre_qgroups);
+      write_prefix_partial<D>(a, lane, true, (int64_t)w + pu, rw.valid[0], zero[0], m0[0], l0[0]);
     }
+    return;
+  }
+  if (PREFIX && cur >= t_seq) {
+    prefix_walk(cur);
     return;
   }
 
   int hq = (int)(cur / per_row);
   int s, before;
-  tile_scan_locate<!CAUSAL>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
+  tile_scan_locate<PREFIX>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
   if (s >= a.num_seqs) return;   // unreachable for consistent context lengths
   int pos = (int)(cur - (int64_t)hq * per_row) - before;   // tile within the unit
   int ctx = a.context_lens[s];
 
   while (true) {
-    const int nt = unit_tiles<!CAUSAL>(a, s, ctx);
-    const int skip = CAUSAL ? 0 : prefix_skip(a, s, ctx);   // tiles before the unit's first
+    const int nt = unit_tiles<PREFIX>(a, s, ctx);
+    const int skip = PREFIX ? prefix_skip(a, s, ctx) : 0;   // tiles before the unit's first
     const int tb = (int)min((int64_t)nt, pos + (end - cur));
     const int h = hq / a.n_qgroups;
     const int qg = hq % a.n_qgroups;
@@ -781,8 +871,8 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, h, qg, ctx);
     f32x4_t acc[NG][VM];
     float m_run[NG], l_run[NG];
-    // a member reading the prefix through the prefix kernel reads its own
-    // tiles once: streamed
+    // a member reading the shared prefix through the prefix units reads
+    // its own tiles once: streamed
     const bool ok =
         skip == 0 && shares_first_block(a, s)
             ? process_segment<D, false, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
@@ -792,15 +882,19 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
     cur += tb - pos;
     if (cur >= end) break;
-    // next unit with work: following sequence, or the next (head, group)
+    // next unit with work: following sequence, or the next (head, group);
+    // after the last, the prefix units
     pos = 0;
     do {
       if (++s == a.num_seqs) {
         s = 0;
-        if (++hq >= n_hq) return;   // unreachable for consistent context lengths
+        if (++hq >= n_hq) {
+          if (PREFIX && a.pre_units > 0) prefix_walk(t_seq);
+          return;
+        }
       }
       ctx = a.context_lens[s];
-    } while (unit_tiles<!CAUSAL>(a, s, ctx) == 0);
+    } while (unit_tiles<PREFIX>(a, s, ctx) == 0);
   }
 }
 
@@ -818,76 +912,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
 template <int D, int NG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_verify_kernel(DecodeArgs a) {
   balanced_body<D, NG, true, kRing>(a);
-}
-
-// Shared prefix: the tiles every member sequence reads from the same
-// blocks, computed once for all of them. Candidates are the sequences
-// pre_first .. pre_first + pre_count - 1; this kernel also records which of
-// them hold the prefix's blocks as the start of their tables, for the merge
-// to check. It runs beside the partition kernel (another stream): neither
-// reads what the other writes. The query rows of KV head h are
-// the pairs (member i, head jj of h's group), row i * group + jj, in groups
-// of 16; one wave per (KV head, row group, part) takes part p of the
-// prefix's tiles, serves its 16 rows from each tile (the decode serves
-// group rows) and leaves a partial (reference max, sum, accumulator) per
-// row. Waves are ordered row group fastest, so the waves reading one tile
-// range run on one XCD and share its L2. Members whose context ends inside
-// the prefix get rows here too; the merge ignores them.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_prefix_kernel(DecodeArgs a) {
-  constexpr int VM = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int wid = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
-  // Membership: candidate m is a member if its first pre_tiles table
-  // entries are the prefix's blocks (wave m, m + all waves, ... checks it).
-  const int all_waves = gridDim.x * kWaves;
-  for (int m = wid; m < a.pre_count; m += all_waves) {
-    const int32_t* row = a.block_tables + (int64_t)(a.pre_first + m) * a.max_blocks;
-    bool same = true;
-    for (int t = lane; t < a.pre_tiles; t += 64) same = same && row[t] == a.pre_table[t];
-    const bool member = __ballot(!same) == 0;
-    if (lane == 0) a.pre_member[m] = member ? 1 : 0;
-  }
-  if (wid >= a.n_kv * a.pre_qgroups * a.pre_parts) return;
-  const int qg = wid % a.pre_qgroups;
-  const int p = (wid / a.pre_qgroups) % a.pre_parts;
-  const int h = wid / (a.pre_qgroups * a.pre_parts);
-  const int tpp = (a.pre_tiles + a.pre_parts - 1) / a.pre_parts;
-  const int ta = p * tpp;
-  const int tb = min(ta + tpp, a.pre_tiles);
-  if (ta >= tb) return;   // the merge reads only parts that hold tiles
-
-  const int c = lane & 15;
-  const int r = lane >> 4;
-  const int gr = qg * 16 + c;
-  Rows<1> rw;
-  rw.valid[0] = gr < a.pre_count * a.group;
-  const int member = gr / a.group;
-  rw.index[0] = (int64_t)(a.pre_first + member) * a.n_q + h * a.group + (gr - member * a.group);
-  rw.lim[0] = 0x7fffffff;
-  f32x4_t acc[1][VM];
-  float m_run[1], l_run[1];
-  // the prefix's tiles through its own table (row 0 of pre_table): every
-  // block is full, none is written
-  DecodeArgs pa = a;
-  pa.block_tables = a.pre_table;
-  pa.max_blocks = a.pre_tiles;
-  pa.k_new = nullptr;
-  pa.v_new = nullptr;
-  const bool ok = process_segment<D, false, 1, false, kRing>(pa, lane, 0, h, rw, a.pre_tiles * 16, ta,
-                                                         tb, false, acc, m_run, l_run);
-  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
-  const float l_tot = wave_sum_across_rows(l_run[0]);
-  if (!rw.valid[0]) return;
-  const float nan = __builtin_nanf("");
-  const int64_t row = ((int64_t)(h * a.pre_qgroups + qg) * a.pre_parts + p) * 16 + c;
-  if (r == 0) {
-    a.pre_ml[2 * row] = ok ? m_run[0] : nan;
-    a.pre_ml[2 * row + 1] = ok ? l_tot : nan;
-  }
-  float* w = a.pre_acc + row * D + 4 * r;
-#pragma unroll
-  for (int m = 0; m < VM; ++m) *(f32x4_t*)(w + 16 * m) = acc[0][m];
 }
 
 // Chunked prefill with the K/V tiles staged in LDS. A workgroup of
@@ -1180,8 +1204,8 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 // sums l_p and accumulators a_p of the row's partials (all relative to
 // 2^(x - m_p)): M = max_p m_p, L = sum_p l_p 2^(m_p - M) and
 // out = (sum_p 2^(m_p - M) a_p) / L, summed in partial order. The partials
-// are the unit's slots of the partition kernel, then (a member of a shared
-// prefix that reads it) the prefix kernel's parts of the row. Lane p holds
+// are the unit's slots, then (a member that reads the shared prefix) the
+// slots of the prefix unit holding the row. Lane p holds
 // partial p's weight; lane i owns dims PER*i .. PER*i + PER - 1; the
 // accumulators are loaded eight partials at a time. A NaN maximum (a bad
 // block id) makes the row NaN; a sequence with an invalid context length
@@ -1232,22 +1256,26 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     first = info.x;
     n = info.y;
   }
-  // the prefix kernel's parts of this row (decode rows: i = 0, head gr)
+  // the prefix unit's partials of this row (decode rows: i = 0, head gr)
   int np = 0;
   int64_t pre_row = 0;
   if (prefix_skip(a, s, ctx) > 0) {
-    // the partition kernel skipped the prefix's tiles of this sequence: its
-    // table must start with the prefix's blocks, else the row is NaN
-    if (a.pre_member[s - a.pre_first] == 0) {
+    // the partition kernel took this sequence's prefix tiles from the
+    // prefix's table: its own table must start with the same blocks, else
+    // the row is NaN
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+    bool same = true;
+    for (int t = lane; t < a.pre_tiles; t += 64) same = same && row[t] == a.pre_table[t];
+    if (__ballot(!same) != 0) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) o[e] = nan;
       if (hq == 0 && gr == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_PREFIX);
       return;
     }
-    const int tpp = (a.pre_tiles + a.pre_parts - 1) / a.pre_parts;
-    np = (a.pre_tiles + tpp - 1) / tpp;
     const int pr = (s - a.pre_first) * a.group + gr;
-    pre_row = (int64_t)(h * a.pre_qgroups + pr / 16) * a.pre_parts * 16 + (pr % 16);
+    const int2 pinfo = *(const int2*)(a.pre_info + 2 * (h * a.pre_qgroups + pr / 16));
+    np = pinfo.y;
+    pre_row = (int64_t)pinfo.x * 16 + (pr % 16);
   }
   const int tot = n + np;
   if (tot <= 1) return;   // written directly by the partition kernel
@@ -1434,33 +1462,19 @@ static size_t workspace_bytes(const Geom& g, int d, int max_ctx, int part) {
   return (part > 0 ? 0 : unit_info_bytes(g)) + slots_bytes;
 }
 
-// Shared prefix: 16-row groups per KV head, and tile ranges per group, so
-// that the prefix kernel launches about kPrefixWaves waves of at least
-// kPrefixMinTiles tiles each.
-constexpr int kPrefixWaves = 1024;   // one per SIMD; per LLaMA-3-8B call 3 % faster than 2,048, 5 % than 512
-constexpr int kPrefixMinTiles = 8;
-
-struct PrefixGeom {
-  int qgroups, parts;
-  int64_t rows() const { return (int64_t)qgroups * parts * 16; }   // per KV head
-};
-
-static PrefixGeom prefix_geom(int n_kv, int group, int count, int blocks) {
-  PrefixGeom pg{0, 0};
-  if (count <= 0 || blocks <= 0) return pg;
-  pg.qgroups = (int)(((int64_t)count * group + 15) / 16);
-  const int64_t units = (int64_t)n_kv * pg.qgroups;
-  int64_t parts = (kPrefixWaves + units - 1) / units;
-  const int64_t most = (blocks + kPrefixMinTiles - 1) / kPrefixMinTiles;
-  if (parts > most) parts = most;
-  pg.parts = (int)(parts < 1 ? 1 : parts);
-  return pg;
+// Shared prefix: 16-row groups of member rows per KV head, and the bytes
+// after the decode's workspace (rounded up to 256 bytes): each prefix
+// unit's first slot and count, then its partial slots, 16 rows each. A
+// prefix unit's slot is wave + unit, as for the decode's units, so there
+// are at most (waves + units) slots.
+static int prefix_qgroups(int group, int count) {
+  return (int)(((int64_t)count * group + 15) / 16);
 }
 
-// Bytes of the prefix kernel's partials and membership flags, after the
-// decode's workspace (which is rounded up to 256 bytes first).
-static size_t prefix_bytes(const PrefixGeom& pg, int n_kv, int d, int count) {
-  return (size_t)(n_kv * pg.rows()) * (2 + d) * sizeof(float) + (size_t)count * sizeof(int32_t);
+static size_t prefix_bytes(const Geom& g, int d, int max_ctx, int count) {
+  const int64_t units = (int64_t)g.n_kv * prefix_qgroups(g.n_q / g.n_kv, count);
+  const int64_t slots = split_wave_cap(g, max_ctx) + units;
+  return (size_t)((units * 8 + 255) / 256 * 256) + (size_t)slots * 16 * (2 + d) * sizeof(float);
 }
 
 }  // namespace pkv
@@ -1549,9 +1563,9 @@ static int prepare(DecodeArgs& a, int& head_dim_out, const Geom& g, float* out, 
   a.scale_log2 = scale * kLog2e;
   a.pre_table = nullptr;
   a.pre_first = a.pre_count = a.pre_tiles = 0;
-  a.pre_qgroups = a.pre_parts = 0;
+  a.pre_qgroups = a.pre_units = 0;
+  a.pre_info = nullptr;
   a.pre_ml = a.pre_acc = nullptr;
-  a.pre_member = nullptr;
   head_dim_out = head_dim;
 
   const int64_t units = g.units();
@@ -1723,31 +1737,6 @@ extern "C" int pkv_decode_step(PKV_STEP_PARAMS) {
   return launch_merge(a, d, (hipStream_t)stream);
 }
 
-// A second stream (default priority) and two events per host thread and
-// device, created on first use and kept until the process ends: the shared
-// prefix's kernel runs there beside the partition kernel.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-static SideStream* side_stream() {
-  thread_local SideStream per_device[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& s = per_device[dev];
-  if (!s.stream) {
-    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
-      hipStreamDestroy(s.stream);
-      s.stream = nullptr;
-      return nullptr;
-    }
-  }
-  return &s;
-}
-
 static bool valid_prefix_args(int32_t num_seqs, int32_t max_blocks_per_seq,
                               const int32_t* prefix_table, int32_t prefix_blocks,
                               int32_t prefix_first_seq, int32_t prefix_num_seqs) {
@@ -1767,9 +1756,8 @@ extern "C" size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t n_
   const size_t base =
       pkv_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len, 0);
   if (base == 0 || prefix_blocks <= 0 || prefix_num_seqs <= 0) return base;
-  const PrefixGeom pg =
-      prefix_geom(n_kv_heads, n_q_heads / n_kv_heads, prefix_num_seqs, prefix_blocks);
-  return round256(base) + prefix_bytes(pg, n_kv_heads, head_dim, prefix_num_seqs);
+  return round256(base) + prefix_bytes(decode_geom(num_seqs, n_q_heads, n_kv_heads), head_dim,
+                                       max_context_len, prefix_num_seqs);
 }
 
 extern "C" int pkv_decode_step_prefix(float* out, const void* q, const void* k_new,
@@ -1793,46 +1781,27 @@ extern "C" int pkv_decode_step_prefix(float* out, const void* q, const void* k_n
   if (!k_new || !v_new) return PKV_EINVAL;
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
-  hipStream_t st = (hipStream_t)stream;
   if (prefix_blocks > 0 && prefix_num_seqs > 0) {
-    const PrefixGeom pg = prefix_geom(n_kv_heads, a.group, prefix_num_seqs, prefix_blocks);
-    const int64_t waves = (int64_t)n_kv_heads * pg.qgroups * pg.parts;
-    if (waves > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
-    const size_t base = round256(workspace_bytes(decode_geom(num_seqs, n_q_heads, n_kv_heads),
-                                                 head_dim, max_context_len, 0));
-    if (workspace_bytes_given < base + prefix_bytes(pg, n_kv_heads, head_dim, prefix_num_seqs))
+    const Geom g = decode_geom(num_seqs, n_q_heads, n_kv_heads);
+    const size_t base = round256(workspace_bytes(g, head_dim, max_context_len, 0));
+    if (workspace_bytes_given < base + prefix_bytes(g, head_dim, max_context_len, prefix_num_seqs))
       return PKV_EWORKSPACE;
     a.pre_table = prefix_table;
     a.pre_first = prefix_first_seq;
     a.pre_count = prefix_num_seqs;
     a.pre_tiles = prefix_blocks;
-    a.pre_qgroups = pg.qgroups;
-    a.pre_parts = pg.parts;
-    a.pre_ml = (float*)((char*)workspace + base);
-    a.pre_acc = a.pre_ml + 2 * (int64_t)n_kv_heads * pg.rows();
-    a.pre_member = (int32_t*)(a.pre_acc + (int64_t)head_dim * n_kv_heads * pg.rows());
-    DecodeArgs pa = a;
-    const int64_t wgs = (waves + kWaves - 1) / kWaves;
-    pa.wg_per_xcd = (int)((wgs + kXcds - 1) / kXcds);
-    const unsigned grid = (unsigned)pa.wg_per_xcd * kXcds;
-    // The prefix kernel on this thread's side stream, beside the partition
-    // kernel: forked after the caller's earlier work, joined before the
-    // merge (also inside a stream capture, as a fork and a join).
-    SideStream* side = side_stream();
-    if (!side) return PKV_EHIP;
-    if (hipEventRecord(side->fork, st) != hipSuccess ||
-        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
-      return PKV_EHIP;
-    if (d == 128)
-      hipLaunchKernelGGL(paged_attn_prefix_kernel<128>, dim3(grid), dim3(256), 0, side->stream, pa);
-    else
-      hipLaunchKernelGGL(paged_attn_prefix_kernel<64>, dim3(grid), dim3(256), 0, side->stream, pa);
-    if (hipGetLastError() != hipSuccess) return PKV_EHIP;
-    if (hipEventRecord(side->join, side->stream) != hipSuccess) return PKV_EHIP;
-    const int prc = launch_partition(a, d, st);
-    if (hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return PKV_EHIP;
-    return prc != PKV_OK ? prc : launch_merge(a, d, st);
+    a.pre_qgroups = prefix_qgroups(a.group, prefix_num_seqs);
+    const int64_t units = (int64_t)n_kv_heads * a.pre_qgroups;
+    // tile indices of the split (sequences' and prefix units') fit 62 bits;
+    // the unit and slot counts fit 32
+    if (units > (int64_t)INT32_MAX / 64) return PKV_EINVAL;
+    a.pre_units = (int)units;
+    a.pre_info = (int32_t*)((char*)workspace + base);
+    a.pre_ml = (float*)((char*)workspace + base + (units * 8 + 255) / 256 * 256);
+    const int64_t slots = split_wave_cap(g, max_context_len) + units;
+    a.pre_acc = a.pre_ml + 2 * 16 * slots;
   }
+  const hipStream_t st = (hipStream_t)stream;
   const int prc = launch_partition(a, d, st);
   return prc != PKV_OK ? prc : launch_merge(a, d, st);
 }

@@ -4,8 +4,8 @@ sequence by the prefix kernel, the partition kernel covers the rest, and the
 merge kernel combines both.
 
 The bar: outputs within 1e-3 of the oracle (which walks every sequence's own
-table), within 1e-5 of pkv_decode_step on the same inputs (only the order of
-the softmax merge differs), and the pools bitwise equal to pkv_decode_step's
+table), within 2.5e-5 of pkv_decode_step on the same inputs (only the order
+of the fp32 sums differs), and the pools bitwise equal to pkv_decode_step's
 (the append is the same). Members whose context ends inside the prefix,
 sequences outside the member range, head groups above 16 and both head
 sizes are covered; an empty prefix is pkv_decode_step bit for bit; a member
@@ -21,6 +21,11 @@ from gpu_util import (TOL, DevCase, gpu_step, max_abs, oracle_step, to_dev_bf16,
                       to_host_u16)
 
 pytestmark = pytest.mark.gpu
+
+# GPU against GPU in another summation order: each fp32 result lies within
+# about 1e-5 of the exact value (up to 9.3e-6 against the float64 oracle in
+# these cases), so the two differ by at most about twice that.
+CROSS = 2.5e-5
 
 
 @pytest.fixture(scope="module")
@@ -79,7 +84,7 @@ def test_prefix_step_parity(pkv, orc, case, members):
     print(f"case {CASES[case][:4]} members {members}: vs oracle {err_o:.2e}, "
           f"vs pkv_decode_step {err_d:.2e}")
     assert err_o <= TOL
-    assert err_d <= 1e-5
+    assert err_d <= CROSS
     assert np.array_equal(to_host_u16(a.k_pool), to_host_u16(b.k_pool))
     assert np.array_equal(to_host_u16(a.v_pool), to_host_u16(b.v_pool))
     assert np.array_equal(to_host_u16(a.k_pool), k_ref)
@@ -108,7 +113,7 @@ def test_member_table_mismatch_flagged(pkv, orc):
     print(f"mismatch: other rows vs oracle {max_abs(got[others], want[others]):.2e}")
     assert max_abs(got[others], want[others]) <= TOL
     ref = gpu_step(pkv, DevCase(hc), fused=True)
-    assert max_abs(got[others], ref[others]) <= 1e-5
+    assert max_abs(got[others], ref[others]) <= CROSS
 
 
 def test_empty_prefix_is_decode_step(pkv):
@@ -175,12 +180,12 @@ def test_prefix_bad_block_id(pkv):
     assert np.array_equal(nan_rows, holders)
     assert np.array_equal(np.isnan(ref).all(axis=(1, 2)), holders)
     assert np.isfinite(got[~holders]).all()
-    assert max_abs(got[~holders], ref[~holders]) <= 1e-5
+    assert max_abs(got[~holders], ref[~holders]) <= CROSS
 
 
 def test_prefix_llama3_shape(pkv, orc):
     """The LLaMA-3-8B layer at full size (64 sequences, contexts U[1024, 8192],
-    2,048-token prefix): within 1e-5 of pkv_decode_step everywhere, pools
+    2,048-token prefix): within CROSS of pkv_decode_step everywhere, pools
     equal, and sampled rows within 1e-3 of the oracle."""
     import torch
     cfg = w.CONFIGS[4]
@@ -240,7 +245,7 @@ def test_prefix_llama3_shape(pkv, orc):
         assert rc == 0
         worst = max(worst, max_abs(got[s, j], want))
     print(f"llama3 shape: vs pkv_decode_step {err_d:.2e}, {len(seqs)} oracle rows {worst:.2e}")
-    assert err_d <= 1e-5
+    assert err_d <= CROSS
     assert worst <= TOL
 
 
