@@ -304,32 +304,28 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
  * Sequences prefix_first_seq .. prefix_first_seq + prefix_num_seqs - 1 are
  * the members. A member whose context extends past the prefix
  * (context_lens[s] > 16 * prefix_blocks) must hold prefix_table's ids as
- * its first prefix_blocks table entries; its first prefix_blocks tiles are
- * read through the prefix kernel, which serves the query rows of all
- * members from each prefix tile (16 rows per K/V read where the decode
- * serves n_q/n_kv), and the partition kernel covers only its later tiles.
- * The device checks the claim at every call: a member whose table differs
- * there gets NaN rows and sets PKV_DEVERR_PREFIX (never a wrong finite
- * result). A member whose context ends inside the prefix, and every
- * sequence outside the range, runs as in pkv_decode_step. The prefix
- * kernel runs on a second stream of the library's (one per host thread and
- * device, default priority, created on first use), forked from and joined
- * back into `stream`, so it overlaps the partition kernel; inside a stream
- * capture this records a fork and a join.
+ * its first prefix_blocks table entries. The partition kernel then reads
+ * the prefix's tiles once for all members, as prefix units of its balanced
+ * split that serve 32 member rows per K/V tile (the decode serves
+ * n_q/n_kv), and each member's own unit covers only its later tiles; the
+ * merge kernel combines both. The merge checks every such member's table
+ * at each call: one whose table differs there gets NaN rows and sets
+ * PKV_DEVERR_PREFIX (never a wrong finite result). A member whose context
+ * ends inside the prefix, and every sequence outside the range, runs as in
+ * pkv_decode_step.
  *   prefix_table    : device int32 [prefix_blocks], the prefix's block ids
  *   prefix_blocks   : whole 16-token blocks of the prefix, in
  *                     [0, max_blocks_per_seq]; 0 (or prefix_num_seqs = 0)
  *                     is pkv_decode_step with the balanced split
  *   workspace       : at least pkv_decode_prefix_workspace_bytes(...) bytes
- *                     (the decode's workspace, then the prefix kernel's
- *                     partials and one check flag per member); no
- *                     initialisation needed
- * Other arguments as for pkv_decode_step with partition_tokens = 0. Three
- * launches: the prefix kernel (second stream), the partition kernel with
- * the append, then the merge kernel (both on `stream`). Host-checked errors: PKV_EINVAL for a member range
- * outside [0, num_seqs), a negative count or prefix_blocks >
- * max_blocks_per_seq, a null prefix_table with a non-empty prefix, and
- * everything pkv_decode_step checks; PKV_EWORKSPACE. Device errors as for
+ *                     (the decode's workspace, then the prefix units'
+ *                     bookkeeping and partials); no initialisation needed
+ * Other arguments as for pkv_decode_step with partition_tokens = 0. Two
+ * launches on `stream`: the partition kernel (prefix units, the members'
+ * own tiles and the append), then the merge kernel. Host-checked errors:
+ * PKV_EINVAL for a member range outside [0, num_seqs), a negative count or
+ * prefix_blocks > max_blocks_per_seq, a null prefix_table with a non-empty
+ * prefix, and everything pkv_decode_step checks; PKV_EWORKSPACE. Device errors as for
  * pkv_decode_step; an id in prefix_table outside the pool sets
  * PKV_DEVERR_BLOCK_ID and makes the rows of every member that reads the
  * prefix NaN (never read out of bounds). */

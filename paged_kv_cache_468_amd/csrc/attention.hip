@@ -65,7 +65,7 @@
 //            accumulator; the merge kernel uses the same convention.
 //
 //   Shared prefix (pkv_decode_step_prefix): the prefix's tiles become
-//   prefix units, one per (KV head, 16 member rows), placed after every
+//   prefix units, one per (KV head, 32 member rows), placed after every
 //   sequence's tiles in the split; a prefix unit serves the rows of several
 //   member sequences from each tile (the decode serves group rows), and a
 //   member's own unit covers only its tiles after the prefix. The merge
@@ -101,6 +101,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // other kernels run two waves per SIMD and keep two.
 constexpr int kDecodeRing128 = 3;
 constexpr int kRing = 2;
+// Shared prefix: member rows served per prefix tile, in groups of 16.
+constexpr int kPrefixNG = 2;
+constexpr int kPrefixRows = 16 * kPrefixNG;
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
 struct DecodeArgs {
@@ -133,18 +136,18 @@ struct DecodeArgs {
   // Shared prefix (pkv_decode_step_prefix): sequences pre_first ..
   // pre_first + pre_count - 1 whose last tile lies after the prefix read its
   // pre_tiles tiles (blocks pre_table[0 .. pre_tiles - 1]) through prefix
-  // units: one per (KV head, 16 member rows), pre_tiles tiles each, placed
-  // after every sequence's tiles in the split. A prefix unit serves 16
-  // rows of several members from each tile, and its partials (16 rows per
+  // units: one per (KV head, 32 member rows), pre_tiles tiles each, placed
+  // after every sequence's tiles in the split. A prefix unit serves 32
+  // rows of several members from each tile, and its partials (32 rows per
   // slot) go to pre_ml / pre_acc; pre_info holds each prefix unit's first
   // slot and partial count. pre_tiles = 0: no prefix.
   const int32_t* pre_table;
   int pre_first, pre_count, pre_tiles;
-  int pre_qgroups;   // 16-row groups per KV head: ceil(pre_count * group / 16)
+  int pre_qgroups;   // row groups per KV head: ceil(pre_count * group / kPrefixRows)
   int pre_units;     // n_kv * pre_qgroups
   int32_t* pre_info; // [pre_units][2]
-  float* pre_ml;     // [slots][16][2]
-  float* pre_acc;    // [slots][16][D]
+  float* pre_ml;     // [slots][kPrefixRows][2]
+  float* pre_acc;    // [slots][kPrefixRows][D]
 };
 
 __device__ inline float wave_max_across_rows(float x) {
@@ -186,12 +189,12 @@ __device__ inline int seq_tiles(int ctx, int q_len, int max_ctx) {
   return (ctx >= q_len && ctx <= max_ctx) ? (ctx + 15) >> 4 : 0;
 }
 
-// Tiles of sequence s read through the shared prefix (the prefix kernel's
-// partials): all of them for a candidate whose last tile lies after the
-// prefix (such a candidate holds the prefix's blocks as its first table
-// entries; the prefix kernel checks that, and the merge turns a candidate
-// that does not into NaN rows), none otherwise (its context ends inside the
-// prefix, so the block it writes is not a prefix block).
+// Tiles of sequence s read through the shared prefix (the prefix units'
+// partials): all of them for a member whose last tile lies after the
+// prefix (such a member holds the prefix's blocks as its first table
+// entries; the merge checks that, and turns a member that does not into
+// NaN rows), none otherwise (its context ends inside the prefix, so the
+// block it writes is not a prefix block).
 __device__ inline int prefix_skip(const DecodeArgs& a, int s, int ctx) {
   return (a.pre_tiles > 0 && (unsigned)(s - a.pre_first) < (unsigned)a.pre_count &&
           ((ctx - 1) >> 4) >= a.pre_tiles)
@@ -714,18 +717,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     l_run);
 }
 
-// A prefix unit's partial (16 rows per slot): reference max, sum and
-// accumulator of the rows this wave served, NaN after a bad block id.
+// A prefix unit's partial (kPrefixRows rows per slot; row group g):
+// reference max, sum and accumulator of the rows this wave served, NaN
+// after a bad block id.
 template <int D>
 __device__ inline void write_prefix_partial(const DecodeArgs& a, int lane, bool ok, int64_t slot,
-                                            bool valid, const f32x4_t* acc, float m_run,
+                                            int g, bool valid, const f32x4_t* acc, float m_run,
                                             float l_run) {
   constexpr int VM = D / 16;
   const int r = lane >> 4;
   const float l_tot = wave_sum_across_rows(l_run);
   if (!valid) return;
   const float nan = __builtin_nanf("");
-  const int64_t row = slot * 16 + (lane & 15);
+  const int64_t row = slot * kPrefixRows + 16 * g + (lane & 15);
   if (r == 0) {
     a.pre_ml[2 * row] = ok ? m_run : nan;
     a.pre_ml[2 * row + 1] = ok ? l_tot : nan;
@@ -736,14 +740,18 @@ __device__ inline void write_prefix_partial(const DecodeArgs& a, int lane, bool 
 }
 
 // The rows of prefix unit pu: (member i, head jj of KV head h's group),
-// row i * group + jj, rows qg * 16 .. qg * 16 + 15 of KV head h.
-__device__ inline Rows<1> prefix_rows(const DecodeArgs& a, int lane, int h, int qg) {
-  Rows<1> rw;
-  const int gr = qg * 16 + (lane & 15);
-  rw.valid[0] = gr < a.pre_count * a.group;
-  const int member = gr / a.group;
-  rw.index[0] = (int64_t)(a.pre_first + member) * a.n_q + h * a.group + (gr - member * a.group);
-  rw.lim[0] = 0x7fffffff;
+// row i * group + jj, rows qg * 32 .. qg * 32 + 31 of KV head h (two
+// groups of 16).
+__device__ inline Rows<kPrefixNG> prefix_rows(const DecodeArgs& a, int lane, int h, int qg) {
+  Rows<kPrefixNG> rw;
+#pragma unroll
+  for (int g = 0; g < kPrefixNG; ++g) {
+    const int gr = qg * kPrefixRows + 16 * g + (lane & 15);
+    rw.valid[g] = gr < a.pre_count * a.group;
+    const int member = gr / a.group;
+    rw.index[g] = (int64_t)(a.pre_first + member) * a.n_q + h * a.group + (gr - member * a.group);
+    rw.lim[g] = 0x7fffffff;
+  }
   return rw;
 }
 
@@ -755,18 +763,20 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
                                       int64_t slot) {
   constexpr int VM = D / 16;
   const int h = pu / a.pre_qgroups;
-  const Rows<1> rw = prefix_rows(a, lane, h, pu % a.pre_qgroups);
+  const Rows<kPrefixNG> rw = prefix_rows(a, lane, h, pu % a.pre_qgroups);
   DecodeArgs pa = a;
   pa.block_tables = a.pre_table;
   pa.max_blocks = a.pre_tiles;
   pa.k_new = nullptr;
   pa.v_new = nullptr;
-  f32x4_t acc[1][VM];
-  float m_run[1], l_run[1];
-  const bool ok = process_segment<D, false, 1, false, NBUF>(pa, lane, 0, h, rw, a.pre_tiles * 16, ta,
-                                                            tb, false, acc, m_run, l_run);
+  f32x4_t acc[kPrefixNG][VM];
+  float m_run[kPrefixNG], l_run[kPrefixNG];
+  const bool ok = process_segment<D, false, kPrefixNG, false, NBUF>(
+      pa, lane, 0, h, rw, a.pre_tiles * 16, ta, tb, false, acc, m_run, l_run);
   if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
-  write_prefix_partial<D>(a, lane, ok, slot, rw.valid[0], acc[0], m_run[0], l_run[0]);
+#pragma unroll
+  for (int g = 0; g < kPrefixNG; ++g)
+    write_prefix_partial<D>(a, lane, ok, slot, g, rw.valid[g], acc[g], m_run[g], l_run[g]);
 }
 
 // Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
@@ -775,10 +785,9 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
 // group, tile) order. The wave holding a unit's first tile records, for
 // the merge kernel, the unit's first partial slot and its number of
 // partials (1: written here).
-template <int D, int NG, bool CAUSAL, int NBUF>
+template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX>
 __device__ inline void balanced_body(const DecodeArgs& a) {
   constexpr int VM = D / 16;
-  constexpr bool PREFIX = !CAUSAL;   // the verification pass never has one
   const int lane = threadIdx.x & 63;
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
   if (w >= a.n_waves) return;
@@ -836,8 +845,11 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     } else if (PREFIX && cur < total) {
       const int pu = (int)((cur - t_seq) / a.pre_tiles);
       if (cur - t_seq == (int64_t)pu * a.pre_tiles) return;
-      const Rows<1> rw = prefix_rows(a, lane, pu / a.pre_qgroups, pu % a.pre_qgroups);
-      write_prefix_partial<D>(a, lane, true, (int64_t)w + pu, rw.valid[0], zero[0], m0[0], l0[0]);
+      const Rows<kPrefixNG> rw = prefix_rows(a, lane, pu / a.pre_qgroups, pu % a.pre_qgroups);
+#pragma unroll
+      for (int g = 0; g < kPrefixNG; ++g)
+        write_prefix_partial<D>(a, lane, true, (int64_t)w + pu, g, rw.valid[g], zero[0], m0[0],
+                                l0[0]);
     }
     return;
   }
@@ -899,9 +911,11 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
 }
 
 // The decode step's kernel: one query row per head, the append fused in.
-template <int D>
+// PREFIX: the split also holds a shared prefix's units (compiled apart, so
+// the plain decode keeps its registers).
+template <int D, bool PREFIX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void paged_attn_balanced_kernel(DecodeArgs a) {
-  balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing>(a);
+  balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing, PREFIX>(a);
 }
 
 // The verification pass: q_len query tokens per sequence, causal among
@@ -911,7 +925,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
 // schedules the loads of the next tile further ahead.
 template <int D, int NG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_verify_kernel(DecodeArgs a) {
-  balanced_body<D, NG, true, kRing>(a);
+  balanced_body<D, NG, true, kRing, false>(a);
 }
 
 // Chunked prefill with the K/V tiles staged in LDS. A workgroup of
@@ -1273,9 +1287,9 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
       return;
     }
     const int pr = (s - a.pre_first) * a.group + gr;
-    const int2 pinfo = *(const int2*)(a.pre_info + 2 * (h * a.pre_qgroups + pr / 16));
+    const int2 pinfo = *(const int2*)(a.pre_info + 2 * (h * a.pre_qgroups + pr / kPrefixRows));
     np = pinfo.y;
-    pre_row = (int64_t)pinfo.x * 16 + (pr % 16);
+    pre_row = (int64_t)pinfo.x * kPrefixRows + (pr % kPrefixRows);
   }
   const int tot = n + np;
   if (tot <= 1) return;   // written directly by the partition kernel
@@ -1283,11 +1297,11 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   // partial p: the unit's slot first + p, then prefix part p - n
   auto ml_of = [&](int pp) -> const float* {
     return pp < n ? a.ws_ml + ((first + pp) * a.rows + g_in_slot) * 2
-                  : a.pre_ml + (pre_row + (int64_t)(pp - n) * 16) * 2;
+                  : a.pre_ml + (pre_row + (int64_t)(pp - n) * kPrefixRows) * 2;
   };
   auto acc_of = [&](int pp) -> const float* {
     return (pp < n ? a.ws_acc + ((first + pp) * a.rows + g_in_slot) * D
-                   : a.pre_acc + (pre_row + (int64_t)(pp - n) * 16) * D) +
+                   : a.pre_acc + (pre_row + (int64_t)(pp - n) * kPrefixRows) * D) +
            lane * PER;
   };
 
@@ -1409,8 +1423,10 @@ static int occupancy_blocks(K kernel) {
 
 static int kernel_blocks_per_cu(const Geom& g, int head_dim) {
   if (!g.causal)
-    return head_dim == 128 ? occupancy_blocks(paged_attn_balanced_kernel<128>)
-                           : occupancy_blocks(paged_attn_balanced_kernel<64>);
+    // both instantiations hold the same waves per SIMD (one at head_dim
+    // 128, two at 64)
+    return head_dim == 128 ? occupancy_blocks(paged_attn_balanced_kernel<128, false>)
+                           : occupancy_blocks(paged_attn_balanced_kernel<64, false>);
   if (g.ng == 1)
     return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 1>)
                            : occupancy_blocks(paged_attn_verify_kernel<64, 1>);
@@ -1468,13 +1484,14 @@ static size_t workspace_bytes(const Geom& g, int d, int max_ctx, int part) {
 // prefix unit's slot is wave + unit, as for the decode's units, so there
 // are at most (waves + units) slots.
 static int prefix_qgroups(int group, int count) {
-  return (int)(((int64_t)count * group + 15) / 16);
+  return (int)(((int64_t)count * group + kPrefixRows - 1) / kPrefixRows);
 }
 
 static size_t prefix_bytes(const Geom& g, int d, int max_ctx, int count) {
   const int64_t units = (int64_t)g.n_kv * prefix_qgroups(g.n_q / g.n_kv, count);
   const int64_t slots = split_wave_cap(g, max_ctx) + units;
-  return (size_t)((units * 8 + 255) / 256 * 256) + (size_t)slots * 16 * (2 + d) * sizeof(float);
+  return (size_t)((units * 8 + 255) / 256 * 256) +
+         (size_t)slots * kPrefixRows * (2 + d) * sizeof(float);
 }
 
 }  // namespace pkv
@@ -1617,11 +1634,16 @@ static int launch_partition(const DecodeArgs& a, int head_dim, hipStream_t st) {
       hipLaunchKernelGGL(paged_attn_fixed_kernel<128>, dim3(grid), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL(paged_attn_fixed_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  } else if (a.pre_tiles > 0) {   // a shared prefix's units in the split
+    if (head_dim == 128)
+      hipLaunchKernelGGL((paged_attn_balanced_kernel<128, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((paged_attn_balanced_kernel<64, true>), dim3(grid), dim3(256), 0, st, a);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL(paged_attn_balanced_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((paged_attn_balanced_kernel<128, false>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(paged_attn_balanced_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((paged_attn_balanced_kernel<64, false>), dim3(grid), dim3(256), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
@@ -1799,7 +1821,7 @@ extern "C" int pkv_decode_step_prefix(float* out, const void* q, const void* k_n
     a.pre_info = (int32_t*)((char*)workspace + base);
     a.pre_ml = (float*)((char*)workspace + base + (units * 8 + 255) / 256 * 256);
     const int64_t slots = split_wave_cap(g, max_context_len) + units;
-    a.pre_acc = a.pre_ml + 2 * 16 * slots;
+    a.pre_acc = a.pre_ml + 2 * kPrefixRows * slots;
   }
   const hipStream_t st = (hipStream_t)stream;
   const int prc = launch_partition(a, d, st);

@@ -1,7 +1,8 @@
 """The decode step for a batch that shares a prompt prefix
-(pkv_decode_step_prefix): the prefix's tiles are read once for every member
-sequence by the prefix kernel, the partition kernel covers the rest, and the
-merge kernel combines both.
+(pkv_decode_step_prefix): the partition kernel reads the prefix's tiles once
+for every member sequence (prefix units of its split, 32 member rows per
+tile) and each member's own tiles after the prefix, and the merge kernel
+combines both.
 
 The bar: outputs within 1e-3 of the oracle (which walks every sequence's own
 table), within 2.5e-5 of pkv_decode_step on the same inputs (only the order
@@ -159,7 +160,7 @@ def test_prefix_bad_block_id(pkv):
     """An id outside the pool inside the prefix, in the prefix table and in
     the tables of the sequences holding that block: flagged, and the same
     rows are NaN as with pkv_decode_step on the same tables (the members
-    through the prefix kernel, the short sequences through their own
+    through the prefix units, the short sequences through their own
     tables); the other rows agree; nothing is read out of bounds."""
     n_q, n_kv, d, prefix, ctx = CASES[0]
     hc = w.host_case(_shape(n_q, n_kv, d, prefix), 312, context_lens=ctx, share=True)
@@ -250,9 +251,9 @@ def test_prefix_llama3_shape(pkv, orc):
 
 
 def test_prefix_step_in_graph(pkv):
-    """The call captured in a HIP graph (its second stream becomes a fork and
-    a join of the capture) and replayed with new inputs between replays:
-    every replay equals an eager call on the same state, bit for bit."""
+    """The call captured in a HIP graph and replayed with new inputs between
+    replays: every replay equals an eager call on the same state, bit for
+    bit."""
     import torch
     n_q, n_kv, d, prefix, ctx = CASES[0]
     hc = w.host_case(_shape(n_q, n_kv, d, prefix), 314, context_lens=ctx, share=True)
@@ -263,7 +264,7 @@ def test_prefix_step_in_graph(pkv):
                      dtype=torch.uint8, device="cuda")
     out_ref = torch.empty_like(dc.out)
     assert pkv.pkv_decode_split_waves(B, n_q, n_kv, d, dc.max_ctx) > 0
-    # one eager call first: the library's second stream exists before capture
+    # one eager call first (device queries behind the split are cached outside capture)
     pkv.pkv_decode_step_prefix(out_ref, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt,
                                dc.cl, hc.shape.scale, dc.max_ctx, pt, 0, B, workspace=ws,
                                err_flag=dc.err)
