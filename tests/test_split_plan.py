@@ -3,7 +3,10 @@
 The decode kernel cuts all tiles of a call, in (KV head, query group,
 sequence, tile) order, into W equal ranges, one per wavefront; a wavefront
 leaves one partial per unit (head, group, sequence) its range touches, in
-slot wave + unit, and the last of a unit's wavefronts to arrive merges them.
+slot wave + unit, and the merge kernel combines a unit's partials. With a
+shared prefix (run_prefix below) the order ends with the prefix units, one
+per (KV head, 32 member rows) over the prefix's tiles, and a member's own
+unit holds only its tiles after the prefix.
 This model follows the same integer formulas and checks, for random mixes
 of context lengths (invalid ones included), head counts and wave counts
 (more waves than tiles included), that:
@@ -11,8 +14,8 @@ of context lengths (invalid ones included), head counts and wave counts
   * no two partials share a slot, and every slot is below W + units;
   * the merge of a unit reads exactly the slots of its wavefronts, whose
     tiles add up to the unit's, and reads no unwritten slot;
-  * the arrival count of a unit equals the number of partials merged, and
-    units written directly see no arrival.
+  * the number of partials written for a unit equals the number merged, and
+    units written directly have none.
 """
 import random
 
@@ -139,3 +142,159 @@ def test_many_more_waves_than_tiles():
     many sit at a unit's first tile and must not join its merge."""
     run([1, 2, 3], 16384, 8, 1024)
     run([1] * 64, 100, 8, 8192)
+
+
+def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
+    """The decode split with prefix units (pkv_decode_step_prefix), one
+    query group per KV head (group <= 16): the same integer formulas as the
+    kernel, checked like run()."""
+    B = len(ctxs)
+
+    def skip(s):
+        c = ctxs[s]
+        return pre_tiles if (pre_tiles > 0 and first <= s < first + count and
+                             seq_tiles(c, max_ctx) > 0 and (c - 1) // 16 >= pre_tiles) else 0
+
+    unit_t = [seq_tiles(ctxs[s], max_ctx) - skip(s) if seq_tiles(ctxs[s], max_ctx) else 0
+              for s in range(B)]
+    per_row = sum(unit_t)
+    t_seq = n_kv * per_row
+    qgroups = (count * group + 31) // 32 if pre_tiles > 0 and count > 0 else 0
+    pre_units = n_kv * qgroups
+    total = t_seq + pre_units * pre_tiles
+    if total == 0:
+        return
+    covered = [0] * total
+    seq_writes, pre_writes = {}, {}
+    direct = set()
+
+    def locate(r):
+        acc = 0
+        for s in range(B):
+            if acc + unit_t[s] > r:
+                return s, acc
+            acc += unit_t[s]
+        raise AssertionError
+
+    def prefix_walk(w, c, end):
+        pu = (c - t_seq) // pre_tiles
+        pos = (c - t_seq) - pu * pre_tiles
+        while c < end:
+            assert pu < pre_units
+            tb = min(pre_tiles, pos + (end - c))
+            for t in range(pos, tb):
+                covered[t_seq + pu * pre_tiles + t] += 1
+            slot = w + pu
+            assert slot not in pre_writes, ("dup prefix slot", slot)
+            pre_writes[slot] = (pu, tb - pos)
+            c += tb - pos
+            pos = 0
+            pu += 1
+
+    for w in range(W):
+        cur = total * w // W
+        end = total * (w + 1) // W
+        if cur >= end:
+            if cur < t_seq:
+                hq = cur // per_row
+                s, before = locate(cur - hq * per_row)
+                if cur - hq * per_row != before:
+                    slot = w + hq * B + s
+                    assert slot not in seq_writes
+                    seq_writes[slot] = (hq * B + s, 0)
+            elif cur < total:
+                pu = (cur - t_seq) // pre_tiles
+                if cur - t_seq != pu * pre_tiles:
+                    slot = w + pu
+                    assert slot not in pre_writes
+                    pre_writes[slot] = (pu, 0)
+            continue
+        if cur >= t_seq:
+            prefix_walk(w, cur, end)
+            continue
+        hq = cur // per_row
+        s, before = locate(cur - hq * per_row)
+        pos = cur - hq * per_row - before
+        while True:
+            nt = unit_t[s]
+            assert 0 <= pos < nt
+            tb = min(nt, pos + (end - cur))
+            u = hq * B + s
+            base = hq * per_row + sum(unit_t[:s])
+            for t in range(pos, tb):
+                covered[base + t] += 1
+            if pos == 0 and tb == nt and skip(s) == 0:
+                direct.add(u)
+            else:
+                slot = w + u
+                assert slot not in seq_writes, ("dup", slot)
+                seq_writes[slot] = (u, tb - pos)
+            cur += tb - pos
+            if cur >= end:
+                break
+            pos = 0
+            done = False
+            while True:
+                s += 1
+                if s == B:
+                    s = 0
+                    hq += 1
+                    if hq >= n_kv:
+                        done = True
+                        break
+                if unit_t[s]:
+                    break
+            if done:
+                prefix_walk(w, cur, end)
+                break
+    assert all(c == 1 for c in covered), "coverage"
+    assert max(seq_writes, default=0) < W + n_kv * B
+    assert max(pre_writes, default=0) < W + pre_units
+    # merge side: a member past the prefix reads its own unit's slots, then
+    # its prefix unit's slots; both sets hold exactly their tiles
+    for h in range(n_kv):
+        for s in range(B):
+            nt = unit_t[s]
+            if nt == 0:
+                continue
+            u = h * B + s
+            t0 = h * per_row + sum(unit_t[:s])
+            w0 = ((t0 + 1) * W - 1) // total
+            w1 = ((t0 + nt) * W - 1) // total
+            n = w1 - w0 + 1
+            if n <= 1 and skip(s) == 0:
+                assert u in direct
+                continue
+            got = sum(seq_writes[w0 + u + p][1] for p in range(n)
+                      if seq_writes.get(w0 + u + p, (None,))[0] == u)
+            assert all(seq_writes.get(w0 + u + p, (None,))[0] == u for p in range(n)), ("slots", u)
+            assert got == nt
+            if skip(s):
+                for jj in range(group):
+                    pr = (s - first) * group + jj
+                    pu = h * qgroups + pr // 32
+                    x0 = t_seq + pu * pre_tiles
+                    p0 = ((x0 + 1) * W - 1) // total
+                    p1 = ((x0 + pre_tiles) * W - 1) // total
+                    slots = [p0 + pu + p for p in range(p1 - p0 + 1)]
+                    assert all(pre_writes.get(sl, (None,))[0] == pu for sl in slots), ("pre slots", pu)
+                    assert sum(pre_writes[sl][1] for sl in slots) == pre_tiles
+
+
+def test_split_with_prefix_units():
+    rnd = random.Random(1)
+    n_cases = 0
+    for _ in range(1500):
+        B = rnd.randint(1, 40)
+        pre_tiles = rnd.choice([1, 2, 5, 16, 40])
+        max_ctx = rnd.choice([16 * pre_tiles + 1, 16 * pre_tiles + 200, 3000])
+        ctxs = [rnd.choice([0, 1, rnd.randint(1, max_ctx), max_ctx, 16 * pre_tiles,
+                            16 * pre_tiles + 1]) for _ in range(B)]
+        n_kv = rnd.randint(1, 8)
+        group = rnd.choice([1, 4, 5, 8, 16])
+        first = rnd.randint(0, B - 1)
+        count = rnd.randint(0, B - first)
+        W = rnd.choice([1, 3, 64, 1000, rnd.randint(1, 2000)])
+        run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count)
+        n_cases += 1
+    assert n_cases == 1500
