@@ -1,5 +1,6 @@
-"""A seeded random sweep of the decode step and the verification pass
-against the oracle, beside the hand-picked cases of the other tests. Each
+"""A seeded random sweep of the decode step, the verification pass, chunked
+prefill and the shared-prefix step against the oracle, beside the
+hand-picked cases of the other tests. Each
 case draws: KV heads (1, 2, 4, 8) and group size (1 .. 20, at most 64 query
 heads), head size 64 or 128, 1 .. 24 sequences whose contexts mix tiny ones,
 ones around a block boundary and long ones (up to 3,000 tokens), table
@@ -132,6 +133,48 @@ def test_prefill_sweep(pkv, orc, seed):
                           hc.tables.context_lens, n_kv, hc.shape.scale)
     assert rc == 0 and int(err.item()) == 0
     got = out.cpu().numpy().astype(np.float64)
+    e = max_abs(got, want)
+    print(f"  max-abs {e:.2e}")
+    assert np.isfinite(got).all() and e <= TOL
+
+
+@pytest.mark.parametrize("seed", range(300, 315))
+def test_prefix_sweep(pkv, orc, seed):
+    """pkv_decode_step_prefix on random shapes: a prefix of 1 .. 40 blocks
+    shared by every sequence longer than it (shorter ones hold a copy of
+    the block they write), a random member range, contexts past the
+    prefix by 1 .. 3,000 tokens; against the oracle, pools bit-exact."""
+    g = np.random.default_rng([9300, seed])
+    while True:
+        n_kv = int(g.choice([1, 2, 4, 8]))
+        G = int(g.choice([1, 2, 3, 4, 5, 7, 8, 16, 20]))
+        if n_kv * G <= 64:
+            break
+    d = int(g.choice([64, 128]))
+    B = int(g.integers(2, 25))
+    pre = int(g.choice([1, 2, 7, 16, 40]))
+    ctx = [int(16 * pre + g.integers(1, 3001)) if g.random() < 0.75 else int(g.integers(1, 16 * pre + 1))
+           for _ in range(B)]
+    first = int(g.integers(0, B))
+    count = int(g.integers(0, B - first + 1))
+    slack = int(g.choice([0, 16, 700]))
+    print(f"seed {seed}: {n_kv * G}/{n_kv} heads, d {d}, {B} sequences up to {max(ctx)}, prefix "
+          f"{pre} blocks, members {first}..{first + count - 1}, slack {slack}", flush=True)
+    shape = w.Shape(f"prefix sweep {seed}", 1, n_kv * G, n_kv, d, 1, 1, 1, prefix_tokens=16 * pre)
+    max_ctx = max(ctx) + slack
+    hc = w.host_case(shape, 9300 + seed, context_lens=ctx, share=True,
+                     max_blocks=math.ceil(max_ctx / w.BLOCK))
+    dc = DevCase(hc)
+    pkv.pkv_decode_step_prefix(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool, dc.bt,
+                               dc.cl, shape.scale, max_ctx, to_dev_i32(hc.tables.prefix_phys),
+                               first, count, err_flag=dc.err)
+    import torch
+    torch.cuda.synchronize()
+    got = dc.out.cpu().numpy().astype(np.float64)
+    want, rc, k_ref, v_ref = oracle_step(orc, hc)
+    assert rc == 0 and int(dc.err.item()) == 0
+    assert np.array_equal(to_host_u16(dc.k_pool), k_ref)
+    assert np.array_equal(to_host_u16(dc.v_pool), v_ref)
     e = max_abs(got, want)
     print(f"  max-abs {e:.2e}")
     assert np.isfinite(got).all() and e <= TOL
