@@ -104,6 +104,11 @@ constexpr int kRing = 2;
 // Shared prefix: member rows served per prefix tile, in groups of 16.
 constexpr int kPrefixNG = 2;
 constexpr int kPrefixRows = 16 * kPrefixNG;
+// Time per tile of a wave that reads only a shared prefix's tiles (from
+// L2), relative to a wave streaming tiles from HBM: the prefix's share of
+// the waves (see balanced_body).
+constexpr int kPrefixCostNum = 2;
+constexpr int kPrefixCostDen = 3;
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
 struct DecodeArgs {
@@ -780,11 +785,16 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
 }
 
 // Balanced split: wave w processes tiles [w*T/W, (w+1)*T/W) of the
-// (head, group, sequence, tile) order, T = all tiles of the launch, and
-// after them (shared prefix) the prefix units' tiles in (KV head, row
-// group, tile) order. The wave holding a unit's first tile records, for
-// the merge kernel, the unit's first partial slot and its number of
-// partials (1: written here).
+// (head, group, sequence, tile) order, T = all tiles of the launch. With a
+// shared prefix the waves form two classes: waves [0, W - Wp) split the
+// sequences' tiles that way, and the last Wp waves split the prefix units'
+// tiles, in (KV head, row group, tile) order. Wp follows from the tile
+// counts and the relative cost of a prefix tile (a wave that reads only
+// L2-resident prefix tiles takes about kPrefixCostNum / kPrefixCostDen of
+// the time per tile of a wave streaming from HBM), so both classes end
+// together. (With a single wave, one order holds both.) The wave holding
+// a unit's first tile records, for the merge kernel, the unit's first
+// partial slot and its number of partials (1: written here).
 template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX>
 __device__ inline void balanced_body(const DecodeArgs& a) {
   constexpr int VM = D / 16;
@@ -796,20 +806,37 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
   const int per_row = tile_scan_total<PREFIX>(a, lane, ts);   // tiles of one (head, group)
   const int n_hq = a.n_kv * a.n_qgroups;
   const int64_t t_seq = (int64_t)n_hq * per_row;
-  const int64_t total = t_seq + (PREFIX ? (int64_t)a.pre_units * a.pre_tiles : 0);
-  int64_t cur = total * w / a.n_waves;
-  const int64_t end = total * (w + 1) / a.n_waves;
+  const int64_t t_pre = PREFIX ? (int64_t)a.pre_units * a.pre_tiles : 0;
+  int w_pre = 0;   // waves of the prefix class (0: one order for all tiles)
+  if (PREFIX && t_pre > 0 && a.n_waves >= 2) {
+    if (t_seq == 0) {
+      w_pre = a.n_waves;
+    } else {
+      const int64_t num = (int64_t)a.n_waves * kPrefixCostNum * t_pre;
+      const int64_t den = t_seq * kPrefixCostDen + (int64_t)kPrefixCostNum * t_pre;
+      w_pre = (int)max((int64_t)1, min((int64_t)a.n_waves - 1, (num + den / 2) / den));
+    }
+  }
+  // This wave's span: its tiles, waves and first wave, and where in it the
+  // prefix units begin.
+  const bool pre_class = w_pre > 0 && w >= a.n_waves - w_pre;
+  const int64_t total = w_pre == 0 ? t_seq + t_pre : (pre_class ? t_pre : t_seq);
+  const int span_waves = w_pre == 0 ? a.n_waves : (pre_class ? w_pre : a.n_waves - w_pre);
+  const int wave_base = pre_class ? a.n_waves - w_pre : 0;
+  const int64_t pre_origin = pre_class ? 0 : t_seq;
+  int64_t cur = total * (w - wave_base) / span_waves;
+  const int64_t end = total * (w - wave_base + 1) / span_waves;
 
-  // Prefix segments from tile c (at or after t_seq) up to end.
+  // Prefix segments from tile c (at or after pre_origin) up to end.
   auto prefix_walk = [&](int64_t c) {
-    int pu = (int)((c - t_seq) / a.pre_tiles);
-    int pos = (int)((c - t_seq) - (int64_t)pu * a.pre_tiles);
+    int pu = (int)((c - pre_origin) / a.pre_tiles);
+    int pos = (int)((c - pre_origin) - (int64_t)pu * a.pre_tiles);
     while (c < end) {
       const int tb = (int)min((int64_t)a.pre_tiles, pos + (end - c));
       if (pos == 0 && lane == 0) {
         int w0, w1;
-        waves_of_range(c, c + a.pre_tiles, total, a.n_waves, w0, w1);
-        a.pre_info[2 * pu] = w0 + pu;
+        waves_of_range(c, c + a.pre_tiles, total, span_waves, w0, w1);
+        a.pre_info[2 * pu] = wave_base + w0 + pu;
         a.pre_info[2 * pu + 1] = w1 - w0 + 1;
       }
       prefix_segment<D, NBUF>(a, lane, pu, pos, tb, (int64_t)w + pu);
@@ -833,7 +860,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
       m0[g] = -__builtin_inff();
       l0[g] = 0.f;
     }
-    if (cur < t_seq) {
+    if (cur < pre_origin) {
       const int hq = (int)(cur / per_row);
       int s, before;
       tile_scan_locate<PREFIX>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
@@ -843,8 +870,8 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
                                               a.context_lens[s]);
       finish_rows<D, NG>(a, lane, true, false, (int64_t)w + u, rw, zero, m0, l0);
     } else if (PREFIX && cur < total) {
-      const int pu = (int)((cur - t_seq) / a.pre_tiles);
-      if (cur - t_seq == (int64_t)pu * a.pre_tiles) return;
+      const int pu = (int)((cur - pre_origin) / a.pre_tiles);
+      if (cur - pre_origin == (int64_t)pu * a.pre_tiles) return;
       const Rows<kPrefixNG> rw = prefix_rows(a, lane, pu / a.pre_qgroups, pu % a.pre_qgroups);
 #pragma unroll
       for (int g = 0; g < kPrefixNG; ++g)
@@ -853,7 +880,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     }
     return;
   }
-  if (PREFIX && cur >= t_seq) {
+  if (PREFIX && cur >= pre_origin) {
     prefix_walk(cur);
     return;
   }
@@ -876,7 +903,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
 
     if (pos == 0 && lane == 0) {
       int w0, w1;
-      waves_of_range(cur, cur + nt, total, a.n_waves, w0, w1);
+      waves_of_range(cur, cur + nt, total, span_waves, w0, w1);
       a.unit_info[2 * u] = w0 + u;
       a.unit_info[2 * u + 1] = w1 - w0 + 1;
     }
@@ -901,7 +928,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
       if (++s == a.num_seqs) {
         s = 0;
         if (++hq >= n_hq) {
-          if (PREFIX && a.pre_units > 0) prefix_walk(t_seq);
+          if (PREFIX && w_pre == 0 && a.pre_units > 0) prefix_walk(pre_origin);
           return;
         }
       }

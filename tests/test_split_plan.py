@@ -4,9 +4,9 @@ The decode kernel cuts all tiles of a call, in (KV head, query group,
 sequence, tile) order, into W equal ranges, one per wavefront; a wavefront
 leaves one partial per unit (head, group, sequence) its range touches, in
 slot wave + unit, and the merge kernel combines a unit's partials. With a
-shared prefix (run_prefix below) the order ends with the prefix units, one
-per (KV head, 32 member rows) over the prefix's tiles, and a member's own
-unit holds only its tiles after the prefix.
+shared prefix (run_prefix below) the prefix units, one per (KV head, 32
+member rows) over the prefix's tiles, are split by their own class of
+waves, and a member's own unit holds only its tiles after the prefix.
 This model follows the same integer formulas and checks, for random mixes
 of context lengths (invalid ones included), head counts and wave counts
 (more waves than tiles included), that:
@@ -144,10 +144,12 @@ def test_many_more_waves_than_tiles():
     run([1] * 64, 100, 8, 8192)
 
 
-def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
+def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 3)):
     """The decode split with prefix units (pkv_decode_step_prefix), one
     query group per KV head (group <= 16): the same integer formulas as the
-    kernel, checked like run()."""
+    kernel, checked like run(). With a prefix and two or more waves the
+    waves form two classes, the last Wp splitting the prefix units' tiles;
+    with one wave a single order holds both."""
     B = len(ctxs)
 
     def skip(s):
@@ -161,12 +163,29 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
     t_seq = n_kv * per_row
     qgroups = (count * group + 31) // 32 if pre_tiles > 0 and count > 0 else 0
     pre_units = n_kv * qgroups
-    total = t_seq + pre_units * pre_tiles
-    if total == 0:
+    t_pre = pre_units * pre_tiles
+    if t_seq + t_pre == 0:
         return
-    covered = [0] * total
+    w_pre = 0
+    if t_pre > 0 and W >= 2:
+        if t_seq == 0:
+            w_pre = W
+        else:
+            num = W * cost[0] * t_pre
+            den = t_seq * cost[1] + cost[0] * t_pre
+            w_pre = max(1, min(W - 1, (num + den // 2) // den))
+    # global tile index: the sequences' tiles, then the prefix units'
+    covered = [0] * (t_seq + t_pre)
     seq_writes, pre_writes = {}, {}
     direct = set()
+
+    def span(w):
+        pre_class = w_pre > 0 and w >= W - w_pre
+        total = t_seq + t_pre if w_pre == 0 else (t_pre if pre_class else t_seq)
+        waves = W if w_pre == 0 else (w_pre if pre_class else W - w_pre)
+        base = W - w_pre if pre_class else 0
+        origin = 0 if pre_class else t_seq
+        return total, waves, base, origin
 
     def locate(r):
         acc = 0
@@ -176,9 +195,9 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
             acc += unit_t[s]
         raise AssertionError
 
-    def prefix_walk(w, c, end):
-        pu = (c - t_seq) // pre_tiles
-        pos = (c - t_seq) - pu * pre_tiles
+    def prefix_walk(w, c, end, origin):
+        pu = (c - origin) // pre_tiles
+        pos = (c - origin) - pu * pre_tiles
         while c < end:
             assert pu < pre_units
             tb = min(pre_tiles, pos + (end - c))
@@ -192,10 +211,11 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
             pu += 1
 
     for w in range(W):
-        cur = total * w // W
-        end = total * (w + 1) // W
+        total, waves, base, origin = span(w)
+        cur = total * (w - base) // waves
+        end = total * (w - base + 1) // waves
         if cur >= end:
-            if cur < t_seq:
+            if cur < origin:
                 hq = cur // per_row
                 s, before = locate(cur - hq * per_row)
                 if cur - hq * per_row != before:
@@ -203,14 +223,14 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
                     assert slot not in seq_writes
                     seq_writes[slot] = (hq * B + s, 0)
             elif cur < total:
-                pu = (cur - t_seq) // pre_tiles
-                if cur - t_seq != pu * pre_tiles:
+                pu = (cur - origin) // pre_tiles
+                if cur - origin != pu * pre_tiles:
                     slot = w + pu
                     assert slot not in pre_writes
                     pre_writes[slot] = (pu, 0)
             continue
-        if cur >= t_seq:
-            prefix_walk(w, cur, end)
+        if cur >= origin:
+            prefix_walk(w, cur, end, origin)
             continue
         hq = cur // per_row
         s, before = locate(cur - hq * per_row)
@@ -220,9 +240,9 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
             assert 0 <= pos < nt
             tb = min(nt, pos + (end - cur))
             u = hq * B + s
-            base = hq * per_row + sum(unit_t[:s])
+            base_t = hq * per_row + sum(unit_t[:s])
             for t in range(pos, tb):
-                covered[base + t] += 1
+                covered[base_t + t] += 1
             if pos == 0 and tb == nt and skip(s) == 0:
                 direct.add(u)
             else:
@@ -245,40 +265,44 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count):
                 if unit_t[s]:
                     break
             if done:
-                prefix_walk(w, cur, end)
+                assert w_pre == 0
+                prefix_walk(w, cur, end, origin)
                 break
     assert all(c == 1 for c in covered), "coverage"
     assert max(seq_writes, default=0) < W + n_kv * B
     assert max(pre_writes, default=0) < W + pre_units
-    # merge side: a member past the prefix reads its own unit's slots, then
-    # its prefix unit's slots; both sets hold exactly their tiles
+    # merge side: the bookkeeping the kernel writes (first slot, count) per
+    # unit, from the unit's span; the slots hold exactly the unit's tiles
+    seq_span = span(0)
+    pre_span = span(W - 1)
     for h in range(n_kv):
         for s in range(B):
             nt = unit_t[s]
             if nt == 0:
                 continue
             u = h * B + s
+            total, waves, _, _ = seq_span
             t0 = h * per_row + sum(unit_t[:s])
-            w0 = ((t0 + 1) * W - 1) // total
-            w1 = ((t0 + nt) * W - 1) // total
+            w0 = ((t0 + 1) * waves - 1) // total
+            w1 = ((t0 + nt) * waves - 1) // total
             n = w1 - w0 + 1
             if n <= 1 and skip(s) == 0:
                 assert u in direct
                 continue
-            got = sum(seq_writes[w0 + u + p][1] for p in range(n)
-                      if seq_writes.get(w0 + u + p, (None,))[0] == u)
-            assert all(seq_writes.get(w0 + u + p, (None,))[0] == u for p in range(n)), ("slots", u)
-            assert got == nt
+            slots = [w0 + u + p for p in range(n)]
+            assert all(seq_writes.get(sl, (None,))[0] == u for sl in slots), ("slots", u)
+            assert sum(seq_writes[sl][1] for sl in slots) == nt
             if skip(s):
+                total, waves, base, origin = pre_span if w_pre else seq_span
                 for jj in range(group):
                     pr = (s - first) * group + jj
                     pu = h * qgroups + pr // 32
-                    x0 = t_seq + pu * pre_tiles
-                    p0 = ((x0 + 1) * W - 1) // total
-                    p1 = ((x0 + pre_tiles) * W - 1) // total
-                    slots = [p0 + pu + p for p in range(p1 - p0 + 1)]
-                    assert all(pre_writes.get(sl, (None,))[0] == pu for sl in slots), ("pre slots", pu)
-                    assert sum(pre_writes[sl][1] for sl in slots) == pre_tiles
+                    x0 = origin + pu * pre_tiles
+                    p0 = ((x0 + 1) * waves - 1) // total
+                    p1 = ((x0 + pre_tiles) * waves - 1) // total
+                    pslots = [base + p0 + pu + p for p in range(p1 - p0 + 1)]
+                    assert all(pre_writes.get(sl, (None,))[0] == pu for sl in pslots), ("pre slots", pu)
+                    assert sum(pre_writes[sl][1] for sl in pslots) == pre_tiles
 
 
 def test_split_with_prefix_units():
@@ -294,7 +318,8 @@ def test_split_with_prefix_units():
         group = rnd.choice([1, 4, 5, 8, 16])
         first = rnd.randint(0, B - 1)
         count = rnd.randint(0, B - first)
-        W = rnd.choice([1, 3, 64, 1000, rnd.randint(1, 2000)])
-        run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count)
+        W = rnd.choice([1, 2, 3, 64, 1000, rnd.randint(1, 2000)])
+        cost = rnd.choice([(2, 3), (1, 2), (1, 1), (1, 5)])
+        run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost)
         n_cases += 1
     assert n_cases == 1500
