@@ -767,7 +767,7 @@ def prefix_cache_bench(pkv, seed, n_req=2000):
     }
 
 
-def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False):
+def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False, prefix_kernel=True):
     """Continuous batching at a model shape: requests with prompts uniform in
     [prefix, ctx_hi - 256] tokens (all beginning with the shared prefix when
     the shape has one) and 32..256 generated tokens, queued ahead; the
@@ -805,7 +805,8 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False):
     src_v = torch.empty_like(src_k)
     w.device_normal_bf16_(src_k, seed * 1000 + 900)
     w.device_normal_bf16_(src_v, seed * 1000 + 901)
-    loop = ServingLoop(b, kp, vp, shape.n_q, shape.scale, B, graphs=graphs)
+    loop = ServingLoop(b, kp, vp, shape.n_q, shape.scale, B, graphs=graphs,
+                       prefix_kernel=prefix_kernel)
     for i, t in enumerate(loop.inputs()):
         w.device_normal_bf16_(t, seed * 1000 + 950 + i)
     if prefix:
@@ -912,6 +913,9 @@ def main():
                     help="host benchmark of the prefix cache on a multi-turn chat workload")
     ap.add_argument("--loop", action="store_true",
                     help="continuous batching instead: the batcher's plans carried out step by step")
+    ap.add_argument("--loop-no-prefix-kernel", action="store_true",
+                    help="serving loop: pkv_decode_step for every row, the shared prefix "
+                         "included, instead of pkv_decode_step_prefix")
     ap.add_argument("--loop-graphs", action="store_true",
                     help="continuous batching with the decode launches replayed from cached graphs")
     ap.add_argument("--loop-steps", type=int, default=300)
@@ -941,7 +945,7 @@ def main():
     if args.loop:
         log(f"[bench] continuous batching, {wname}")
         line = loop_bench(pkv, torch, shape, wname, args.seed, args.loop_steps, args.loop_warmup,
-                          graphs=args.loop_graphs)
+                          graphs=args.loop_graphs, prefix_kernel=not args.loop_no_prefix_kernel)
         print(json.dumps(line), flush=True)
         return
     if args.prefill_chunk > 0:

@@ -771,6 +771,7 @@ class Batcher:
                                       ctypes.byref(h)), "pkv_batcher_create")
         self._h = h
         self.max_blocks_per_seq = max_blocks_per_seq
+        self.prefix_tokens = prefix_tokens
 
     def close(self):
         if self._h:

@@ -13,7 +13,10 @@ are admitted, one decode step runs for the resident batch):
      step (their keys and values come from the caller: a prefill's output,
      or a preempted request's recomputed tokens), pkv_decode_step for the
      resident rows (the new token's key/value appended inside the
-     attention).
+     attention); with the batcher's shared prefix, pkv_decode_step_prefix
+     over the longest run of rows whose tables start with the prefix's
+     blocks (found on the host from the plan), so the prefix's tiles are
+     read once for all of them.
 Everything runs in the library's kernels and its native batcher; this
 module only moves arguments. The keys, values and queries are the
 caller's: in a model they come from the layers' projections.
@@ -34,8 +37,8 @@ from collections import OrderedDict
 
 import numpy as np
 
-from . import (Batcher, _torch, pkv_copy_blocks, pkv_decode_step, pkv_decode_workspace_bytes,
-               pkv_kv_write)
+from . import (Batcher, _torch, pkv_copy_blocks, pkv_decode_prefix_workspace_bytes,
+               pkv_decode_step, pkv_decode_step_prefix, pkv_decode_workspace_bytes, pkv_kv_write)
 
 
 class ServingLoop:
@@ -43,7 +46,8 @@ class ServingLoop:
     tables, one workspace sized for the largest batch and context."""
 
     def __init__(self, batcher: Batcher, k_pools, v_pools, n_q: int, scale: float,
-                 max_batch: int, stream=None, graphs: bool = False, max_graphs: int = 4):
+                 max_batch: int, stream=None, graphs: bool = False, max_graphs: int = 4,
+                 prefix_kernel: bool = True):
         torch = _torch()
         self.b = batcher
         self.k_pools, self.v_pools = k_pools, v_pools
@@ -69,6 +73,19 @@ class ServingLoop:
                                device=dev)
         self.err = torch.zeros(1, dtype=i32, device=dev)
         ws = pkv_decode_workspace_bytes(max_batch, n_q, self.n_kv, self.d, self.max_ctx, 0)
+        # the shared prefix's whole blocks, read once per step for the rows
+        # that hold them (a partly filled last block is copied by every
+        # request that shares the prefix, so it is not shared)
+        table, _ = batcher.prefix_table()
+        n_pre = batcher.prefix_tokens // 16
+        self.n_pre = n_pre if prefix_kernel else 0
+        self.pre_h = table[:n_pre].copy()
+        self.pre_table = None
+        self.members = (0, 0)   # (first row, count) of this step's prefix call
+        if self.n_pre:
+            self.pre_table = torch.from_numpy(self.pre_h).to(dev)
+            ws = max(ws, pkv_decode_prefix_workspace_bytes(max_batch, n_q, self.n_kv, self.d,
+                                                           self.max_ctx, self.n_pre, max_batch))
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.uploaded = torch.cuda.Event()
         self.uploaded.record(self.stream)
@@ -126,6 +143,7 @@ class ServingLoop:
         p = self.b.step()
         self.plan = p
         n, n_cow, n_fill = p.num_seqs, len(p.cow_src), len(p.fill_rows)
+        self.members = self._member_run(p) if self.n_pre and n else (0, 0)
         self.uploaded.synchronize()       # the staging buffers are free again
         self._size_cow(n_cow)
         self._size_fill(n_fill)
@@ -145,6 +163,23 @@ class ServingLoop:
                 self.fill[:, :n_fill].copy_(self.fill_h[:, :n_fill], non_blocking=True)
             self.uploaded.record(self.stream)
         return p
+
+    def _member_run(self, p):
+        """The longest run of rows whose contexts extend past the shared
+        prefix and whose tables start with its blocks (rows whose contexts
+        end inside it may sit in the run too: they read their own blocks)."""
+        pre = self.n_pre
+        holds = (p.block_tables[:, :pre] == self.pre_h).all(axis=1)
+        ok = holds | ((p.context_lens.astype(np.int64) - 1) // 16 < pre)
+        best, start = (0, 0), None
+        for i, v in enumerate(list(ok) + [False]):
+            if v and start is None:
+                start = i
+            elif not v and start is not None:
+                if i - start > best[1]:
+                    best = (start, i - start)
+                start = None
+        return best
 
     def run(self, fill_kv, q, k_new, v_new):
         """Device half of the scheduled step. fill_kv(l) -> (k_src, v_src)
@@ -169,8 +204,8 @@ class ServingLoop:
             for l in range(self.n_layers):
                 self._writes(l, n, n_cow, n_fill, fill_kv)
             if n:
-                key = (n,) + tuple(t.data_ptr() for x in (q, k_new, v_new)
-                                   for t in (x[l] for l in range(self.n_layers)))
+                key = (n,) + self.members + tuple(t.data_ptr() for x in (q, k_new, v_new)
+                                                  for t in (x[l] for l in range(self.n_layers)))
                 g = self.graphs.pop(key, None)
                 if g is None:
                     g = torch.cuda.CUDAGraph()
@@ -199,6 +234,13 @@ class ServingLoop:
                          stream=self.stream)
 
     def _decode(self, l, n, q, k_new, v_new, stream):
+        first, count = self.members
+        if count:
+            pkv_decode_step_prefix(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
+                                   self.v_pools[l], self.bt[:n], self.cl[:n], self.scale,
+                                   self.max_ctx, self.pre_table, first, count, workspace=self.ws,
+                                   err_flag=self.err, stream=stream)
+            return
         pkv_decode_step(self.out[l, :n], q[l], k_new[l], v_new[l], self.k_pools[l],
                         self.v_pools[l], self.bt[:n], self.cl[:n], self.scale, self.max_ctx, 0,
                         workspace=self.ws, err_flag=self.err, stream=stream)

@@ -127,13 +127,14 @@ def test_continuous_batching_matches_contiguous_recompute(pkv, orc, d):
                             np.zeros(lu.PREFIX, np.int32),
                             np.arange(lu.PREFIX, dtype=np.int32)) == 0
 
-    steps_seen, finished, preempted = {}, [], 0
+    steps_seen, finished, preempted, prefix_calls = {}, [], 0, 0
     for step in range(2000):
         for rid, (arr, prompt, gen, shares) in reqs.items():
             if arr == step:
                 b.submit(rid, prompt, gen, shares)
         p = loop.schedule()
         n = p.num_seqs
+        prefix_calls += loop.members[1] > 0
         ids = [int(x) for x in p.request_ids]
         finished += [int(x) for x in p.finished_ids]
         preempted += len(p.preempted_ids)
@@ -166,6 +167,8 @@ def test_continuous_batching_matches_contiguous_recompute(pkv, orc, d):
     assert sorted(finished) == sorted(reqs)
     assert all(steps_seen[rid] == reqs[rid][2] for rid in reqs)
     assert preempted > 0, "the pool was meant to force preemption"
+    # the prefix's whole block went through pkv_decode_step_prefix
+    assert prefix_calls > 0
 
 
 @pytest.mark.parametrize("d", [64, 128])
