@@ -13,13 +13,13 @@ NUM_BLOCKS = 24      # tight: growth outruns the admission reserve, requests are
 MAX_BATCH = 6
 
 
-def requests(seed, n=14):
+def requests(seed, n=14, prefix=PREFIX):
     """{id: (arrival step, prompt_len, gen_len, shares_prefix)}."""
     rnd = np.random.default_rng(seed)
     reqs = {}
     for rid in range(n):
         shares = bool(rnd.random() < 0.5)
-        prompt = int(rnd.integers(PREFIX if shares else 1, 70))
+        prompt = int(rnd.integers(prefix if shares else 1, 70))
         reqs[rid] = (int(rnd.integers(0, 30)), prompt, int(rnd.integers(10, 120)), shares)
     return reqs
 
@@ -27,14 +27,16 @@ def requests(seed, n=14):
 class History:
     """Keys/values (bf16 bits) of every (layer, request, position): a
     request's own tokens are drawn once per (layer, request); positions
-    below PREFIX of a sharing request are the prefix's. So a request that
-    is preempted and recomputed gets the same keys and values back."""
+    below the prefix length of a sharing request are the prefix's. So a
+    request that is preempted and recomputed gets the same keys and values
+    back."""
 
-    def __init__(self, d, shares):
+    def __init__(self, d, shares, prefix=PREFIX):
         self.d = d
         self.shares = shares
-        self.pk = [w.normal_bf16(w.rng(7000 + l, 6), (PREFIX, N_KV, d)) for l in range(L)]
-        self.pv = [w.normal_bf16(w.rng(7100 + l, 6), (PREFIX, N_KV, d)) for l in range(L)]
+        self.prefix = prefix
+        self.pk = [w.normal_bf16(w.rng(7000 + l, 6), (prefix, N_KV, d)) for l in range(L)]
+        self.pv = [w.normal_bf16(w.rng(7100 + l, 6), (prefix, N_KV, d)) for l in range(L)]
         self.cache = {}
 
     def _own(self, l, rid):
@@ -50,7 +52,7 @@ class History:
         pos = np.asarray(positions, dtype=np.int64)
         ks, vs = k[pos].copy(), v[pos].copy()
         if self.shares[rid]:
-            pre = pos < PREFIX
+            pre = pos < self.prefix
             ks[pre] = self.pk[l][pos[pre]]
             vs[pre] = self.pv[l][pos[pre]]
         return ks, vs
