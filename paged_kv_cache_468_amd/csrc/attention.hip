@@ -1300,19 +1300,8 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   // the prefix unit's partials of this row (decode rows: i = 0, head gr)
   int np = 0;
   int64_t pre_row = 0;
-  if (prefix_skip(a, s, ctx) > 0) {
-    // the partition kernel took this sequence's prefix tiles from the
-    // prefix's table: its own table must start with the same blocks, else
-    // the row is NaN
-    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
-    bool same = true;
-    for (int t = lane; t < a.pre_tiles; t += 64) same = same && row[t] == a.pre_table[t];
-    if (__ballot(!same) != 0) {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = nan;
-      if (hq == 0 && gr == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_PREFIX);
-      return;
-    }
+  const bool member = prefix_skip(a, s, ctx) > 0;
+  if (member) {
     const int pr = (s - a.pre_first) * a.group + gr;
     const int2 pinfo = *(const int2*)(a.pre_info + 2 * (h * a.pre_qgroups + pr / kPrefixRows));
     np = pinfo.y;
@@ -1343,6 +1332,21 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) v[k][e] = src[e];
   }
   f32x2_t mine = lane < tot ? *(const f32x2_t*)ml_of(lane) : f32x2_t{-__builtin_inff(), 0.f};
+  if (member) {
+    // the partition kernel took this sequence's prefix tiles from the
+    // prefix's table: its own table must start with the same blocks, else
+    // the row is NaN (checked while the partials above are in flight; the
+    // prefix partials are the prefix unit's whatever the table holds)
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+    bool same = true;
+    for (int t = lane; t < a.pre_tiles; t += 64) same = same && row[t] == a.pre_table[t];
+    if (__ballot(!same) != 0) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = nan;
+      if (hq == 0 && gr == 0 && lane == 0) flag_error(a.err_flag, PKV_DEVERR_PREFIX);
+      return;
+    }
+  }
 
   float mx = mine[0];
   bool bad = mine[0] != mine[0];
