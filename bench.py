@@ -822,6 +822,7 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False, prefi
         loop.run(lambda l: (src_k[:n_fill], src_v[:n_fill]), None, None, None)
         stream.synchronize()
         acc["tokens"] += n
+        acc["members"] += loop.members[1]
         acc["kv_bytes"] += per_token * int(p.context_lens.astype(np.int64).sum())
         acc["fill"] += n_fill
         ids = set(p.request_ids.tolist())
@@ -831,8 +832,8 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False, prefi
         acc["cow"] += len(p.cow_src)
 
     def fresh():
-        return dict(host_s=0.0, tokens=0, kv_bytes=0, fill=0, admitted=0, finished=0, cow=0,
-                    prev=set())
+        return dict(host_s=0.0, tokens=0, members=0, kv_bytes=0, fill=0, admitted=0, finished=0,
+                    cow=0, prev=set())
 
     acc = fresh()
     for _ in range(warmup):
@@ -866,6 +867,9 @@ def loop_bench(pkv, torch, shape, name, seed, steps, warmup, graphs=False, prefi
         "admitted_per_step": acc["admitted"] / steps,
         "finished_per_step": acc["finished"] / steps,
         "cow_per_step": acc["cow"] / steps,
+        "decode_call": ("pkv_decode_step_prefix over the rows holding the shared prefix"
+                        if loop.n_pre else "pkv_decode_step"),
+        "prefix_member_rows_per_step": acc["members"] / steps,
         "decode_launches": "hip-graph, cached per row count" if graphs else "eager",
         "graph_captures": loop.graph_captures, "graph_replays_from_cache": loop.graph_hits,
     }
