@@ -278,6 +278,37 @@ int pkv_decode_step(float* out, const void* q, const void* k_new,
                     int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pkv_decode_step with the balanced split (partition_tokens = 0) and no
+ * workspace argument. Its workspace is a device array of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it
+ * runs on, from the first call made with that GPU current until the process
+ * ends. The call allocates nothing: no hipMalloc, no allocating library
+ * routine. Results, pools included, are bit for bit those of
+ * pkv_decode_step with partition_tokens = 0 on the same arguments.
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (the kernels need no initialisation: every value the
+ * merge reads is written by the same call's partition kernel). Calls on one
+ * stream are ordered; calls on one GPU that can overlap (different
+ * streams, or other processes' threads sharing the library's state) race
+ * on the array. Arguments, layouts and device errors as for pkv_decode_step.
+ * Host-checked errors: those of pkv_decode_step, and PKV_EWORKSPACE when the
+ * call needs more than PKV_NOALLOC_SCRATCH_BYTES
+ * (pkv_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim,
+ * max_context_len, 0) is the need), before anything is launched; PKV_EHIP if
+ * the array's device address cannot be looked up. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_decode_step_noalloc(float* out, const void* q, const void* k_new,
+                            const void* v_new, void* k_pool, void* v_pool,
+                            const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t num_blocks,
+                            int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float scale,
+                            int32_t max_context_len, int32_t* err_flag,
+                            void* stream);
+
 /* The first half of pkv_decode_step: the append and the partition kernel
  * (with the balanced split one launch, the append inside it). Same arguments
  * as pkv_decode_step; pkv_paged_attn_merge with the same arguments then

@@ -52,6 +52,8 @@ SIGNATURES = {
     "pkv_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_decode_step_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pkv_decode_step_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                                  _vp, _sz, _vp, _vp]),
@@ -246,6 +248,9 @@ def pkv_decode_split_waves(num_seqs, n_q_heads, n_kv_heads, head_dim, max_contex
                                           max_context_len))
 
 
+_NO_WORKSPACE = False   # workspace argument of a call that takes none (nothing is allocated)
+
+
 def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
                  partition_tokens, workspace, err_flag, stream):
     torch = _torch()
@@ -265,7 +270,7 @@ def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
+    if workspace is not None and workspace is not _NO_WORKSPACE:
         ws_ptr = _dev(workspace, "workspace", torch.uint8)
         ws_bytes = workspace.numel()
     return (_dev(out, "out", torch.float32), _dev(q, "q", torch.bfloat16),
@@ -310,6 +315,20 @@ def pkv_decode_step(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_
     args, _ = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
                          max_context_len, partition_tokens, workspace, err_flag, stream)
     _check(lib.pkv_decode_step(*args), "pkv_decode_step")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def pkv_decode_step_noalloc(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                            scale, max_context_len, err_flag=None, stream=None):
+    """pkv_decode_step (balanced split) with no workspace: the library's own
+    device array of NOALLOC_SCRATCH_BYTES per GPU serves as one; nothing is
+    allocated, here or in the library. Overlapping calls on one GPU race."""
+    args, _ = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                         max_context_len, 0, _NO_WORKSPACE, err_flag, stream)
+    # C order: the step's arguments without partition_tokens, workspace and its size
+    _check(lib.pkv_decode_step_noalloc(*(args[:16] + args[19:])), "pkv_decode_step_noalloc")
 
 
 def pkv_decode_prefix_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
