@@ -194,6 +194,30 @@ class Oracle:
             raise ValueError("oracle_verify: bad heads or q_len")
         return out, rc
 
+    def decode_sharded(self, q, k_pool, v_pool, block_tables, context_lens, n_kv, scale,
+                       threads):
+        """decode() with the sequences split into `threads` contiguous shards,
+        each shard one call of the same single-threaded C function on its
+        own host thread (ctypes releases the interpreter lock for the call).
+        The rows are computed exactly as by decode(): each row's arithmetic
+        depends only on its own sequence. Returns (out, worst status)."""
+        from concurrent.futures import ThreadPoolExecutor
+        q = _u16(q, "q")
+        k_pool = _u16(k_pool, "k_pool")
+        v_pool = _u16(v_pool, "v_pool")
+        bt = _i32(block_tables, "block_tables")
+        cl = _i32(context_lens, "context_lens")
+        B = q.shape[0]
+        threads = max(1, min(int(threads), B))
+        cuts = [B * i // threads for i in range(threads + 1)]
+        parts = [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        with ThreadPoolExecutor(max_workers=len(parts)) as pool:
+            res = list(pool.map(lambda ab: self.decode(q[ab[0]:ab[1]], k_pool, v_pool,
+                                                       bt[ab[0]:ab[1]], cl[ab[0]:ab[1]], n_kv,
+                                                       scale), parts))
+        out = np.concatenate([r[0] for r in res]) if res else np.empty(q.shape, np.float64)
+        return out, min((r[1] for r in res), default=0)
+
     def decode_row(self, q_row, k_pool, v_pool, table_row, ctx, n_kv, h, scale):
         """One output row (one sequence, one query head, KV head h)."""
         q_row = _u16(q_row, "q_row")
@@ -245,6 +269,20 @@ def kv_write(*a, **k):
 
 def decode(*a, **k):
     return default().decode(*a, **k)
+
+
+def decode_sharded(*a, **k):
+    return default().decode_sharded(*a, **k)
+
+
+def host_threads(cap=16):
+    """Threads for a sharded oracle run: the CPUs this process may use, at
+    most cap."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
 
 
 def verify(*a, **k):

@@ -12,16 +12,18 @@ benchmark's 44 extra decode steps; one shape also runs the unfused
 kv_append + decode. Checked:
   * kv_append: the whole K and V pools after the append, bit for bit,
     against the oracle's append on the pre-append bytes;
-  * decode: sampled (sequence, query head) rows, each recomputed by the
-    oracle one by one in float64, max-abs error <= 1e-3; the sample always
-    includes the shortest and the longest sequence and, for the shared
-    prefix, a sequence whose written block is a copy of a prefix block.
+  * decode: every (sequence, query head) row of the layer against the
+    oracle in float64 (the same single-threaded C function run on disjoint
+    shards of the sequences, one host thread each), max-abs error <= 1e-3;
+    the shared-prefix shape includes sequences whose written block is a
+    copy of a prefix block.
 """
 import math
 
 import numpy as np
 import pytest
 
+import oracle
 import workload as w
 from gpu_util import TOL, max_abs, to_dev_i32, to_host_u16
 
@@ -95,23 +97,13 @@ def test_full_size_layer(pkv, orc, cfg, fused, shard):
 
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
-    cl_h = t.context_lens
-    seqs = [int(np.argmin(cl_h)), int(np.argmax(cl_h))]
-    if len(t.copies):
-        short = np.nonzero(cl_h <= shape.prefix_tokens)[0]
-        if len(short):
-            seqs.append(int(short[0]))
-    pick = w.rng(seed, 9)
-    rows = [(s, int(pick.integers(shape.n_q))) for s in seqs]
-    rows += [(int(pick.integers(B)), int(pick.integers(shape.n_q))) for _ in range(24)]
-    G = shape.n_q // shape.n_kv
-    worst = 0.0
-    for s, j in rows:
-        want, rc = orc.decode_row(q_h[s, j], k_ref, v_ref, t.block_tables[s], int(cl_h[s]),
-                                  shape.n_kv, j // G, shape.scale)
-        assert rc == 0
-        worst = max(worst, max_abs(got[s, j], want))
-    print(f"config {cfg}: {len(rows)} sampled rows, max-abs {worst:.2e}")
+    threads = oracle.host_threads()
+    want, rc = orc.decode_sharded(q_h, k_ref, v_ref, t.block_tables, t.context_lens, shape.n_kv,
+                                  shape.scale, threads)
+    assert rc == 0
+    worst = max_abs(got, want)
+    print(f"config {cfg}: all {B * shape.n_q} rows of the layer ({threads} oracle threads), "
+          f"max-abs {worst:.2e}")
     assert worst <= TOL
 
 
