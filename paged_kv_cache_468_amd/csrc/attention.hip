@@ -280,25 +280,62 @@ __device__ inline bool shares_first_block(const DecodeArgs& a, int s) {
 }
 
 // The context lengths read once per wave: for up to 256 sequences each
-// lane loads its (at most four) lengths together and keeps their tile
-// counts in registers, from which both the total and the location of a
-// tile follow; longer batches use the chunked loops above.
+// lane loads its (at most four) lengths, and the first table entries of
+// the same sequences, together, and keeps them and the tile counts in
+// registers. The total, the location of a tile, a sequence's context length
+// and its load policy then follow without another round trip to memory;
+// longer batches use the chunked loops above and read memory each time.
 struct TileScan {
-  int n[4];   // tiles of sequences lane, lane + 64, lane + 128, lane + 192
+  int n[4];       // tiles of sequences lane, lane + 64, lane + 128, lane + 192
+  int ctx[4];     // their context lengths
+  int first[4];   // their first table entries
 };
 
-template <bool PREFIX>
+// Sequence s's value of a per-lane quadruple (s wave-uniform, s < 256).
+__device__ inline int scan_value(const int (&v)[4], int s) {
+  const int k = s >> 6;
+  const int x = k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
+  return __builtin_amdgcn_readlane(x, s & 63);
+}
+
+// KEEP: keep the context lengths and first table entries in registers (the
+// decode kernels); without it only the tile counts are kept (the
+// verification pass, whose registers are spoken for).
+template <bool PREFIX, bool KEEP>
 __device__ inline int tile_scan_total(const DecodeArgs& a, int lane, TileScan& ts) {
   if (a.num_seqs > 256) return total_seq_tiles<PREFIX>(a, lane);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = lane + 64 * k;
-    ts.n[k] = i < a.num_seqs ? unit_tiles<PREFIX>(a, i, a.context_lens[i]) : 0;
+    ts.ctx[k] = i < a.num_seqs ? a.context_lens[i] : 0;
+    ts.first[k] = KEEP && i < a.num_seqs ? a.block_tables[(int64_t)i * a.max_blocks] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = lane + 64 * k;
+    ts.n[k] = i < a.num_seqs ? unit_tiles<PREFIX>(a, i, ts.ctx[k]) : 0;
   }
   int total = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) total += wave_sum(ts.n[k]);
   return total;
+}
+
+// Context length of sequence s (from the scan's registers when it holds
+// them).
+template <bool KEEP>
+__device__ inline int scan_ctx(const DecodeArgs& a, const TileScan& ts, int s) {
+  return KEEP && a.num_seqs <= 256 ? scan_value(ts.ctx, s) : a.context_lens[s];
+}
+
+// shares_first_block from the scan's registers when it holds them.
+template <bool KEEP>
+__device__ inline bool scan_shares_first(const DecodeArgs& a, const TileScan& ts, int s) {
+  if (!KEEP || a.num_seqs > 256) return shares_first_block(a, s);
+  const int f = scan_value(ts.first, s);
+  const bool prev = s > 0 && scan_value(ts.first, s > 0 ? s - 1 : 0) == f;
+  const bool next = s + 1 < a.num_seqs && scan_value(ts.first, s + 1 < a.num_seqs ? s + 1 : s) == f;
+  return prev || next;
 }
 
 template <bool PREFIX>
@@ -360,6 +397,43 @@ __device__ inline Rows<NG> rows_of(const DecodeArgs& a, int lane, int s, int h, 
   return rw;
 }
 
+// What a segment needs loaded before its first tile: its query rows (the B
+// operand of the score MFMA: lane (c, r) holds row c, dims 32m + 8r .. +8,
+// zero for rows past the group) and its first block ids (lane l: the id of
+// tile l, and of tile NBUF - 1 + l, clamped to the segment's last). The
+// decode loop issues these loads one segment ahead, so that a wave moving
+// to its next unit finds them in registers instead of waiting two memory
+// round trips with its loads drained.
+template <int D, int NG>
+struct SegPre {
+  bf16x8_t qv[NG][D / 32];
+  int id0, idw;
+};
+
+template <int D, int NG, int NBUF, bool IDS = true>
+__device__ inline void segment_preload(const DecodeArgs& a, int lane, int s, const Rows<NG>& rw,
+                                       int ta, int tb, SegPre<D, NG>& p) {
+  constexpr int KM = D / 32;
+  const int r = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
+      p.qv[g][m] = rw.valid[g] ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  if (!IDS) {   // the verification pass loads its ids in chunks of its own
+    p.id0 = p.idw = 0;
+    return;
+  }
+  const int n = tb - ta;
+  const int32_t* ids = a.block_tables + (int64_t)s * a.max_blocks + ta;
+  p.id0 = ids[min(lane, n - 1)];
+  p.idw = ids[min(NBUF - 1 + lane, n - 1)];
+}
+
 // One segment: tiles [ta, tb) of unit (h, qg, s). Leaves, per row group g,
 // the running reference max m_run[g] (log2 units, per query row c,
 // identical in the 4 lanes of a column), the column's partial sum l_run[g]
@@ -385,8 +459,8 @@ __device__ inline Rows<NG> rows_of(const DecodeArgs& a, int lane, int s, int h, 
 template <int D, bool STREAM, int NG, bool CAUSAL, int NBUF>
 __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int h,
                                        const Rows<NG>& rw, int ctx, int ta, int tb, bool store_new,
-                                       f32x4_t (&acc)[NG][D / 16], float (&m_run)[NG],
-                                       float (&l_run)[NG]) {
+                                       const SegPre<D, NG>& pre, f32x4_t (&acc)[NG][D / 16],
+                                       float (&m_run)[NG], float (&l_run)[NG]) {
   constexpr int KM = D / 32;   // score MFMAs per tile (k = 32 dims each)
   constexpr int VM = D / 16;   // value MFMAs per tile (16 dims each)
   const int c = lane & 15;
@@ -400,18 +474,7 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
     l_run[g] = 0.f;
   }
 
-  // Q as the B operand of the score MFMA: lane (c, r) holds row c, dims
-  // 32m + 8r .. +8. Rows past the group are zero.
-  bf16x8_t qv[NG][KM];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
-#pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
-      qv[g][m] = rw.valid[g] ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
+  const auto& qv = pre.qv;   // the query rows, loaded by segment_preload
 
   const int64_t tile_elems = 16 * D;
   const int64_t head_off = (int64_t)h * tile_elems;
@@ -610,8 +673,8 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   // The steady loop runs while every load it issues is inside the segment,
   // so its loads are unconditional and the compiler's waits on them stay
   // exact; the last (at most 2 NBUF - 2) tiles are computed after it.
-  const int id0 = ids_from(0);
-  int idw = ids_from(NBUF - 1);
+  const int id0 = pre.id0;   // ids of tiles 0 .. and NBUF - 1 .., from segment_preload
+  int idw = pre.idw;
   int j0 = 0;
   if (n >= 2 * NBUF - 1) {
 #pragma unroll
@@ -712,12 +775,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int tb = min(ta + tiles_per_part, nt);
 
   const Rows<1> rw = rows_of<1, false>(a, lane, s, h, qg, ctx);
+  SegPre<D, 1> pre;
+  segment_preload<D, 1, kRing>(a, lane, s, rw, ta, tb, pre);
   f32x4_t acc[1][VM];
   float m_run[1], l_run[1];
   const bool ok =
       shares_first_block(a, s)
-          ? process_segment<D, false, 1, false, kRing>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run)
-          : process_segment<D, true, 1, false, kRing>(a, lane, s, h, rw, ctx, ta, tb, false, acc, m_run, l_run);
+          ? process_segment<D, false, 1, false, kRing>(a, lane, s, h, rw, ctx, ta, tb, false, pre,
+                                                       acc, m_run, l_run)
+          : process_segment<D, true, 1, false, kRing>(a, lane, s, h, rw, ctx, ta, tb, false, pre,
+                                                      acc, m_run, l_run);
   finish_rows<D, 1>(a, lane, ok, ta == 0 && tb == nt, (int64_t)u * a.p_max + part, rw, acc, m_run,
                     l_run);
 }
@@ -774,10 +841,12 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
   pa.max_blocks = a.pre_tiles;
   pa.k_new = nullptr;
   pa.v_new = nullptr;
+  SegPre<D, kPrefixNG> pre;
+  segment_preload<D, kPrefixNG, NBUF>(pa, lane, 0, rw, ta, tb, pre);
   f32x4_t acc[kPrefixNG][VM];
   float m_run[kPrefixNG], l_run[kPrefixNG];
   const bool ok = process_segment<D, false, kPrefixNG, false, NBUF>(
-      pa, lane, 0, h, rw, a.pre_tiles * 16, ta, tb, false, acc, m_run, l_run);
+      pa, lane, 0, h, rw, a.pre_tiles * 16, ta, tb, false, pre, acc, m_run, l_run);
   if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
 #pragma unroll
   for (int g = 0; g < kPrefixNG; ++g)
@@ -803,7 +872,8 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
   if (w >= a.n_waves) return;
 
   TileScan ts;
-  const int per_row = tile_scan_total<PREFIX>(a, lane, ts);   // tiles of one (head, group)
+  constexpr bool KEEP = !CAUSAL;
+  const int per_row = tile_scan_total<PREFIX, KEEP>(a, lane, ts);   // tiles of one (head, group)
   const int n_hq = a.n_kv * a.n_qgroups;
   const int64_t t_seq = (int64_t)n_hq * per_row;
   const int64_t t_pre = PREFIX ? (int64_t)a.pre_units * a.pre_tiles : 0;
@@ -867,7 +937,7 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
       if (s >= a.num_seqs || (int)(cur - (int64_t)hq * per_row) == before) return;
       const int u = hq * a.num_seqs + s;
       const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups,
-                                              a.context_lens[s]);
+                                              scan_ctx<KEEP>(a, ts, s));
       finish_rows<D, NG>(a, lane, true, false, (int64_t)w + u, rw, zero, m0, l0);
     } else if (PREFIX && cur < total) {
       const int pu = (int)((cur - pre_origin) / a.pre_tiles);
@@ -890,7 +960,19 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
   tile_scan_locate<PREFIX>(a, lane, ts, (int)(cur - (int64_t)hq * per_row), s, before);
   if (s >= a.num_seqs) return;   // unreachable for consistent context lengths
   int pos = (int)(cur - (int64_t)hq * per_row) - before;   // tile within the unit
-  int ctx = a.context_lens[s];
+  int ctx = scan_ctx<KEEP>(a, ts, s);
+
+  // The first segment's query rows and block ids; later ones are loaded
+  // while the segment before them streams (decode; the verification pass
+  // loads each segment's at its start).
+  SegPre<D, NG> pre;
+  {
+    const int skip = PREFIX ? prefix_skip(a, s, ctx) : 0;
+    const int tb = (int)min((int64_t)unit_tiles<PREFIX>(a, s, ctx), pos + (end - cur));
+    segment_preload<D, NG, NBUF, !CAUSAL>(
+        a, lane, s, rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups, ctx),
+        skip + pos, skip + tb, pre);
+  }
 
   while (true) {
     const int nt = unit_tiles<PREFIX>(a, s, ctx);
@@ -908,32 +990,73 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
       a.unit_info[2 * u + 1] = w1 - w0 + 1;
     }
     const Rows<NG> rw = rows_of<NG, CAUSAL>(a, lane, s, h, qg, ctx);
+
+    // The next unit with work in this wave's range: the following
+    // sequence, or the next (head, group); past the last, the prefix
+    // units (after_last). The decode finds it and issues its preload now;
+    // the verification pass, whose registers are spoken for, after this
+    // segment.
+    const int64_t cur_next = cur + (tb - pos);
+    const bool more = cur_next < end;
+    bool after_last = false;
+    int hq2 = hq, s2 = s, ctx2 = ctx;
+    auto find_next = [&]() {
+      if (!more) return;
+      do {
+        if (++s2 == a.num_seqs) {
+          s2 = 0;
+          if (++hq2 >= n_hq) {
+            after_last = true;
+            break;
+          }
+        }
+        ctx2 = scan_ctx<KEEP>(a, ts, s2);
+      } while (unit_tiles<PREFIX>(a, s2, ctx2) == 0);
+    };
+    if (!CAUSAL) find_next();
+    SegPre<D, NG> pre2;
+    if (!CAUSAL && more && !after_last) {
+      const int skip2 = PREFIX ? prefix_skip(a, s2, ctx2) : 0;
+      const int tb2 = (int)min((int64_t)unit_tiles<PREFIX>(a, s2, ctx2), end - cur_next);
+      segment_preload<D, NG, NBUF>(
+          a, lane, s2,
+          rows_of<NG, CAUSAL>(a, lane, s2, hq2 / a.n_qgroups, hq2 % a.n_qgroups, ctx2), skip2,
+          skip2 + tb2, pre2);
+    }
+
     f32x4_t acc[NG][VM];
     float m_run[NG], l_run[NG];
     // a member reading the shared prefix through the prefix units reads
     // its own tiles once: streamed
     const bool ok =
-        skip == 0 && shares_first_block(a, s)
+        skip == 0 && scan_shares_first<KEEP>(a, ts, s)
             ? process_segment<D, false, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
-                                                          skip + tb, qg == 0, acc, m_run, l_run)
+                                                          skip + tb, qg == 0, pre, acc, m_run,
+                                                          l_run)
             : process_segment<D, true, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
-                                                         skip + tb, qg == 0, acc, m_run, l_run);
+                                                         skip + tb, qg == 0, pre, acc, m_run,
+                                                         l_run);
     finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
-    cur += tb - pos;
-    if (cur >= end) break;
-    // next unit with work: following sequence, or the next (head, group);
-    // after the last, the prefix units
+    cur = cur_next;
+    if (!more) break;
+    if (CAUSAL) find_next();
+    if (after_last) {
+      if (PREFIX && w_pre == 0 && a.pre_units > 0) prefix_walk(pre_origin);
+      return;
+    }
+    hq = hq2;
+    s = s2;
+    ctx = ctx2;
     pos = 0;
-    do {
-      if (++s == a.num_seqs) {
-        s = 0;
-        if (++hq >= n_hq) {
-          if (PREFIX && w_pre == 0 && a.pre_units > 0) prefix_walk(pre_origin);
-          return;
-        }
-      }
-      ctx = a.context_lens[s];
-    } while (unit_tiles<PREFIX>(a, s, ctx) == 0);
+    if (CAUSAL) {
+      const int skip2 = PREFIX ? prefix_skip(a, s, ctx) : 0;
+      const int tb2 = (int)min((int64_t)unit_tiles<PREFIX>(a, s, ctx), end - cur);
+      segment_preload<D, NG, NBUF, false>(
+          a, lane, s, rows_of<NG, CAUSAL>(a, lane, s, hq / a.n_qgroups, hq % a.n_qgroups, ctx),
+          skip2, skip2 + tb2, pre);
+    } else {
+      pre = pre2;
+    }
   }
 }
 
