@@ -589,12 +589,12 @@ int32_t pkv_prefix_evict(pkv_prefix_cache* pc, int32_t n_blocks);
 int32_t pkv_prefix_cached_blocks(const pkv_prefix_cache* pc);
 
 /* ------------------------------------------------------------------------
- * Continuous batching ([DSS] "Continuous batching": before every token step
- * the scheduler releases the cache blocks of finished sequences, admits
- * waiting requests into the freed space and runs one decode step for what
- * is resident; [M23] 23.3; [SLS] "Batching: static to continuous";
- * [DSS] "Scheduling: when prefill meets decode": when memory runs out a
- * sequence yields, its blocks discarded and recomputed on resumption).
+ * Continuous batching ([DSS] "Continuous batching": each step first frees
+ * the blocks of sequences that are done, then brings queued requests in
+ * while room remains, then decodes the batch that results; [M23] 23.3;
+ * [SLS] "Batching: static to continuous"; [DSS] "Scheduling: when prefill
+ * meets decode": a sequence that runs out of memory gives up its blocks
+ * and is recomputed when it comes back).
  *
  * Host only, not thread-safe. The batcher owns a block allocator of
  * num_blocks blocks and, if prefix_tokens > 0, the blocks of a shared prefix

@@ -1,12 +1,12 @@
 """Reference model of the continuous-batching scheduler -- TEST INFRASTRUCTURE ONLY.
 
 Plain Python over AllocatorModel, written from the pages:
-  * "Designing an LLM serving system", "Continuous batching": before every
-    token step the scheduler releases the blocks of finished sequences,
-    admits waiting requests into the freed space, and runs one decode step
-    for whatever is resident; "Paged attention": blocks allocated as a
-    sequence grows, a shared prefix's blocks pointed at by every request
-    that begins with it, copy on write of a shared block; "Scheduling: when
+  * "Designing an LLM serving system", "Continuous batching": a step frees
+    the blocks of sequences that are done, brings queued requests in while
+    room remains, then decodes the batch that results; "Paged attention":
+    blocks allocated as a sequence grows, a shared prefix's blocks pointed
+    at by every request that begins with it, copy on write of a shared
+    block; "Scheduling: when
     prefill meets decode": when memory runs out a sequence yields, its
     blocks discarded and recomputed when it resumes.
   * "Module 23: Serving", 23.3 (a waiting request takes a finished one's

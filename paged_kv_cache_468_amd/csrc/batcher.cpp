@@ -1,9 +1,9 @@
 // Continuous batching over the block allocator, host only.
 //
 // From the pages: "Designing an LLM serving system", "Continuous batching"
-// (before every token step the scheduler releases the cache blocks of
-// finished sequences, admits waiting requests into the freed space, and runs
-// one decode step for whatever is resident), "Paged attention" (blocks
+// (a step frees the blocks of sequences that are done, brings queued
+// requests in while room remains, then decodes the batch that results),
+// "Paged attention" (blocks
 // allocated as a sequence grows; requests that begin with the same prompt
 // point at the same prefix blocks; a shared block is copied on write) and
 // "Scheduling: when prefill meets decode" (when memory runs out mid

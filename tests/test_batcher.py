@@ -2,9 +2,9 @@
 model in oracle/batcher_model.py, and the invariants of the loop itself.
 No GPU needed.
 
-The loop ("Designing an LLM serving system", "Continuous batching"): before
-every token step, release the blocks of finished sequences, admit waiting
-requests into the freed space, run one decode step for the resident batch;
+The loop ("Designing an LLM serving system", "Continuous batching"): each
+step frees the blocks of sequences that are done, brings queued requests in
+while room remains, and decodes the batch that results;
 blocks allocated as sequences grow, prefix blocks shared and copied on
 write ("Paged attention"); preemption by recompute when memory runs out
 ("Scheduling: when prefill meets decode")."""
