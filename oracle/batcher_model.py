@@ -6,9 +6,8 @@ Plain Python over AllocatorModel, written from the pages:
     room remains, then decodes the batch that results; "Paged attention":
     blocks allocated as a sequence grows, a shared prefix's blocks pointed
     at by every request that begins with it, copy on write of a shared
-    block; "Scheduling: when
-    prefill meets decode": when memory runs out a sequence yields, its
-    blocks discarded and recomputed when it resumes.
+    block; "Scheduling: when prefill meets decode": when memory runs out a
+    sequence yields, its blocks discarded and recomputed when it resumes.
   * "Module 23: Serving", 23.3 (a waiting request takes a finished one's
     place at once).
 
