@@ -622,9 +622,11 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
     unif = torch.rand((B, q_len), device=dev, generator=gen)
     n_acc = torch.empty(B, dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    acc_ws = torch.empty(max(pkv.pkv_spec_accept_workspace_bytes(B, VOCAB), 1), dtype=torch.uint8,
+                         device=dev)
 
     def accept():
-        pkv.pkv_spec_accept(p_t, q_d, drafts, unif, n_acc, nxt, err_flag=S.err)
+        pkv.pkv_spec_accept(p_t, q_d, drafts, unif, n_acc, nxt, workspace=acc_ws, err_flag=S.err)
 
     def write(l):
         pkv.pkv_kv_write(S.k_pool[l], S.v_pool[l], k_src[l], v_src[l], S.bt, rows, pos,

@@ -463,16 +463,24 @@ int pkv_paged_prefill(float* out, const void* q, const void* k_pool,
  *                 the caller's)
  *   n_accepted:   device int32 [num_seqs] out: drafts kept (0 .. gamma)
  *   next_token:   device int32 [num_seqs] out: the drawn token
+ *   workspace:    device scratch of at least
+ *                 pkv_spec_accept_workspace_bytes(num_seqs, vocab) bytes
+ *                 (caller-owned, no initialisation needed; one call at a time)
  * A pass yields n_accepted + 1 tokens. gamma in [0, 64] (0: a plain draw
  * from p_0; q_draft and draft_tokens may then be null); vocab in
- * [1, 2097152]. A row with no positive weight draws token 0. Device errors: a
- * draft outside [0, vocab) sets PKV_DEVERR_TOKEN and that sequence's
- * outputs are -1. */
+ * [1, 2097152]. A row with no positive weight draws token 0. Two launches
+ * on `stream`: the weight sums of 2,048-entry tiles of the chosen rows,
+ * spread over 4-tile workgroups, into the workspace; then one workgroup per
+ * sequence for the draw. Host-checked errors: PKV_EINVAL for bad sizes or
+ * null pointers, PKV_EWORKSPACE. Device errors: a draft outside [0, vocab)
+ * sets PKV_DEVERR_TOKEN and that sequence's outputs are -1. Workspace
+ * bytes: 16 * num_seqs * ceil(vocab / 2048) (two float64 sums per tile). */
+size_t pkv_spec_accept_workspace_bytes(int32_t num_seqs, int32_t vocab);
 int pkv_spec_accept(const float* p_target, const float* q_draft,
                     const int32_t* draft_tokens, const float* uniforms,
                     int32_t num_seqs, int32_t gamma, int32_t vocab,
-                    int32_t* n_accepted, int32_t* next_token, int32_t* err_flag,
-                    void* stream);
+                    int32_t* n_accepted, int32_t* next_token, void* workspace,
+                    size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 /* Wavefronts of the decode's balanced split on the current device for this
  * shape: one per SIMD for head_dim 128 and two for head_dim 64 (fewer if the

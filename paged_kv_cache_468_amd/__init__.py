@@ -66,7 +66,9 @@ SIGNATURES = {
                                              _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _vp, _vp]),
-    "pkv_spec_accept": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "pkv_spec_accept_workspace_bytes": (_sz, [_i32, _i32]),
+    "pkv_spec_accept": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                       _vp, _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp]),
@@ -461,11 +463,17 @@ def pkv_paged_prefill(out, q, k_pool, v_pool, block_tables, context_lens, scale,
            "pkv_paged_prefill")
 
 
+def pkv_spec_accept_workspace_bytes(num_seqs, vocab):
+    return int(lib.pkv_spec_accept_workspace_bytes(num_seqs, vocab))
+
+
 def pkv_spec_accept(p_target, q_draft, draft_tokens, uniforms, n_accepted, next_token,
-                    err_flag=None, stream=None):
+                    workspace=None, err_flag=None, stream=None):
     """The acceptance rule: p_target fp32 [B, gamma+1, V], q_draft fp32
     [B, gamma, V], draft_tokens int32 [B, gamma], uniforms fp32 [B, gamma+1];
-    writes n_accepted and next_token (int32 [B])."""
+    writes n_accepted and next_token (int32 [B]). workspace: a torch uint8
+    CUDA tensor of at least pkv_spec_accept_workspace_bytes(B, V) bytes, or
+    None to have one allocated here. Returns the workspace."""
     torch = _torch()
     _dev(p_target, "p_target", torch.float32, 3)
     B, g1, V = p_target.shape
@@ -481,13 +489,18 @@ def pkv_spec_accept(p_target, q_draft, draft_tokens, uniforms, n_accepted, next_
         _dev(t, name, torch.int32, 1)
         if t.shape[0] != B:
             raise ValueError(f"{name}: one entry per sequence")
+    if workspace is None:
+        workspace = torch.empty(max(pkv_spec_accept_workspace_bytes(B, V), 1), dtype=torch.uint8,
+                                device=p_target.device)
+    ws = _dev(workspace, "workspace", torch.uint8, 1)
     _check(lib.pkv_spec_accept(_dev(p_target, "p_target", torch.float32),
                                _dev(q_draft, "q_draft", torch.float32) if gamma > 0 else None,
                                _dev(draft_tokens, "draft_tokens", torch.int32) if gamma > 0 else None,
                                _dev(uniforms, "uniforms", torch.float32), B, gamma, V,
                                _dev(n_accepted, "n_accepted", torch.int32),
-                               _dev(next_token, "next_token", torch.int32), _flag(err_flag),
-                               _stream(stream)), "pkv_spec_accept")
+                               _dev(next_token, "next_token", torch.int32), ws, workspace.numel(),
+                               _flag(err_flag), _stream(stream)), "pkv_spec_accept")
+    return workspace
 
 
 def pkv_kv_write(k_pool, v_pool, k_src, v_src, block_tables, seq_rows, positions, err_flag=None,

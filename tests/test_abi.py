@@ -203,3 +203,15 @@ def test_verify_host_checks():
     assert f(d, d, d, d, d, d, 4, 5, 16, 64, 8, 2, 128, 0.1, 257, d, 1 << 30, None, None) == pkv.PKV_EINVAL
     assert f(d, d, d, d, d, d, 0, 5, 16, 64, 8, 2, 128, 0.1, 256, None, 0, None, None) == pkv.PKV_OK
     assert f(d, d, d, d, d, d, 4, 5, 16, 64, 8, 2, 128, 0.1, 256, d, 16, None, None) == pkv.PKV_EWORKSPACE
+
+
+def test_accept_workspace_formula():
+    """Two float64 sums per 2,048-entry tile of every sequence's row."""
+    import paged_kv_cache_468_amd as pkv
+    assert pkv.pkv_spec_accept_workspace_bytes(64, 128256) == 16 * 64 * 63
+    assert pkv.pkv_spec_accept_workspace_bytes(1, 1) == 16
+    assert pkv.pkv_spec_accept_workspace_bytes(3, 2048) == 16 * 3
+    assert pkv.pkv_spec_accept_workspace_bytes(3, 2049) == 16 * 3 * 2
+    assert pkv.pkv_spec_accept_workspace_bytes(-1, 100) == 0
+    assert pkv.pkv_spec_accept_workspace_bytes(2, 0) == 0
+    assert pkv.pkv_spec_accept_workspace_bytes(2, 2097153) == 0

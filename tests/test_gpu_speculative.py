@@ -90,6 +90,9 @@ CASES = [  # seed, B, gamma, V
     (5, 4, 4, 128256),
     (6, 64, 0, 300),
     (7, 8, 64, 50),
+    (8, 16, 3, 8193),     # 5 tiles: the second 4-tile workgroup holds one tile
+    (9, 64, 4, 128256),   # the benchmark's batch and vocabulary (16 workgroups per sequence)
+    (10, 3, 2, 140000),   # 69 tiles: the draw's prefix sums over two rounds of 64
 ]
 
 
@@ -136,3 +139,40 @@ def test_bad_draft_flagged(pkv):
     assert n[2] == -1 and tok[2] == -1
     keep = [0, 1, 3]
     _compare(p[keep], q[keep], draft[keep], u[keep], n[keep], tok[keep])
+
+
+def test_workspace_reused_across_calls(pkv):
+    """One workspace for two calls in a row (a larger vocabulary, then a
+    smaller one): each call writes every tile sum it reads."""
+    import torch
+    p1, q1, d1, u1 = _case(21, 8, 3, 9000)
+    p2, q2, d2, u2 = _case(22, 5, 2, 700)
+    ws = torch.empty(pkv.pkv_spec_accept_workspace_bytes(8, 9000), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for p, q, d, u in ((p1, q1, d1, u1), (p2, q2, d2, u2)):
+        B = p.shape[0]
+        n = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        tok = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        pkv.pkv_spec_accept(torch.from_numpy(p).cuda(), torch.from_numpy(q).cuda(),
+                            torch.from_numpy(d).cuda(), torch.from_numpy(u).cuda(), n, tok,
+                            workspace=ws)
+        outs.append((n, tok))
+    torch.cuda.synchronize()
+    for (p, q, d, u), (n, tok) in zip(((p1, q1, d1, u1), (p2, q2, d2, u2)), outs):
+        _compare(p, q, d, u, n.cpu().numpy(), tok.cpu().numpy())
+
+
+def test_workspace_too_small_refused(pkv):
+    import torch
+    p, q, draft, u = _case(23, 4, 2, 5000)
+    need = pkv.pkv_spec_accept_workspace_bytes(4, 5000)
+    assert need == 16 * 4 * 3
+    n = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError) as info:
+        pkv.pkv_spec_accept(torch.from_numpy(p).cuda(), torch.from_numpy(q).cuda(),
+                            torch.from_numpy(draft).cuda(), torch.from_numpy(u).cuda(), n, n.clone(),
+                            workspace=torch.empty(need - 8, dtype=torch.uint8, device="cuda"))
+    assert info.value.status == pkv.PKV_EWORKSPACE
+    torch.cuda.synchronize()
+    assert (n.cpu().numpy() == -7).all()
