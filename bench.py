@@ -138,6 +138,9 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
     S.shared_blocks = (np.array([int((tables[s, :n_prefix] == prefix[:n_prefix]).sum())
                                  for s in range(B)], np.int64) if n_prefix else np.zeros(B, np.int64))
     S.prefix_shared_tokens = BLOCK * n_prefix if n_prefix and S.shared_blocks.any() else 0
+    # the prefix's block ids, and the sequences past it (placed first)
+    S.prefix_ids = prefix[:n_prefix].copy() if n_prefix else np.zeros(0, np.int32)
+    S.past_prefix = int((cl > shape.prefix_tokens).sum()) if n_prefix else 0
     S.ctx = cl.copy()
     S.tables, S.nblk, S.num_blocks, S.max_blocks = tables, nblk, num_blocks, max_blocks
     S.max_ctx = int(final_ctx.max())
@@ -583,13 +586,16 @@ def stored_traffic(workload, kernel, kernel_file="paged_attn_balanced"):
     return per[kernel], None
 
 
-def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
+def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True, prefix_kernel=True):
     """The verification pass of speculative decoding on the decode bench's
     state: per layer, pkv_kv_write of the q_len new tokens of every sequence
-    (at positions ctx - q_len .. ctx - 1) and pkv_paged_attn_verify; then
-    once, pkv_spec_accept over a 128,256-token vocabulary. The contexts
-    stay fixed between steps (the tokens are rewritten in place); the KV
-    bytes per step are those of the decode at the same contexts."""
+    (at positions ctx - q_len .. ctx - 1) and the verification attention;
+    then once, pkv_spec_accept over a 128,256-token vocabulary. With a
+    shared prefix (and prefix_kernel) the attention is
+    pkv_paged_attn_verify_prefix over the sequences past the prefix (placed
+    first), else pkv_paged_attn_verify. The contexts stay fixed between
+    steps (the tokens are rewritten in place); the KV bytes per step are
+    those of the decode at the same contexts."""
     sh, L, B = S.shape, S.shape.n_layers, S.B
     dev = torch.device("cuda")
     base = 7000
@@ -604,9 +610,15 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
     pos = (ctx.repeat_interleave(q_len) - q_len +
            torch.arange(q_len, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
     S.cl.copy_(ctx)
-    ws = torch.empty(max(pkv.pkv_verify_workspace_bytes(B, q_len, sh.n_q, sh.n_kv, sh.d,
-                                                        S.max_ctx), 1),
-                     dtype=torch.uint8, device=dev)
+    use_prefix = prefix_kernel and S.share and len(S.prefix_ids) > 0 and S.past_prefix > 0
+    # (measured slower than the plain pass at the LLaMA-3-8B shape: off by default)
+    if use_prefix:
+        pre_ids = torch.from_numpy(S.prefix_ids).to(dev)
+        ws_bytes = pkv.pkv_verify_prefix_workspace_bytes(B, q_len, sh.n_q, sh.n_kv, sh.d, S.max_ctx,
+                                                         len(S.prefix_ids), S.past_prefix)
+    else:
+        ws_bytes = pkv.pkv_verify_workspace_bytes(B, q_len, sh.n_q, sh.n_kv, sh.d, S.max_ctx)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     # the acceptance rule once per step over a LLaMA-3 sized vocabulary:
     # target probabilities for the q_len positions, draft probabilities for
@@ -633,8 +645,13 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
                          err_flag=S.err)
 
     def verify(l):
-        pkv.pkv_paged_attn_verify(out[l], q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale,
-                                  S.max_ctx, workspace=ws, err_flag=S.err)
+        if use_prefix:
+            pkv.pkv_paged_attn_verify_prefix(out[l], q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl,
+                                             sh.scale, S.max_ctx, pre_ids, 0, S.past_prefix,
+                                             workspace=ws, err_flag=S.err)
+        else:
+            pkv.pkv_paged_attn_verify(out[l], q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale,
+                                      S.max_ctx, workspace=ws, err_flag=S.err)
 
     for _ in range(warmup):
         for l in range(L):
@@ -692,7 +709,9 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True):
             "verify_alg_bytes_logical": alg,
             "verify_gbs": alg_u / (verify_us * 1e-6) / 1e9,
             "verify_gbs_logical": alg / (verify_us * 1e-6) / 1e9,
-            "query_tokens_per_s": B * q_len / (ms * 1e-3)}
+            "query_tokens_per_s": B * q_len / (ms * 1e-3),
+            "verify_call": ("pkv_paged_attn_verify_prefix over the sequences past the prefix"
+                            if use_prefix else "pkv_paged_attn_verify")}
 
 
 def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=True):
@@ -1014,6 +1033,9 @@ def main():
                          "one layer); 0 skips it")
     ap.add_argument("--verify-tokens", type=int, default=0,
                     help="speculative verification instead: this many query tokens per sequence")
+    ap.add_argument("--verify-prefix-kernel", action="store_true",
+                    help="verification pass: pkv_paged_attn_verify_prefix over the sequences past "
+                         "the shared prefix instead of pkv_paged_attn_verify")
     ap.add_argument("--prefill-chunk", type=int, default=0,
                     help="chunked prefill instead: chunk tokens per sequence on top of cached context")
     ap.add_argument("--prefill-batch", type=int, default=8)
@@ -1067,11 +1089,12 @@ def main():
     if args.verify_tokens > 0:
         log(f"[bench] verification pass, {args.verify_tokens} query tokens, {wname}")
         share_v = shape.prefix_tokens > 0 and not args.no_share
-        S = build_state(pkv, torch, shape, args.seed, share_v, extra, 0)
+        S = build_state(pkv, torch, shape, args.seed, share_v, extra, 0,
+                        prefix_kernel=not args.no_prefix_kernel)
         dec = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
         log(f"[bench] decode on the same state: {dec['ms_per_step']:.3f} ms/step")
         vr = verify_bench(pkv, torch, S, args.verify_tokens, args.steps, args.warmup,
-                          graph=not args.no_graph)
+                          graph=not args.no_graph, prefix_kernel=args.verify_prefix_kernel)
         log(f"[bench] verify: {vr['ms_per_step']:.3f} ms/step, write {vr['write_us']:.1f} us, "
             f"verify {vr['verify_us']:.1f} us per layer")
         vtraffic, vwhy = (stored_traffic(f"llama3-8b-verify{args.verify_tokens}", "paged_attn_verify",
@@ -1089,6 +1112,7 @@ def main():
                        "head_dim": shape.d, "shared_prefix_tokens": shape.prefix_tokens if share_v else 0},
             "step_mode": vr["step_mode"], "decode_ms_per_step": dec["ms_per_step"],
             "verify_over_decode": vr["ms_per_step"] / dec["ms_per_step"],
+            "verify_call": vr["verify_call"],
             "kv_gbs_logical": vr["kv_gbs"], "kv_gbs_unique": vr["kv_gbs_unique"],
             "query_tokens_per_s": vr["query_tokens_per_s"],
             "kernels_us": {"kv_write": vr["write_us"], "paged_attn_verify": vr["verify_us"],

@@ -414,6 +414,50 @@ int pkv_paged_attn_verify(float* out, const void* q, const void* k_pool,
                           size_t workspace_bytes, int32_t* err_flag,
                           void* stream);
 
+/* The verification pass for a batch whose member sequences share a prompt
+ * prefix held once in the pools ([SLS] "Reuse shared prefixes"; [M23] 23.5;
+ * [DSS] "Paged attention": shared blocks are reference-counted). The result
+ * is that of pkv_paged_attn_verify on the same arguments, to fp32 rounding
+ * (the softmax is merged in another order). Sequences prefix_first_seq ..
+ * prefix_first_seq + prefix_num_seqs - 1 are the members. A member whose
+ * query tokens all lie after the prefix (context_lens[s] - q_len >=
+ * 16 * prefix_blocks) must hold prefix_table's ids as its first
+ * prefix_blocks table entries: the prefix's tiles are then read once for
+ * all such members, as prefix units of the balanced split that serve 32
+ * member rows (query token, head) per K/V tile, and each member's own unit
+ * covers only its later tiles; the merge kernel combines both and checks
+ * every such member's table at each call (one whose table differs there
+ * gets NaN rows and PKV_DEVERR_PREFIX). Any other member, and every
+ * sequence outside the range, runs as in pkv_paged_attn_verify.
+ *   prefix_table : device int32 [prefix_blocks], the prefix's block ids
+ *   workspace    : at least pkv_verify_prefix_workspace_bytes(...) bytes (the
+ *                  verification pass's workspace, then the prefix units'
+ *                  bookkeeping and partials); no initialisation needed
+ * q_len in [1, 64]. Other arguments, host-checked errors and device errors
+ * as for pkv_paged_attn_verify and pkv_decode_step_prefix; prefix_blocks = 0
+ * or prefix_num_seqs = 0 runs pkv_paged_attn_verify's computation. Two
+ * launches on `stream`. */
+size_t pkv_verify_prefix_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                         int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t head_dim,
+                                         int32_t max_context_len,
+                                         int32_t prefix_blocks,
+                                         int32_t prefix_num_seqs);
+int pkv_paged_attn_verify_prefix(float* out, const void* q, const void* k_pool,
+                                 const void* v_pool,
+                                 const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t q_len, int32_t max_blocks_per_seq,
+                                 int32_t num_blocks, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 float scale, int32_t max_context_len,
+                                 const int32_t* prefix_table,
+                                 int32_t prefix_blocks,
+                                 int32_t prefix_first_seq,
+                                 int32_t prefix_num_seqs, void* workspace,
+                                 size_t workspace_bytes, int32_t* err_flag,
+                                 void* stream);
+
 /* ------------------------------------------------------------------------
  * Chunked prefill against the paged cache ([SLS] "Split long prefills into
  * chunks": a long prompt is taken a chunk per step beside the ongoing

@@ -64,6 +64,10 @@ SIGNATURES = {
     "pkv_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_verify_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_verify_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
+                                                    _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _vp, _vp]),
     "pkv_spec_accept_workspace_bytes": (_sz, [_i32, _i32]),
@@ -436,6 +440,49 @@ def pkv_paged_attn_verify(out, q, k_pool, v_pool, block_tables, context_lens, sc
                                      block_tables.shape[1], nb, n_q, n_kv, d, float(scale),
                                      int(max_context_len), ws, workspace.numel(), _flag(err_flag),
                                      _stream(stream)), "pkv_paged_attn_verify")
+    return workspace
+
+
+def pkv_verify_prefix_workspace_bytes(num_seqs, q_len, n_q_heads, n_kv_heads, head_dim,
+                                      max_context_len, prefix_blocks, prefix_num_seqs):
+    return int(lib.pkv_verify_prefix_workspace_bytes(num_seqs, q_len, n_q_heads, n_kv_heads,
+                                                     head_dim, max_context_len, prefix_blocks,
+                                                     prefix_num_seqs))
+
+
+def pkv_paged_attn_verify_prefix(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                                 max_context_len, prefix_table, prefix_first_seq,
+                                 prefix_num_seqs, workspace=None, err_flag=None, stream=None):
+    """The verification pass with a shared prefix read once for the member
+    sequences prefix_first_seq .. + prefix_num_seqs - 1: prefix_table a
+    torch int32 CUDA tensor of the prefix's block ids (its length is the
+    prefix's block count). Other arguments as for pkv_paged_attn_verify;
+    workspace of at least pkv_verify_prefix_workspace_bytes(...) bytes, or
+    None to have one allocated here. Returns the workspace."""
+    torch = _torch()
+    nb, n_kv, d = _pool_dims(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(out, "out", torch.float32, 4)
+    B, q_len, n_q, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out: expected [num_seqs, q_len, n_q, head_dim], the same shape")
+    bt = _dev(block_tables, "block_tables", torch.int32, 2)
+    cl = _dev(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens: one row per sequence")
+    pt = _dev(prefix_table, "prefix_table", torch.int32, 1)
+    n_pre = prefix_table.shape[0]
+    need = pkv_verify_prefix_workspace_bytes(B, q_len, n_q, n_kv, d, max_context_len, n_pre,
+                                             prefix_num_seqs) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_paged_attn_verify_prefix(
+        _dev(out, "out", torch.float32), _dev(q, "q", torch.bfloat16),
+        _dev(k_pool, "k_pool", torch.bfloat16), _dev(v_pool, "v_pool", torch.bfloat16), bt, cl, B,
+        q_len, block_tables.shape[1], nb, n_q, n_kv, d, float(scale), int(max_context_len), pt,
+        n_pre, int(prefix_first_seq), int(prefix_num_seqs), ws, workspace.numel(),
+        _flag(err_flag), _stream(stream)), "pkv_paged_attn_verify_prefix")
     return workspace
 
 

@@ -106,9 +106,15 @@ constexpr int kPrefixNG = 2;
 constexpr int kPrefixRows = 16 * kPrefixNG;
 // Time per tile of a wave that reads only a shared prefix's tiles (from
 // L2), relative to a wave streaming tiles from HBM: the prefix's share of
-// the waves (see balanced_body).
+// the waves (see balanced_body). Measured best: 2/3 for the decode (4
+// rows per member tile, 32 per prefix tile); 1/2 for the verification pass
+// (its member tiles carry q_len times the rows, so they cost relatively
+// more): 192.0 us per LLaMA-3-8B layer at 5 query tokens, against 194.9
+// at 2/3 and 203.6 at 1.
 constexpr int kPrefixCostNum = 2;
 constexpr int kPrefixCostDen = 3;
+constexpr int kVerifyPrefixCostNum = 1;
+constexpr int kVerifyPrefixCostDen = 2;
 constexpr float kRescaleSlack = 8.0f; // log2 units a tile max may exceed the reference
 
 struct DecodeArgs {
@@ -148,9 +154,10 @@ struct DecodeArgs {
   // slot and partial count. pre_tiles = 0: no prefix.
   const int32_t* pre_table;
   int pre_first, pre_count, pre_tiles;
-  int pre_qgroups;   // row groups per KV head: ceil(pre_count * group / kPrefixRows)
+  int pre_qgroups;   // row groups per KV head: ceil(pre_count * qrows / kPrefixRows)
   int pre_units;     // n_kv * pre_qgroups
   int32_t* pre_info; // [pre_units][2]
+  int pre_cost_num, pre_cost_den;   // relative time per prefix tile (see kPrefixCostNum)
   float* pre_ml;     // [slots][kPrefixRows][2]
   float* pre_acc;    // [slots][kPrefixRows][D]
 };
@@ -195,14 +202,15 @@ __device__ inline int seq_tiles(int ctx, int q_len, int max_ctx) {
 }
 
 // Tiles of sequence s read through the shared prefix (the prefix units'
-// partials): all of them for a member whose last tile lies after the
-// prefix (such a member holds the prefix's blocks as its first table
-// entries; the merge checks that, and turns a member that does not into
-// NaN rows), none otherwise (its context ends inside the prefix, so the
-// block it writes is not a prefix block).
+// partials): all of them for a member whose query tokens (positions
+// ctx - q_len .. ctx - 1; the decode's one new token) all lie after the
+// prefix, so that every query row sees the whole prefix and no token it
+// writes is in a prefix block (such a member holds the prefix's blocks as
+// its first table entries; the merge checks that, and turns a member that
+// does not into NaN rows); none otherwise.
 __device__ inline int prefix_skip(const DecodeArgs& a, int s, int ctx) {
   return (a.pre_tiles > 0 && (unsigned)(s - a.pre_first) < (unsigned)a.pre_count &&
-          ((ctx - 1) >> 4) >= a.pre_tiles)
+          ctx - a.q_len >= 16 * a.pre_tiles)
              ? a.pre_tiles
              : 0;
 }
@@ -811,17 +819,21 @@ __device__ inline void write_prefix_partial(const DecodeArgs& a, int lane, bool 
   for (int m = 0; m < VM; ++m) *(f32x4_t*)(o + 16 * m) = acc[m];
 }
 
-// The rows of prefix unit pu: (member i, head jj of KV head h's group),
-// row i * group + jj, rows qg * 32 .. qg * 32 + 31 of KV head h (two
-// groups of 16).
+// The rows of prefix unit pu: a member's qrows rows (query token i, head
+// jj of KV head h's group; the decode's one token), row
+// member * qrows + i * group + jj, rows qg * 32 .. qg * 32 + 31 of KV head h
+// (two groups of 16). Every prefix position is visible to all of them.
 __device__ inline Rows<kPrefixNG> prefix_rows(const DecodeArgs& a, int lane, int h, int qg) {
   Rows<kPrefixNG> rw;
 #pragma unroll
   for (int g = 0; g < kPrefixNG; ++g) {
     const int gr = qg * kPrefixRows + 16 * g + (lane & 15);
-    rw.valid[g] = gr < a.pre_count * a.group;
-    const int member = gr / a.group;
-    rw.index[g] = (int64_t)(a.pre_first + member) * a.n_q + h * a.group + (gr - member * a.group);
+    rw.valid[g] = gr < a.pre_count * a.qrows;
+    const int member = gr / a.qrows;
+    const int rem = gr - member * a.qrows;
+    const int i = rem / a.group;
+    rw.index[g] = ((int64_t)(a.pre_first + member) * a.q_len + i) * a.n_q + h * a.group +
+                  (rem - i * a.group);
     rw.lim[g] = 0x7fffffff;
   }
   return rw;
@@ -859,7 +871,7 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
 // sequences' tiles that way, and the last Wp waves split the prefix units'
 // tiles, in (KV head, row group, tile) order. Wp follows from the tile
 // counts and the relative cost of a prefix tile (a wave that reads only
-// L2-resident prefix tiles takes about kPrefixCostNum / kPrefixCostDen of
+// L2-resident prefix tiles takes about pre_cost_num / pre_cost_den of
 // the time per tile of a wave streaming from HBM), so both classes end
 // together. (With a single wave, one order holds both.) The wave holding
 // a unit's first tile records, for the merge kernel, the unit's first
@@ -882,8 +894,8 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
     if (t_seq == 0) {
       w_pre = a.n_waves;
     } else {
-      const int64_t num = (int64_t)a.n_waves * kPrefixCostNum * t_pre;
-      const int64_t den = t_seq * kPrefixCostDen + (int64_t)kPrefixCostNum * t_pre;
+      const int64_t num = (int64_t)a.n_waves * a.pre_cost_num * t_pre;
+      const int64_t den = t_seq * a.pre_cost_den + (int64_t)a.pre_cost_num * t_pre;
       w_pre = (int)max((int64_t)1, min((int64_t)a.n_waves - 1, (num + den / 2) / den));
     }
   }
@@ -1072,10 +1084,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
 // them, NG groups of 16 rows per wave. Held to two waves per SIMD's
 // registers even with two groups (a couple of spilled values at head_dim
 // 128): measured faster than one wave with no spills, as the compiler then
-// schedules the loads of the next tile further ahead.
-template <int D, int NG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_attn_verify_kernel(DecodeArgs a) {
-  balanced_body<D, NG, true, kRing, false>(a);
+// schedules the loads of the next tile further ahead. PREFIX: the split
+// also holds a shared prefix's units (pkv_paged_attn_verify_prefix; a
+// prefix row is a member's (query token, head) pair); at head_dim 128 that
+// instance needs more registers than two waves per SIMD hold, and runs one.
+template <int D, int NG, bool PREFIX = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PREFIX && D == 128 ? 1 : 2))) void paged_attn_verify_kernel(DecodeArgs a) {
+  balanced_body<D, NG, true, kRing, PREFIX>(a);
 }
 
 // Chunked prefill with the K/V tiles staged in LDS. A workgroup of
@@ -1425,7 +1440,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(DecodeArgs a) {
   int64_t pre_row = 0;
   const bool member = prefix_skip(a, s, ctx) > 0;
   if (member) {
-    const int pr = (s - a.pre_first) * a.group + gr;
+    const int pr = (s - a.pre_first) * a.qrows + gr;
     const int2 pinfo = *(const int2*)(a.pre_info + 2 * (h * a.pre_qgroups + pr / kPrefixRows));
     np = pinfo.y;
     pre_row = (int64_t)pinfo.x * kPrefixRows + (pr % kPrefixRows);
@@ -1575,12 +1590,19 @@ static int occupancy_blocks(K kernel) {
   return blocks;
 }
 
-static int kernel_blocks_per_cu(const Geom& g, int head_dim) {
+static int kernel_blocks_per_cu(const Geom& g, int head_dim, bool prefix) {
   if (!g.causal)
     // both instantiations hold the same waves per SIMD (one at head_dim
     // 128, two at 64)
     return head_dim == 128 ? occupancy_blocks(paged_attn_balanced_kernel<128, false>)
                            : occupancy_blocks(paged_attn_balanced_kernel<64, false>);
+  if (prefix) {
+    if (g.ng == 1)
+      return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 1, true>)
+                             : occupancy_blocks(paged_attn_verify_kernel<64, 1, true>);
+    return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 2, true>)
+                           : occupancy_blocks(paged_attn_verify_kernel<64, 2, true>);
+  }
   if (g.ng == 1)
     return head_dim == 128 ? occupancy_blocks(paged_attn_verify_kernel<128, 1>)
                            : occupancy_blocks(paged_attn_verify_kernel<64, 1>);
@@ -1588,16 +1610,19 @@ static int kernel_blocks_per_cu(const Geom& g, int head_dim) {
                          : occupancy_blocks(paged_attn_verify_kernel<64, 2>);
 }
 
-static int resident_waves(const Geom& g, int head_dim) {
-  static int cache[3][2][64];   // [kernel: decode, verify 1 group, verify 2][head_dim == 128][device]
+// prefix: the verification pass's instance with a shared prefix's units.
+static int resident_waves(const Geom& g, int head_dim, bool prefix = false) {
+  // [kernel: decode, verify 1 group, verify 2, the same with a prefix][head_dim == 128][device]
+  static int cache[5][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  const int kind = !g.causal ? 0 : (g.ng == 1 ? 1 : 2);
+  const bool pre = prefix && g.causal;
+  const int kind = !g.causal ? 0 : (g.ng == 1 ? (pre ? 3 : 1) : (pre ? 4 : 2));
   int& slot = cache[kind][head_dim == 128][dev];
   if (slot > 0) return slot;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const int blocks = kernel_blocks_per_cu(g, head_dim);
+  const int blocks = kernel_blocks_per_cu(g, head_dim, pre);
   if (blocks < 1 || cus < 1) return -1;
   // the decode's split uses one wave per SIMD (4 per compute unit) for
   // head_dim 128 and two for head_dim 64, whose tiles are half the bytes:
@@ -1637,12 +1662,12 @@ static size_t workspace_bytes(const Geom& g, int d, int max_ctx, int part) {
 // unit's first slot and count, then its partial slots, 16 rows each. A
 // prefix unit's slot is wave + unit, as for the decode's units, so there
 // are at most (waves + units) slots.
-static int prefix_qgroups(int group, int count) {
-  return (int)(((int64_t)count * group + kPrefixRows - 1) / kPrefixRows);
+static int prefix_qgroups(int rows_per_member, int count) {
+  return (int)(((int64_t)count * rows_per_member + kPrefixRows - 1) / kPrefixRows);
 }
 
 static size_t prefix_bytes(const Geom& g, int d, int max_ctx, int count) {
-  const int64_t units = (int64_t)g.n_kv * prefix_qgroups(g.n_q / g.n_kv, count);
+  const int64_t units = (int64_t)g.n_kv * prefix_qgroups(g.qrows(), count);
   const int64_t slots = split_wave_cap(g, max_ctx) + units;
   return (size_t)((units * 8 + 255) / 256 * 256) +
          (size_t)slots * kPrefixRows * (2 + d) * sizeof(float);
@@ -1697,7 +1722,7 @@ static int prepare(DecodeArgs& a, int& head_dim_out, const Geom& g, float* out, 
                    const int32_t* context_lens, int32_t max_blocks_per_seq, int32_t num_blocks,
                    int32_t head_dim, float scale, int32_t max_context_len,
                    int32_t partition_tokens, void* workspace, size_t workspace_bytes_given,
-                   int32_t* err_flag, bool split = true) {
+                   int32_t* err_flag, bool split = true, bool prefix_units = false) {
   const int32_t num_seqs = g.num_seqs;
   if (num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || g.n_q < 1 || g.n_kv < 1 ||
       max_context_len < 1)
@@ -1735,6 +1760,8 @@ static int prepare(DecodeArgs& a, int& head_dim_out, const Geom& g, float* out, 
   a.pre_table = nullptr;
   a.pre_first = a.pre_count = a.pre_tiles = 0;
   a.pre_qgroups = a.pre_units = 0;
+  a.pre_cost_num = kPrefixCostNum;
+  a.pre_cost_den = kPrefixCostDen;
   a.pre_info = nullptr;
   a.pre_ml = a.pre_acc = nullptr;
   head_dim_out = head_dim;
@@ -1770,7 +1797,7 @@ static int prepare(DecodeArgs& a, int& head_dim_out, const Geom& g, float* out, 
     if (waves > (int64_t)INT32_MAX / 2) return PKV_EINVAL;
     a.n_waves = 0;
   } else {
-    const int res = resident_waves(g, head_dim);
+    const int res = resident_waves(g, head_dim, prefix_units);
     if (res < 1) return PKV_EHIP;
     const int64_t cap = split_wave_cap(g, max_context_len);
     waves = res < cap ? res : cap;
@@ -1805,6 +1832,20 @@ static int launch_partition(const DecodeArgs& a, int head_dim, hipStream_t st) {
 static int launch_verify(const DecodeArgs& a, int head_dim, hipStream_t st) {
   const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
   const bool two = a.group_rows == 32;
+  if (a.pre_tiles > 0) {   // a shared prefix's units in the split
+    if (head_dim == 128) {
+      if (two)
+        hipLaunchKernelGGL((paged_attn_verify_kernel<128, 2, true>), dim3(grid), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((paged_attn_verify_kernel<128, 1, true>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      if (two)
+        hipLaunchKernelGGL((paged_attn_verify_kernel<64, 2, true>), dim3(grid), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((paged_attn_verify_kernel<64, 1, true>), dim3(grid), dim3(256), 0, st, a);
+    }
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+  }
   if (head_dim == 128) {
     if (two)
       hipLaunchKernelGGL((paged_attn_verify_kernel<128, 2>), dim3(grid), dim3(256), 0, st, a);
@@ -1925,6 +1966,34 @@ static bool valid_prefix_args(int32_t num_seqs, int32_t max_blocks_per_seq,
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The shared prefix's part of a call (decode or verification pass): the
+// prefix units' bookkeeping and partials after the call's own workspace.
+static int attach_prefix(DecodeArgs& a, const Geom& g, int head_dim, int max_ctx, void* workspace,
+                         size_t workspace_bytes_given, const int32_t* prefix_table,
+                         int32_t prefix_blocks, int32_t prefix_first_seq,
+                         int32_t prefix_num_seqs) {
+  const size_t base = round256(workspace_bytes(g, head_dim, max_ctx, 0));
+  if (workspace_bytes_given < base + prefix_bytes(g, head_dim, max_ctx, prefix_num_seqs))
+    return PKV_EWORKSPACE;
+  a.pre_table = prefix_table;
+  a.pre_first = prefix_first_seq;
+  a.pre_count = prefix_num_seqs;
+  a.pre_tiles = prefix_blocks;
+  a.pre_cost_num = g.causal ? kVerifyPrefixCostNum : kPrefixCostNum;
+  a.pre_cost_den = g.causal ? kVerifyPrefixCostDen : kPrefixCostDen;
+  a.pre_qgroups = prefix_qgroups(g.qrows(), prefix_num_seqs);
+  const int64_t units = (int64_t)g.n_kv * a.pre_qgroups;
+  // tile indices of the split (sequences' and prefix units') fit 62 bits;
+  // the unit and slot counts fit 32
+  if (units > (int64_t)INT32_MAX / 64) return PKV_EINVAL;
+  a.pre_units = (int)units;
+  a.pre_info = (int32_t*)((char*)workspace + base);
+  a.pre_ml = (float*)((char*)workspace + base + (units * 8 + 255) / 256 * 256);
+  const int64_t slots = split_wave_cap(g, max_ctx) + units;
+  a.pre_acc = a.pre_ml + 2 * kPrefixRows * slots;
+  return PKV_OK;
+}
+
 extern "C" size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                                     int32_t n_kv_heads, int32_t head_dim,
                                                     int32_t max_context_len, int32_t prefix_blocks,
@@ -1958,24 +2027,10 @@ extern "C" int pkv_decode_step_prefix(float* out, const void* q, const void* k_n
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
   if (prefix_blocks > 0 && prefix_num_seqs > 0) {
-    const Geom g = decode_geom(num_seqs, n_q_heads, n_kv_heads);
-    const size_t base = round256(workspace_bytes(g, head_dim, max_context_len, 0));
-    if (workspace_bytes_given < base + prefix_bytes(g, head_dim, max_context_len, prefix_num_seqs))
-      return PKV_EWORKSPACE;
-    a.pre_table = prefix_table;
-    a.pre_first = prefix_first_seq;
-    a.pre_count = prefix_num_seqs;
-    a.pre_tiles = prefix_blocks;
-    a.pre_qgroups = prefix_qgroups(a.group, prefix_num_seqs);
-    const int64_t units = (int64_t)n_kv_heads * a.pre_qgroups;
-    // tile indices of the split (sequences' and prefix units') fit 62 bits;
-    // the unit and slot counts fit 32
-    if (units > (int64_t)INT32_MAX / 64) return PKV_EINVAL;
-    a.pre_units = (int)units;
-    a.pre_info = (int32_t*)((char*)workspace + base);
-    a.pre_ml = (float*)((char*)workspace + base + (units * 8 + 255) / 256 * 256);
-    const int64_t slots = split_wave_cap(g, max_context_len) + units;
-    a.pre_acc = a.pre_ml + 2 * kPrefixRows * slots;
+    const int prc = attach_prefix(a, decode_geom(num_seqs, n_q_heads, n_kv_heads), head_dim,
+                                  max_context_len, workspace, workspace_bytes_given, prefix_table,
+                                  prefix_blocks, prefix_first_seq, prefix_num_seqs);
+    if (prc != PKV_OK) return prc;
   }
   const hipStream_t st = (hipStream_t)stream;
   const int prc = launch_partition(a, d, st);
@@ -2003,6 +2058,48 @@ extern "C" int pkv_paged_attn_verify(float* out, const void* q, const void* k_po
                          num_blocks, head_dim, scale, max_context_len, 0, workspace,
                          workspace_bytes_given, err_flag);
   if (rc != PKV_OK || num_seqs == 0) return rc;
+  const int vrc = launch_verify(a, d, (hipStream_t)stream);
+  return vrc != PKV_OK ? vrc : launch_merge(a, d, (hipStream_t)stream);
+}
+
+extern "C" size_t pkv_verify_prefix_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                                    int32_t n_q_heads, int32_t n_kv_heads,
+                                                    int32_t head_dim, int32_t max_context_len,
+                                                    int32_t prefix_blocks,
+                                                    int32_t prefix_num_seqs) {
+  if (!valid_heads(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len)) return 0;
+  if (q_len < 1 || q_len > kMaxQueryTokens) return 0;
+  const Geom g = verify_geom(num_seqs, q_len, n_q_heads, n_kv_heads);
+  const size_t base = workspace_bytes(g, head_dim, max_context_len, 0);
+  if (prefix_blocks <= 0 || prefix_num_seqs <= 0) return base;
+  return round256(base) + prefix_bytes(g, head_dim, max_context_len, prefix_num_seqs);
+}
+
+extern "C" int pkv_paged_attn_verify_prefix(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t q_len,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+    int32_t head_dim, float scale, int32_t max_context_len, const int32_t* prefix_table,
+    int32_t prefix_blocks, int32_t prefix_first_seq, int32_t prefix_num_seqs, void* workspace,
+    size_t workspace_bytes_given, int32_t* err_flag, void* stream) {
+  if (q_len < 1 || q_len > kMaxQueryTokens || n_kv_heads < 1) return PKV_EINVAL;
+  if (!valid_prefix_args(num_seqs, max_blocks_per_seq, prefix_table, prefix_blocks,
+                         prefix_first_seq, prefix_num_seqs))
+    return PKV_EINVAL;
+  const Geom g = verify_geom(num_seqs, q_len, n_q_heads, n_kv_heads);
+  const bool pre = prefix_blocks > 0 && prefix_num_seqs > 0;
+  DecodeArgs a;
+  int d = 0;
+  const int rc = prepare(a, d, g, out, q, k_pool, v_pool, block_tables, context_lens,
+                         max_blocks_per_seq, num_blocks, head_dim, scale, max_context_len, 0,
+                         workspace, workspace_bytes_given, err_flag, true, pre);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (pre) {
+    const int prc = attach_prefix(a, g, head_dim, max_context_len, workspace,
+                                  workspace_bytes_given, prefix_table, prefix_blocks,
+                                  prefix_first_seq, prefix_num_seqs);
+    if (prc != PKV_OK) return prc;
+  }
   const int vrc = launch_verify(a, d, (hipStream_t)stream);
   return vrc != PKV_OK ? vrc : launch_merge(a, d, (hipStream_t)stream);
 }

@@ -144,24 +144,33 @@ def test_many_more_waves_than_tiles():
     run([1] * 64, 100, 8, 8192)
 
 
-def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 3)):
-    """The decode split with prefix units (pkv_decode_step_prefix), one
-    query group per KV head (group <= 16): the same integer formulas as the
-    kernel, checked like run(). With a prefix and two or more waves the
-    waves form two classes, the last Wp splitting the prefix units' tiles;
-    with one wave a single order holds both."""
+def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 3), q_len=1):
+    """The split with prefix units: the decode's (pkv_decode_step_prefix,
+    q_len 1) or the verification pass's (pkv_paged_attn_verify_prefix, q_len
+    query tokens, causal): the same integer formulas as the kernel, checked
+    like run(). A KV head's q_len * group rows form row groups of 16 (of 32
+    when there are more than 16); a member whose query tokens all lie after
+    the prefix reads it through prefix units of 32 rows. With a prefix and
+    two or more waves the waves form two classes, the last Wp splitting the
+    prefix units' tiles; with one wave a single order holds both."""
     B = len(ctxs)
+    qrows = q_len * group
+    group_rows = 32 if qrows > 16 else 16
+    n_qgroups = (qrows + group_rows - 1) // group_rows
+    n_hq = n_kv * n_qgroups
+
+    def tiles(c):
+        return (c + 15) // 16 if q_len <= c <= max_ctx else 0
 
     def skip(s):
         c = ctxs[s]
-        return pre_tiles if (pre_tiles > 0 and first <= s < first + count and
-                             seq_tiles(c, max_ctx) > 0 and (c - 1) // 16 >= pre_tiles) else 0
+        return pre_tiles if (pre_tiles > 0 and first <= s < first + count and tiles(c) > 0 and
+                             c - q_len >= 16 * pre_tiles) else 0
 
-    unit_t = [seq_tiles(ctxs[s], max_ctx) - skip(s) if seq_tiles(ctxs[s], max_ctx) else 0
-              for s in range(B)]
+    unit_t = [tiles(ctxs[s]) - skip(s) if tiles(ctxs[s]) else 0 for s in range(B)]
     per_row = sum(unit_t)
-    t_seq = n_kv * per_row
-    qgroups = (count * group + 31) // 32 if pre_tiles > 0 and count > 0 else 0
+    t_seq = n_hq * per_row
+    qgroups = (count * qrows + 31) // 32 if pre_tiles > 0 and count > 0 else 0
     pre_units = n_kv * qgroups
     t_pre = pre_units * pre_tiles
     if t_seq + t_pre == 0:
@@ -259,7 +268,7 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 
                 if s == B:
                     s = 0
                     hq += 1
-                    if hq >= n_kv:
+                    if hq >= n_hq:
                         done = True
                         break
                 if unit_t[s]:
@@ -269,20 +278,21 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 
                 prefix_walk(w, cur, end, origin)
                 break
     assert all(c == 1 for c in covered), "coverage"
-    assert max(seq_writes, default=0) < W + n_kv * B
+    assert max(seq_writes, default=0) < W + n_hq * B
     assert max(pre_writes, default=0) < W + pre_units
     # merge side: the bookkeeping the kernel writes (first slot, count) per
     # unit, from the unit's span; the slots hold exactly the unit's tiles
     seq_span = span(0)
     pre_span = span(W - 1)
-    for h in range(n_kv):
+    for hq in range(n_hq):
+        h, qg = divmod(hq, n_qgroups)
         for s in range(B):
             nt = unit_t[s]
             if nt == 0:
                 continue
-            u = h * B + s
+            u = hq * B + s
             total, waves, _, _ = seq_span
-            t0 = h * per_row + sum(unit_t[:s])
+            t0 = hq * per_row + sum(unit_t[:s])
             w0 = ((t0 + 1) * waves - 1) // total
             w1 = ((t0 + nt) * waves - 1) // total
             n = w1 - w0 + 1
@@ -294,8 +304,8 @@ def run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost=(2, 
             assert sum(seq_writes[sl][1] for sl in slots) == nt
             if skip(s):
                 total, waves, base, origin = pre_span if w_pre else seq_span
-                for jj in range(group):
-                    pr = (s - first) * group + jj
+                for gr in range(qg * group_rows, min(qrows, (qg + 1) * group_rows)):
+                    pr = (s - first) * qrows + gr
                     pu = h * qgroups + pr // 32
                     x0 = origin + pu * pre_tiles
                     p0 = ((x0 + 1) * waves - 1) // total
@@ -323,3 +333,25 @@ def test_split_with_prefix_units():
         run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost)
         n_cases += 1
     assert n_cases == 1500
+
+
+def test_verify_split_with_prefix_units():
+    """The verification pass's split with prefix units: q_len query tokens
+    per member, row groups of 32 when a KV head has more than 16 rows,
+    members only if their query tokens all lie after the prefix."""
+    rnd = random.Random(2)
+    for _ in range(1000):
+        B = rnd.randint(1, 30)
+        q_len = rnd.choice([1, 2, 5, 12, 33, 64])
+        pre_tiles = rnd.choice([1, 2, 5, 16, 40])
+        max_ctx = rnd.choice([16 * pre_tiles + q_len, 16 * pre_tiles + 200, 3000])
+        ctxs = [rnd.choice([0, q_len - 1, q_len, rnd.randint(1, max_ctx), max_ctx,
+                            16 * pre_tiles + q_len - 1, 16 * pre_tiles + q_len])
+                for _ in range(B)]
+        n_kv = rnd.randint(1, 8)
+        group = rnd.choice([1, 4, 5, 8, 16])
+        first = rnd.randint(0, B - 1)
+        count = rnd.randint(0, B - first)
+        W = rnd.choice([1, 2, 3, 64, 1000, rnd.randint(1, 2000)])
+        cost = rnd.choice([(2, 3), (1, 2), (1, 1)])
+        run_prefix(ctxs, max_ctx, n_kv, group, W, pre_tiles, first, count, cost, q_len)
