@@ -251,7 +251,7 @@ def upload_tables(torch, S, i):
 
 def kv_bytes(S, ctx):
     """Algorithmic KV bytes of one layer: K and V of every cached token,
-    n_kv heads x head_dim x 2 bytes each."""
+    each 2 bytes per element over n_kv * head_dim elements."""
     return 2 * S.shape.n_kv * S.shape.d * 2 * int(ctx.astype(np.int64).sum())
 
 

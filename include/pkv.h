@@ -48,15 +48,15 @@
  *   k_new  bf16  [num_seqs][n_kv_heads][head_dim]   (same for v_new)
  *   out    fp32  [num_seqs][n_q_heads][head_dim]
  *
- *   Grouped-query attention ([SLS] "The KV cache": a few KV heads, each
- *   shared by a group of query heads): G = n_q_heads / n_kv_heads, and query
+ *   Grouped-query attention ([SLS] "The KV cache": fewer KV heads than query
+ *   heads, every KV head serving several query heads): G = n_q_heads / n_kv_heads, and query
  *   head j reads KV head j / G (consecutive groups). G = 1 is multi-head
  *   attention, n_kv_heads = 1 is multi-query attention.
  *
  * What the decode computes, for each sequence s and query head j with
  * h = j / G (softmax attention of the one new query token over the whole
- * cached context, [M23] 23.2: decode reads the whole KV cache for one token
- * per sequence):
+ * cached context, [M23] 23.2: every decode step streams a sequence's entire
+ * cache to produce its single new token):
  *
  *   z_t       = scale * sum_i q[s,j,i] * K(bt[s][t/16], h, t%16, i),  0 <= t < ctx_s
  *   out[s,j,:] = sum_t softmax(z)_t * V(bt[s][t/16], h, t%16, :)
@@ -125,8 +125,8 @@ uint64_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim
 /* ------------------------------------------------------------------------
  * kv_append: scatter this step's new key and value of every sequence into
  * its pool slot ([M23] 23.4 and [DSS] "Paged attention": positions reach
- * physical blocks through the per-sequence table; blocks are allocated as
- * the sequence grows, so the caller has already made bt[s][(ctx_s-1)/16]
+ * physical blocks through the per-sequence table; a sequence gains blocks
+ * only as its context lengthens, so the caller has already made bt[s][(ctx_s-1)/16]
  * valid and private, e.g. with pkv_seq_grow).
  *
  * For each s: p = ctx_s - 1, blk = bt[s][p/16], slot = p % 16, and for every
@@ -462,8 +462,8 @@ int pkv_paged_attn_verify_prefix(float* out, const void* q, const void* k_pool,
  * Chunked prefill against the paged cache ([SLS] "Split long prefills into
  * chunks": a long prompt is taken a chunk per step beside the ongoing
  * decodes; [DSS] "Scheduling: when prefill meets decode"; [M23] 23.2:
- * prefill uses each weight for every prompt token, so it is bound by
- * arithmetic).
+ * prefill reuses every weight across all the prompt's tokens, which makes it
+ * compute-bound).
  *
  * Each sequence's chunk is its last chunk_len cached tokens (the chunk's
  * keys and values already written, pkv_kv_write); chunk token i, at position
@@ -537,8 +537,8 @@ int32_t pkv_decode_split_waves(int32_t num_seqs, int32_t n_q_heads,
                                int32_t max_context_len);
 
 /* ------------------------------------------------------------------------
- * copy_blocks: copy-on-write support ([DSS] "Paged attention": when
- * sequences that share blocks diverge, the shared block is copied on write).
+ * copy_blocks: copy-on-write support ([DSS] "Paged attention": a block
+ * held by several sequences is duplicated before one of them writes to it).
  * For each pair p: the whole K and V block src[p] (all heads, all 16 slots)
  * is copied to block dst[p] of the given layer's pools. src/dst are device
  * int32 arrays of n_pairs entries; the dst blocks must be distinct and must
@@ -576,9 +576,9 @@ int32_t pkv_num_blocks(const pkv_allocator* a);
 
 /* Make the table ready for writing position new_context_len - 1:
  *  1. allocate blocks until n_blocks >= ceil(new_context_len / 16), so a
- *     sequence holds exactly the blocks its context needs and at most one
- *     partly filled block ([M23] Exercises: the waste is at most one partly
- *     filled block per request);
+ *     sequence holds exactly the blocks its context needs, of which only
+ *     the last can be partly filled ([M23] Exercises: paging wastes less
+ *     than one block per request);
  *  2. if the block holding position new_context_len - 1 has refcount > 1,
  *     copy on write: allocate a fresh block, decref the shared one, put the
  *     fresh one in the table and report the pair in (*cow_src, *cow_dst);

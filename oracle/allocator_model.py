@@ -5,8 +5,8 @@ Plain Python, written from the pages' description of paged KV memory:
     blocks, not contiguous, allocated as the sequence grows; requests can
     share blocks.
   * "Module 23: Serving", 23.4 "Paged Attention": 16-token blocks and a
-    per-sequence table from positions to blocks; Exercises: the waste is at
-    most one partly filled block per request.
+    per-sequence table from positions to blocks; Exercises: paging wastes
+    less than one block per request (only its last block is partly filled).
   * "Designing an LLM serving system", "Paged attention": shared prefix
     blocks are copied on write when sequences diverge; "Continuous
     batching": a finished sequence releases its blocks.

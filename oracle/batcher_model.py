@@ -8,8 +8,8 @@ Plain Python over AllocatorModel, written from the pages:
     at by every request that begins with it, copy on write of a shared
     block; "Scheduling: when prefill meets decode": when memory runs out a
     sequence yields, its blocks discarded and recomputed when it resumes.
-  * "Module 23: Serving", 23.3 (a waiting request takes a finished one's
-    place at once).
+  * "Module 23: Serving", 23.3 (a finished request's slot is refilled from
+    the queue in the same step).
 
 The policy details the pages leave open are the library's documented ones
 (include/pkv.h, pkv_batcher_step): growth of resident requests before

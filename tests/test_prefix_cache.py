@@ -2,9 +2,9 @@
 oracle/prefix_cache_model.py, operation by operation, and what it must do
 for the requests that use it. No GPU needed.
 
-"Scaling LLM serving", "Reuse shared prefixes": requests that start the
-same way (a system prompt, earlier turns of a chat) have the same KV cache
-for that start; the cache keeps it so a new request picks it up instead of
+"Scaling LLM serving", "Reuse shared prefixes": requests with a common
+opening (a system prompt, the earlier turns of a chat) produce identical
+keys and values for it; the cache keeps it so a new request picks it up instead of
 recomputing it. "Caching and shortcuts": with paged attention this is
 block sharing.
 """
