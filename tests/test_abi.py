@@ -215,3 +215,30 @@ def test_accept_workspace_formula():
     assert pkv.pkv_spec_accept_workspace_bytes(-1, 100) == 0
     assert pkv.pkv_spec_accept_workspace_bytes(2, 0) == 0
     assert pkv.pkv_spec_accept_workspace_bytes(2, 2097153) == 0
+
+
+def test_empty_batches_launch_nothing():
+    """A batch of zero sequences is a valid call that does nothing: every
+    device entry point returns PKV_OK after its host checks and before any
+    launch or device query (the pointers here are never dereferenced, and
+    on a machine without a GPU any HIP call would report an error)."""
+    import paged_kv_cache_468_amd as pkv
+    d = ctypes.c_void_p(0x1000)
+    ok = pkv.PKV_OK
+    # decode, verification pass, chunked prefill: ..., num_seqs, ...
+    assert pkv.lib.pkv_paged_attn_verify(d, d, d, d, d, d, 0, 5, 16, 64, 32, 8, 128, 0.1, 256,
+                                         None, 0, None, None) == ok
+    assert pkv.lib.pkv_paged_prefill(d, d, d, d, d, d, 0, 64, 16, 64, 32, 8, 128, 0.1, 256,
+                                     None, None) == ok
+    assert pkv.lib.pkv_decode_step_prefix(d, d, d, d, d, d, d, d, 0, 16, 64, 32, 8, 128, 0.1, 256,
+                                          None, 0, 0, 0, None, 0, None, None) == ok
+    assert pkv.lib.pkv_paged_attn_verify_prefix(d, d, d, d, d, d, 0, 5, 16, 64, 32, 8, 128, 0.1,
+                                                256, None, 0, 0, 0, None, 0, None, None) == ok
+    assert pkv.lib.pkv_paged_attn_partition(d, d, d, d, d, d, 0, 16, 64, 32, 8, 128, 0.1, 256, 0,
+                                            None, 0, None, None) == ok
+    assert pkv.lib.pkv_paged_attn_merge(d, d, d, d, d, d, 0, 16, 64, 32, 8, 128, 0.1, 256, 0,
+                                        None, 0, None, None) == ok
+    assert pkv.lib.pkv_kv_append(d, d, d, d, d, d, 0, 16, 64, 8, 128, None, None) == ok
+    assert pkv.lib.pkv_spec_accept(d, d, d, d, 0, 4, 128256, d, d, None, 0, None, None) == ok
+    # and the size queries agree that nothing is needed
+    assert pkv.pkv_spec_accept_workspace_bytes(0, 128256) == 0
