@@ -1,7 +1,9 @@
 """The host half of the library (allocator, prefix cache, batcher) built
 with g++ under AddressSanitizer and UndefinedBehaviorSanitizer and driven
 by tests/host_fuzz.cpp: random valid and invalid call sequences, with
-invariants checked after every call. No GPU and no HIP code involved."""
+invariants checked after every call. The oracle's C functions likewise,
+driven by tests/oracle_fuzz.c with valid and invalid inputs. No GPU and no
+HIP code involved."""
 import os
 import shutil
 import subprocess
@@ -30,3 +32,21 @@ def test_host_code_under_sanitizers(tmp_path):
     stats = dict(zip(out[2::2], map(int, out[3::2])))
     # the run reached the interesting paths
     assert stats["preempted"] > 0 and stats["cached"] > 0 and stats["cow"] > 0, run.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_oracle_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "oracle_fuzz")
+    cmd = ["gcc", "-std=c11", "-g", "-O1", "-fno-omit-frame-pointer", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-static-libasan",
+           os.path.join(ROOT, "tests", "oracle_fuzz.c"), os.path.join(ROOT, "oracle", "oracle.c"),
+           "-lm", "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe, "400"], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0, (run.stdout + run.stderr)[-4000:]
+    calls, errors = (int(x) for x in run.stdout.split()[1::2])
+    # both the valid and the invalid paths were taken
+    assert calls == 2400 and 0 < errors < calls, run.stdout
