@@ -89,7 +89,7 @@ def members_first(cl, prefix_tokens):
 
 
 def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, fused=True,
-                prefix_kernel=False):
+                prefix_kernel=False, valu=False):
     """Block tables from the refcounted allocator, pools filled on the
     device, every layer's buffers, and pre-marshalled library calls."""
     cl = members_first(w.context_lengths(shape, seed).astype(np.int32), shape.prefix_tokens)
@@ -183,6 +183,8 @@ def build_state(pkv, torch, shape, seed, share, extra_tokens, partition_tokens, 
                                                                        n_prefix, S.prefix_members))
     S.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     S.fused = fused
+    # the partition kernel on the vector ALUs (comparison with the matrix path)
+    S.valu = valu and fused and partition_tokens == 0 and not S.prefix_blocks
     S.calls = layer_calls(pkv, S)
     torch.cuda.synchronize()
     assert int(S.err.item()) == 0
@@ -204,6 +206,14 @@ def layer_calls(pkv, S):
                     S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt,
                     S.cl, sh.scale, S.max_ctx, S.prefix_table, 0, S.prefix_members, workspace=S.ws,
                     err_flag=S.err))])
+        elif S.valu:
+            calls.append([
+                ("decode_step_partition_valu", pkv.prepare_decode_step_partition_valu(
+                    S.out[l], S.q[l], S.k_new[l], S.v_new[l], S.k_pool[l], S.v_pool[l], S.bt,
+                    S.cl, sh.scale, S.max_ctx, workspace=S.ws, err_flag=S.err)),
+                ("paged_attn_merge", pkv.prepare_paged_attn_merge(
+                    S.out[l], S.q[l], S.k_pool[l], S.v_pool[l], S.bt, S.cl, sh.scale, S.max_ctx,
+                    S.partition, workspace=S.ws, err_flag=S.err))])
         elif S.fused:
             # pkv_decode_step as its two launches, so that events can time each
             calls.append([
@@ -404,7 +414,8 @@ def run(pkv, torch, S, steps, warmup, graph=True):
         dom = "decode_step_prefix"
         alg = lambda c: prefix_call_alg_bytes(S, c)
     else:
-        dom = "decode_step_partition" if S.fused else "paged_attn_partition"
+        dom = ("decode_step_partition_valu" if S.valu else
+               "decode_step_partition" if S.fused else "paged_attn_partition")
         alg = lambda c: attn_alg_bytes(S, c) + (append_alg_bytes(S, S.B) if S.fused else 0)
     dom_bytes = sum(alg(c) for c in eager_ctx) / steps
     # Its launch duration without the per-launch event overhead: its
@@ -1024,6 +1035,10 @@ def main():
     ap.add_argument("--no-prefix-kernel", action="store_true",
                     help="shared prefix: pkv_decode_step (every sequence reads the prefix through "
                          "its own table) instead of pkv_decode_step_prefix")
+    ap.add_argument("--valu", action="store_true",
+                    help="decode without a shared prefix with the partition kernel's scores and "
+                         "P.V on the vector ALUs (pkv_decode_step_partition_valu) instead of "
+                         "the matrix cores, for comparison")
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per layer (kv_append, partition, merge) instead of pkv_decode_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -1138,7 +1153,8 @@ def main():
     share_main = (not args.no_share) and shape.prefix_tokens > 0
     log(f"[bench] building {wname} share={share_main}")
     S = build_state(pkv, torch, shape, args.seed, share_main, extra, args.partition_tokens,
-                    fused=not args.unfused, prefix_kernel=not args.no_prefix_kernel)
+                    fused=not args.unfused, prefix_kernel=not args.no_prefix_kernel,
+                    valu=args.valu)
     log(f"[bench] {S.num_blocks} blocks/layer, partition {S.partition} (0: balanced over {S.split_waves} waves), cow {S.n_cow}; timing")
     main_r = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
     log(f"[bench] main: {main_r['ms_per_step']:.3f} ms/step ({main_r['step_mode']}), "
@@ -1161,7 +1177,7 @@ def main():
     if shape.prefix_tokens > 0 and share_main and not args.skip_no_share:
         log("[bench] no-share run")
         S2 = build_state(pkv, torch, shape, args.seed, False, extra, args.partition_tokens,
-                         fused=not args.unfused)
+                         fused=not args.unfused, valu=args.valu)
         r2 = run(pkv, torch, S2, args.steps, args.warmup, graph=not args.no_graph)
         log(f"[bench] no-share: {r2['ms_per_step']:.3f} ms/step ({r2['step_mode']}), "
             f"{r2['kv_gbs']:.0f} GB/s; {r2['dominant']} {r2['dominant_us']:.1f} us = "

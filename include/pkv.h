@@ -325,6 +325,31 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
                               void* workspace, size_t workspace_bytes,
                               int32_t* err_flag, void* stream);
 
+/* pkv_decode_step_partition with the balanced split (partition_tokens must
+ * be 0) and the attention's two products on the vector ALUs instead of the
+ * matrix cores: packed bf16 dot products with fp32 accumulation for both
+ * the scores and the weighted sum of the values (the weights split into
+ * bf16 hi + lo, as the matrix path splits them); the same split, loads,
+ * append and partials, so pkv_paged_attn_merge with the same arguments
+ * finishes the step. The unit's query rows are staged in 8 KiB of LDS per
+ * workgroup (head_dim 128). Kept to measure what the matrix cores buy on
+ * this memory-bound path (the pages call the decode a streaming read of the
+ * cache: [M23] 23.2; [SLS] "Why decoding is limited by memory"). Results
+ * within 1e-3 of the oracle, not bit-identical to the matrix path (another
+ * summation order). n_q_heads / n_kv_heads at most 8, else
+ * PKV_EUNSUPPORTED; partition_tokens other than 0: PKV_EINVAL; other errors
+ * as for pkv_decode_step_partition. */
+int pkv_decode_step_partition_valu(float* out, const void* q, const void* k_new,
+                                   const void* v_new, void* k_pool, void* v_pool,
+                                   const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, float scale,
+                                   int32_t max_context_len, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t* err_flag, void* stream);
+
 /* A decode step whose batch shares a prompt prefix held once in the pools
  * ([SLS] "Reuse shared prefixes": requests that begin with the same prompt
  * share its cached blocks; [DSS] "Paged attention": shared blocks are

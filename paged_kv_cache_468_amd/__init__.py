@@ -57,6 +57,9 @@ SIGNATURES = {
     "pkv_decode_step_partition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                                  _vp, _sz, _vp, _vp]),
+    "pkv_decode_step_partition_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_decode_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_step_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32,
@@ -335,6 +338,19 @@ def pkv_decode_step_noalloc(out, q, k_new, v_new, k_pool, v_pool, block_tables, 
                          max_context_len, 0, _NO_WORKSPACE, err_flag, stream)
     # C order: the step's arguments without partition_tokens, workspace and its size
     _check(lib.pkv_decode_step_noalloc(*(args[:16] + args[19:])), "pkv_decode_step_noalloc")
+
+
+def pkv_decode_step_partition_valu(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                   context_lens, scale, max_context_len, workspace=None,
+                                   err_flag=None, stream=None):
+    """pkv_decode_step_partition (balanced split) with the scores and P.V
+    on the vector ALUs instead of the matrix cores; at most 8 query heads
+    per KV head. pkv_paged_attn_merge with the same arguments and workspace
+    finishes the step. Returns the workspace used."""
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, 0, workspace, err_flag, stream)
+    _check(lib.pkv_decode_step_partition_valu(*args), "pkv_decode_step_partition_valu")
+    return ws
 
 
 def pkv_decode_prefix_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim, max_context_len,
@@ -725,6 +741,18 @@ def prepare_decode_step_partition(out, q, k_new, v_new, k_pool, v_pool, block_ta
     args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
                           max_context_len, partition_tokens, workspace, err_flag, stream)
     return PreparedCall("pkv_decode_step_partition", args,
+                        (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
+                         err_flag))
+
+
+def prepare_decode_step_partition_valu(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                       context_lens, scale, max_context_len, workspace=None,
+                                       err_flag=None, stream=None):
+    """prepare_decode_step_partition with the scores and P.V on the vector
+    ALUs (balanced split only); prepare_paged_attn_merge finishes it."""
+    args, ws = _step_args(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                          max_context_len, 0, workspace, err_flag, stream)
+    return PreparedCall("pkv_decode_step_partition_valu", args,
                         (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, ws,
                          err_flag))
 

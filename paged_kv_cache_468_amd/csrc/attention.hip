@@ -710,6 +710,313 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
   return !bad;
 }
 
+// ---------------------------------------------------------------------------
+// The decode's scores and P.V on the vector ALUs instead of the matrix
+// cores, for comparison (pkv_decode_step_partition_valu): the same split,
+// ring of register sets, append and partials as process_segment, its own
+// lane layout for the tiles.
+//   K: each quad of lanes holds one token, lane (c, r) token 4r + c/4, dims
+//      32m + 8(c%4) .. +7 (the same 16-byte loads per lane as the matrix
+//      path). The token's score is four packed bf16 dot-product chains, one
+//      per lane, summed across the quad by two DPP moves.
+//   q: the unit's rows staged in LDS once per segment and read per tile
+//      (every lane of a quad position reads the same 16 bytes).
+//   V: as in the matrix path, lane (c, r) dim 16m + c of tokens 4r .. 4r+3;
+//      the weights of those four tokens are the first lanes of the row's
+//      four quads, broadcast within the row by DPP (row_newbcast).
+//   Softmax: base 2, reference maximum with the same slack as the matrix
+//      path; a ballot finds whether any token exceeds it before any
+//      reduction is taken.
+// At most kVecMaxG query rows per KV head.
+constexpr int kVecMaxG = 8;
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowBcast = 0x150;   // + n: lane n of each row of 16 to the whole row
+
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+// LDS-qualified views, so volatile accesses stay LDS instructions
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// acc + the dot product of 8 bf16 values of k and q, in fp32, as four
+// packed pair products. The pairs are taken with shufflevector: taking them
+// as the dwords of a bit-cast vector has compiled to the first dword read
+// four times.
+__device__ inline float dot8_bf16(const bf16x8_t& k, const bf16x8_t& q, float acc) {
+  const bf16x8v_t a = __builtin_bit_cast(bf16x8v_t, k);
+  const bf16x8v_t b = __builtin_bit_cast(bf16x8v_t, q);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
+                                        __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
+                                        __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
+                                        __builtin_shufflevector(b, b, 4, 5), acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
+                                         __builtin_shufflevector(b, b, 6, 7), acc, false);
+}
+
+// One vector-ALU segment, tiles [ta, tb) of unit (h, qg = 0, s). Leaves per
+// row g: m_run[g] (identical in every lane), l_run[g] (this lane's token's
+// weights: every token is counted by the four lanes of its quad) and
+// acc[g][m] (dim 16m + c over this lane's tokens 4r .. 4r+3).
+template <int D, bool STREAM, int NBUF>
+__device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s, int h, int ctx,
+                                            int ta, int tb, bool store_new,
+                                            const SegPre<D, 1>& pre,
+                                            float (&acc)[kVecMaxG][D / 16],
+                                            float (&m_run)[kVecMaxG], float (&l_run)[kVecMaxG]) {
+  constexpr int KM = D / 32;
+  constexpr int VM = D / 16;
+  const int c = lane & 15;
+  const int r = lane >> 4;
+  const int tok = 4 * r + (c >> 2);   // this lane's token within a tile
+  const int quarter = 8 * (c & 3);    // its first dim within each 32
+  const int G = a.group;
+
+#pragma unroll
+  for (int g = 0; g < kVecMaxG; ++g) {
+#pragma unroll
+    for (int m = 0; m < VM; ++m) acc[g][m] = 0.f;
+    m_run[g] = -__builtin_inff();
+    l_run[g] = 0.f;
+  }
+  // The unit's query rows into this wave's LDS slice: lane (c, r) holds row
+  // c's dims 32m + 8r .. +7 (rows past the group are zeros). Reads and
+  // writes of the slice are volatile, so they stay in program order (one
+  // wave's LDS operations complete in order) and the per-tile reads are not
+  // hoisted into registers.
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kVecMaxG * D];
+  volatile lds_u16_t* qs = (volatile lds_u16_t*)q_lds[threadIdx.x >> 6];
+  if (c < kVecMaxG) {
+#pragma unroll
+    for (int m = 0; m < KM; ++m)
+      *(volatile lds_bf16x8_t*)(qs + c * D + 32 * m + 8 * r) = pre.qv[0][m];
+  }
+
+  const int64_t tile_elems = 16 * D;
+  const int64_t head_off = (int64_t)h * tile_elems;
+  const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
+  const int k_lane_off = tok * D + quarter;
+  const int v_lane_off = c * 16 + 4 * r;
+  const int last_tile = (ctx - 1) >> 4;
+  const int last_valid = ctx - last_tile * 16;
+  const int new_slot = last_valid - 1;
+  const bool has_new = a.k_new != nullptr && tb > last_tile;
+
+  bf16x8_t kn[KM];   // new token: key dims 32m + quarter .. +7
+  short vn[VM];      // new token: value dim 16m + c
+  if (has_new) {
+    const int64_t row = ((int64_t)s * a.n_kv + h) * D;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) kn[m] = *(const bf16x8_t*)(a.k_new + row + 32 * m + quarter);
+#pragma unroll
+    for (int m = 0; m < VM; ++m) vn[m] = (short)a.v_new[row + 16 * m + c];
+  }
+
+  const int n = tb - ta;
+  const int32_t* ids = a.block_tables + (int64_t)s * a.max_blocks + ta;
+  auto ids_from = [&](int j) { return ids[min(j + lane, n - 1)]; };
+  bool bad = false;
+  bf16x8_t kb[NBUF][KM];
+  bf16x4_t vb[NBUF][VM];
+  int blk_of[NBUF];
+
+  auto issue = [&](int blk, int b) {
+    if ((unsigned)blk >= (unsigned)a.num_blocks) {
+      bad = true;
+      blk = 0;
+    }
+    blk_of[b] = blk;
+    const int64_t base = (int64_t)blk * block_stride + head_off;
+    const uint16_t* kt = a.k_pool + base;
+    const uint16_t* vt = a.v_pool + base;
+    if (STREAM) {
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        kb[b][m] = __builtin_nontemporal_load((const bf16x8_t*)(kt + k_lane_off + 32 * m));
+#pragma unroll
+      for (int m = 0; m < VM; ++m)
+        vb[b][m] = __builtin_nontemporal_load((const bf16x4_t*)(vt + v_lane_off + 256 * m));
+    } else {
+#pragma unroll
+      for (int m = 0; m < KM; ++m) kb[b][m] = *(const bf16x8_t*)(kt + k_lane_off + 32 * m);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) vb[b][m] = *(const bf16x4_t*)(vt + v_lane_off + 256 * m);
+    }
+  };
+
+  auto compute_tile = [&](int j, int b, auto maybe_last) {
+    bf16x8_t* kr = kb[b];
+    bf16x4_t* vr = vb[b];
+    const int tile = ta + j;
+    if (maybe_last && has_new && tile == last_tile) {
+      if (tok == new_slot) {
+#pragma unroll
+        for (int m = 0; m < KM; ++m) kr[m] = kn[m];
+      }
+      if (r == (new_slot >> 2)) {
+#pragma unroll
+        for (int m = 0; m < VM; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e == (new_slot & 3)) vr[m][e] = vn[m];
+      }
+      if (store_new && !bad) {
+        const int64_t base = (int64_t)blk_of[b] * block_stride + head_off;
+        uint16_t* kt = (uint16_t*)a.k_pool + base;
+        uint16_t* vt = (uint16_t*)a.v_pool + base;
+        if (tok == new_slot) {
+#pragma unroll
+          for (int m = 0; m < KM; ++m) *(bf16x8_t*)(kt + new_slot * D + 32 * m + quarter) = kn[m];
+        }
+        if (r == 0) {
+#pragma unroll
+          for (int m = 0; m < VM; ++m) vt[(16 * m + c) * 16 + new_slot] = (uint16_t)vn[m];
+        }
+      }
+    }
+    const bool partly = maybe_last && tile == last_tile && last_valid < 16;
+    if (partly) {   // values past the context may hold anything (NaN included): zeroed
+      const int valid = last_valid - 4 * r;
+      const uint32_t keep0 = (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        u32x2_t wv = __builtin_bit_cast(u32x2_t, vr[m]);
+        wv[0] &= keep0;
+        wv[1] &= keep1;
+        vr[m] = __builtin_bit_cast(bf16x4_t, wv);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kVecMaxG; ++g) {
+      if (g >= G) break;
+      float sc = 0.f;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const bf16x8_t qv = *(const volatile lds_bf16x8_t*)(qs + g * D + 32 * m + quarter);
+        sc = dot8_bf16(kr[m], qv, sc);
+      }
+      sc += dpp_f32<kDppQuadXor1>(sc);
+      sc += dpp_f32<kDppQuadXor2>(sc);   // the token's whole score, in all four lanes
+      float x = sc * a.scale_log2;
+      if (partly && tok >= last_valid) x = -__builtin_inff();
+      if (__ballot(x > m_run[g] + kRescaleSlack) != 0) {
+        float mx = x;
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+      }
+      const float p = __builtin_amdgcn_exp2f(x - m_run[g]);
+      l_run[g] += p;
+      // weights of tokens 4r .. 4r+3, each as bf16 hi (truncated: exact
+      // remainder) + lo (rounded), paired for the packed dot products
+      const float pt[4] = {dpp_f32<kDppRowBcast + 0>(p), dpp_f32<kDppRowBcast + 4>(p),
+                           dpp_f32<kDppRowBcast + 8>(p), dpp_f32<kDppRowBcast + 12>(p)};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = __float_as_uint(pt[e]) & 0xFFFF0000u;
+        lo[e] = bf16_rne_bits(pt[e] - __uint_as_float(hi[e]));
+      }
+      const bf16x8_t pw = __builtin_bit_cast(
+          bf16x8_t, u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3], lo[0] | (lo[1] << 16),
+                            lo[2] | (lo[3] << 16)});
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
+        acc[g][m] = dot8_bf16(vv, pw, acc[g][m]);
+      }
+    }
+  };
+
+  // the ring and loop of process_segment
+  const int id0 = pre.id0;
+  int idw = pre.idw;
+  int j0 = 0;
+  if (n >= 2 * NBUF - 1) {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) issue(__builtin_amdgcn_readlane(id0, b), b);
+    do {
+      const int idnext = ids_from(j0 + 2 * NBUF - 1);
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        issue(__builtin_amdgcn_readlane(idw, b), (b + NBUF - 1) % NBUF);
+        compute_tile(j0 + b, b, Flag<false>{});
+      }
+      idw = idnext;
+      j0 += NBUF;
+    } while (j0 + 2 * NBUF - 2 < n);
+  } else {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b)
+      if (b < n) issue(__builtin_amdgcn_readlane(id0, b), b);
+  }
+#pragma unroll
+  for (int b = 0; b < 2 * NBUF - 2; ++b) {
+    if (j0 + b + NBUF - 1 < n) issue(__builtin_amdgcn_readlane(idw, b), (b + NBUF - 1) % NBUF);
+    if (j0 + b < n) compute_tile(j0 + b, b % NBUF, Flag<true>{});
+  }
+  return !bad;
+}
+
+// A finished vector-ALU segment: per row, l summed over the wave (each
+// token counted four times, so a quarter of it: exact in binary) and the
+// accumulators over the four lanes r of a dim; then, as finish_rows does,
+// out directly or a partial. Lane (c, r) writes dims 16m + c for
+// m = r, r + 4, ... of every row.
+template <int D>
+__device__ inline void finish_rows_valu(const DecodeArgs& a, int lane, bool ok, bool whole,
+                                        int64_t slot, int s, int h,
+                                        float (&acc)[kVecMaxG][D / 16],
+                                        const float (&m_run)[kVecMaxG],
+                                        const float (&l_run)[kVecMaxG]) {
+  constexpr int VM = D / 16;
+  const int c = lane & 15;
+  const int r = lane >> 4;
+  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int g = 0; g < kVecMaxG; ++g) {
+    if (g >= a.group) break;
+    float l = l_run[g];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off);
+    l *= 0.25f;
+#pragma unroll
+    for (int m = 0; m < VM; ++m) {
+      acc[g][m] += __shfl_xor(acc[g][m], 16);
+      acc[g][m] += __shfl_xor(acc[g][m], 32);
+    }
+    const int64_t out_row = (int64_t)s * a.n_q + h * a.group + g;
+    if (whole) {
+      const float inv = ok ? 1.0f / l : nan;
+#pragma unroll
+      for (int m = 0; m < VM; ++m)
+        if ((m & 3) == r) a.out[out_row * D + 16 * m + c] = acc[g][m] * inv;
+    } else {
+      const int64_t row = slot * a.rows + g;
+      if (lane == 0) {
+        a.ws_ml[2 * row] = ok ? m_run[g] : nan;
+        a.ws_ml[2 * row + 1] = ok ? l : nan;
+      }
+#pragma unroll
+      for (int m = 0; m < VM; ++m)
+        if ((m & 3) == r) a.ws_acc[row * D + 16 * m + c] = acc[g][m];
+    }
+  }
+}
+
 // Write a finished segment's row: out directly when the segment covers its
 // whole unit, else a partial into its workspace slot (row g_in_slot of the
 // slot). Rows past the group write nothing.
@@ -876,8 +1183,9 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
 // together. (With a single wave, one order holds both.) The wave holding
 // a unit's first tile records, for the merge kernel, the unit's first
 // partial slot and its number of partials (1: written here).
-template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX>
+template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX, bool VALU = false>
 __device__ inline void balanced_body(const DecodeArgs& a) {
+  static_assert(!VALU || (!PREFIX && !CAUSAL && NG == 1), "vector-ALU path: the plain decode only");
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
@@ -1036,19 +1344,31 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
           skip2 + tb2, pre2);
     }
 
-    f32x4_t acc[NG][VM];
-    float m_run[NG], l_run[NG];
-    // a member reading the shared prefix through the prefix units reads
-    // its own tiles once: streamed
-    const bool ok =
-        skip == 0 && scan_shares_first<KEEP>(a, ts, s)
-            ? process_segment<D, false, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
-                                                          skip + tb, qg == 0, pre, acc, m_run,
-                                                          l_run)
-            : process_segment<D, true, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
-                                                         skip + tb, qg == 0, pre, acc, m_run,
-                                                         l_run);
-    finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
+    if constexpr (VALU) {
+      float vacc[kVecMaxG][VM];
+      float vm[kVecMaxG], vl[kVecMaxG];
+      const bool ok =
+          scan_shares_first<KEEP>(a, ts, s)
+              ? process_segment_valu<D, false, NBUF>(a, lane, s, h, ctx, pos, tb, qg == 0, pre,
+                                                     vacc, vm, vl)
+              : process_segment_valu<D, true, NBUF>(a, lane, s, h, ctx, pos, tb, qg == 0, pre,
+                                                    vacc, vm, vl);
+      finish_rows_valu<D>(a, lane, ok, whole, (int64_t)w + u, s, h, vacc, vm, vl);
+    } else {
+      f32x4_t acc[NG][VM];
+      float m_run[NG], l_run[NG];
+      // a member reading the shared prefix through the prefix units reads
+      // its own tiles once: streamed
+      const bool ok =
+          skip == 0 && scan_shares_first<KEEP>(a, ts, s)
+              ? process_segment<D, false, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
+                                                            skip + tb, qg == 0, pre, acc, m_run,
+                                                            l_run)
+              : process_segment<D, true, NG, CAUSAL, NBUF>(a, lane, s, h, rw, ctx, skip + pos,
+                                                           skip + tb, qg == 0, pre, acc, m_run,
+                                                           l_run);
+      finish_rows<D, NG>(a, lane, ok, whole, (int64_t)w + u, rw, acc, m_run, l_run);
+    }
     cur = cur_next;
     if (!more) break;
     if (CAUSAL) find_next();
@@ -1078,6 +1398,14 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
 template <int D, bool PREFIX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void paged_attn_balanced_kernel(DecodeArgs a) {
   balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing, PREFIX>(a);
+}
+
+// The decode's partition kernel with its scores and P.V on the vector ALUs
+// (process_segment_valu), for comparison with the matrix-core kernel above:
+// the same split, waves, ring and partials.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void paged_attn_balanced_valu_kernel(DecodeArgs a) {
+  balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing, false, true>(a);
 }
 
 // The verification pass: q_len query tokens per sequence, causal among
@@ -1950,6 +2278,27 @@ extern "C" int pkv_decode_step_partition(PKV_STEP_PARAMS) {
   DecodeArgs a;
   int d = 0;
   return step_partition(a, d, PKV_STEP_ARGS);
+}
+
+extern "C" int pkv_decode_step_partition_valu(PKV_STEP_PARAMS) {
+  if (partition_tokens != 0) return PKV_EINVAL;
+  if (n_kv_heads > 0 && n_q_heads % n_kv_heads == 0 && n_q_heads / n_kv_heads > kVecMaxG)
+    return PKV_EUNSUPPORTED;
+  DecodeArgs a;
+  int d = 0;
+  const int rc = prepare(a, d, PKV_DECODE_PREP_ARGS);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (!k_new || !v_new) return PKV_EINVAL;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
+  if (d == 128)
+    hipLaunchKernelGGL(paged_attn_balanced_valu_kernel<128>, dim3(grid), dim3(256), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(paged_attn_balanced_valu_kernel<64>, dim3(grid), dim3(256), 0,
+                       (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 extern "C" int pkv_decode_step(PKV_STEP_PARAMS) {
