@@ -494,6 +494,7 @@ def cpu_baseline(torch, S, budget_s, threads_budget_s):
     u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     done, tokens, kvb, t_used, worst, layers = 0, 0, 0, 0.0, 0.0, 0
     order = w.rng(12345, 7).permutation(S.B)
+    pairs = []   # (layer, sequence, float64 rows) in the order computed
     for l in range(sh.n_layers):
         k_l, v_l, q_l = u16(S.k_pool[l]), u16(S.v_pool[l]), u16(S.q[l])
         got = S.out[l].cpu().numpy().astype(np.float64)
@@ -504,6 +505,7 @@ def cpu_baseline(torch, S, budget_s, threads_budget_s):
                                   sh.scale)
             t_used += time.perf_counter() - t0
             assert rc == 0
+            pairs.append((l, int(s), want[0]))
             worst = max(worst, float(np.abs(want[0] - got[s]).max()))
             kvb += 2 * sh.n_kv * sh.d * 2 * int(S.ctx[s])
             tokens += int(S.ctx[s])
@@ -523,6 +525,37 @@ def cpu_baseline(torch, S, budget_s, threads_budget_s):
         "seconds": t_used,
         "steps_per_s_equiv": gbs * 1e9 / (kv_bytes(S, S.ctx) * sh.n_layers),
     }
+    # The oracle's single-precision twin (the naive fp32 loop) over the first
+    # pairs of the same order, for a third of the budget: its rate on one
+    # core, its difference from the float64 oracle (its own rounding error)
+    # and from the GPU.
+    t_f, kvb_f, done_f, err_twin, err_gpu, cur_l = 0.0, 0, 0, 0.0, 0.0, -1
+    for l, s, want in pairs:
+        if l != cur_l:
+            k_l, v_l, q_l = u16(S.k_pool[l]), u16(S.v_pool[l]), u16(S.q[l])
+            got = S.out[l].cpu().numpy().astype(np.float64)
+            cur_l = l
+        t0 = time.perf_counter()
+        want32, rc = orc.decode_f32(q_l[s:s + 1], k_l, v_l, S.tables[s:s + 1], S.ctx[s:s + 1],
+                                    sh.n_kv, sh.scale)
+        t_f += time.perf_counter() - t0
+        assert rc == 0
+        w32 = want32[0].astype(np.float64)
+        err_twin = max(err_twin, float(np.abs(w32 - want).max()))
+        err_gpu = max(err_gpu, float(np.abs(w32 - got[s]).max()))
+        kvb_f += 2 * sh.n_kv * sh.d * 2 * int(S.ctx[s])
+        done_f += 1
+        if t_f >= budget_s / 3:
+            break
+    if cur_l >= 0:
+        del k_l, v_l
+    single["fp32_twin"] = {
+        "value": kvb_f / t_f / 1e9 if t_f > 0 else None, "unit": "GB/s", "cores": 1,
+        "sample": f"the first {done_f} of the same pairs; single-threaded C loop in float32, "
+                  f"{t_f:.1f} s",
+        "max_abs_vs_float64_oracle": err_twin, "max_abs_vs_gpu": err_gpu,
+    }
+    del pairs
     if threads_budget_s <= 0:
         return single, worst, done, None
     # The same function on P host threads, each over its own shard of the

@@ -8,7 +8,8 @@ runs anything here, and nothing here imports the product path.
 Contents
   * ``liboracle.so`` (built from ``oracle.c`` by ``oracle/build.py``): append,
     multi-token write, copy-on-write, decode and the multi-token verification
-    attention in double precision, the KV-size closed form.
+    attention in double precision, the decode's single-precision twin (the
+    naive fp32 loop), the KV-size closed form.
   * ``speculative``: the acceptance rule of speculative decoding (accept,
     leftover distribution, replacement draw) in plain Python.
   * ``allocator_model``: a pure-Python reference model of the refcounted
@@ -57,6 +58,13 @@ def _bind(path):
     lib.oracle_decode.argtypes = [f64p, u16p, u16p, u16p, i32p, i32p, c_int,
                                   c_int, c_int, c_int, c_int, c_int,
                                   ctypes.c_double]
+    f32p = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_decode_row_f32.restype = c_int
+    lib.oracle_decode_row_f32.argtypes = [f32p, u16p, u16p, u16p, i32p, c_int,
+                                          c_int, c_int, c_int, c_int, ctypes.c_float]
+    lib.oracle_decode_f32.restype = c_int
+    lib.oracle_decode_f32.argtypes = [f32p, u16p, u16p, u16p, i32p, i32p, c_int,
+                                      c_int, c_int, c_int, c_int, c_int, ctypes.c_float]
     lib.oracle_verify.restype = c_int
     lib.oracle_verify.argtypes = [f64p, u16p, u16p, u16p, i32p, i32p, c_int, c_int,
                                   c_int, c_int, c_int, c_int, c_int, ctypes.c_double]
@@ -170,6 +178,28 @@ class Oracle:
             raise ValueError("oracle_decode: n_q must be a multiple of n_kv")
         return out, rc
 
+    def decode_f32(self, q, k_pool, v_pool, block_tables, context_lens, n_kv, scale):
+        """decode() as the naive loop in single precision (its float64
+        twin is decode()). Returns (out float32 [num_seqs, n_q, d], status)."""
+        q = _u16(q, "q")
+        k_pool = _u16(k_pool, "k_pool")
+        v_pool = _u16(v_pool, "v_pool")
+        bt = _i32(block_tables, "block_tables")
+        cl = _i32(context_lens, "context_lens")
+        num_seqs, n_q, d = q.shape
+        num_blocks = k_pool.size // (n_kv * 16 * d)
+        out = np.empty((num_seqs, n_q, d), dtype=np.float32)
+        rc = self.lib.oracle_decode_f32(
+            _ptr(out, ctypes.c_float), _ptr(q, ctypes.c_uint16),
+            _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+            _ptr(bt, ctypes.c_int32), _ptr(cl, ctypes.c_int32),
+            num_seqs, bt.shape[1], num_blocks, n_q, n_kv, d, float(scale))
+        if rc == -2:
+            raise MemoryError("oracle_decode_f32: out of host memory")
+        if rc == -3:
+            raise ValueError("oracle_decode_f32: n_q must be a multiple of n_kv")
+        return out, rc
+
     def verify(self, q, k_pool, v_pool, block_tables, context_lens, n_kv, scale):
         """Verification attention of q_len query tokens per sequence, query
         token i at position ctx - q_len + i seeing tokens [0, ctx - q_len + i].
@@ -217,6 +247,24 @@ class Oracle:
                                                        scale), parts))
         out = np.concatenate([r[0] for r in res]) if res else np.empty(q.shape, np.float64)
         return out, min((r[1] for r in res), default=0)
+
+    def decode_row_f32(self, q_row, k_pool, v_pool, table_row, ctx, n_kv, h, scale):
+        """decode_row() in single precision (float32 row, status)."""
+        q_row = _u16(q_row, "q_row")
+        k_pool = _u16(k_pool, "k_pool")
+        v_pool = _u16(v_pool, "v_pool")
+        table_row = _i32(table_row, "table_row")
+        d = q_row.shape[-1]
+        num_blocks = k_pool.size // (n_kv * 16 * d)
+        out = np.empty(d, dtype=np.float32)
+        rc = self.lib.oracle_decode_row_f32(
+            _ptr(out, ctypes.c_float), _ptr(q_row, ctypes.c_uint16),
+            _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+            _ptr(table_row, ctypes.c_int32), int(ctx), num_blocks, n_kv, int(h),
+            d, float(scale))
+        if rc == -2:
+            raise MemoryError("oracle_decode_row_f32: out of host memory")
+        return out, rc
 
     def decode_row(self, q_row, k_pool, v_pool, table_row, ctx, n_kv, h, scale):
         """One output row (one sequence, one query head, KV head h)."""
@@ -271,6 +319,10 @@ def decode(*a, **k):
     return default().decode(*a, **k)
 
 
+def decode_f32(*a, **k):
+    return default().decode_f32(*a, **k)
+
+
 def decode_sharded(*a, **k):
     return default().decode_sharded(*a, **k)
 
@@ -291,3 +343,7 @@ def verify(*a, **k):
 
 def decode_row(*a, **k):
     return default().decode_row(*a, **k)
+
+
+def decode_row_f32(*a, **k):
+    return default().decode_row_f32(*a, **k)

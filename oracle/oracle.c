@@ -7,7 +7,9 @@
  *
  * Single-threaded. Floating point in double precision (the pages fix no
  * precision for the attention itself, so the oracle computes the definition
- * as exactly as a double allows). Built with -O2 -ffp-contract=off and no
+ * as exactly as a double allows); the decode also has a single-precision
+ * twin (oracle_decode_f32), the naive fp32 loop, whose error the double
+ * version measures. Built with -O2 -ffp-contract=off and no
  * fast-math, so every operation is the one written here.
  *
  * Sources (page title, then section):
@@ -235,6 +237,105 @@ int oracle_decode(double* out, const uint16_t* q, const uint16_t* k_pool,
       int rc = oracle_decode_row(row, q + ((size_t)s * n_q + j) * d, k_pool,
                                  v_pool, block_tables + (size_t)s * max_blocks_per_seq,
                                  ctx, num_blocks, n_kv, j / group, d, scale);
+      if (rc == -2) return -2;
+      if (rc != 0) status = -1;
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------
+ * The same decode in single precision: the naive two-pass softmax of one
+ * query row with every operation in float, in the order written ([M23]
+ * 23.2 and [SLS] "The KV cache": one query row attends to every cached
+ * token of its sequence through the table). A product of two bf16 values
+ * is exact in float; the dot products, the exponentials (expf), the sums
+ * and the division round to float. oracle_decode_row above computes the
+ * same definition in double and is this function's twin: the difference
+ * between the two is this function's own rounding error. Returns as
+ * oracle_decode_row. */
+static float bf16_float(uint16_t bits) {
+  uint32_t word = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &word, sizeof f);
+  return f;
+}
+
+int oracle_decode_row_f32(float* out_row, const uint16_t* q_row,
+                          const uint16_t* k_pool, const uint16_t* v_pool,
+                          const int32_t* table_row, int ctx, int num_blocks,
+                          int n_kv, int h, int d, float scale) {
+  if (ctx < 1) {
+    for (int i = 0; i < d; ++i) out_row[i] = NAN;
+    return -1;
+  }
+  for (int b = 0; b < (ctx + ORACLE_BLOCK - 1) / ORACLE_BLOCK; ++b) {
+    if (table_row[b] < 0 || table_row[b] >= num_blocks) {
+      for (int i = 0; i < d; ++i) out_row[i] = NAN;
+      return -1;
+    }
+  }
+  float* w = (float*)malloc(sizeof(float) * (size_t)ctx);
+  if (!w) return -2;
+
+  /* scores: w[p] = scale * (q . k_p) */
+  for (int p = 0; p < ctx; ++p) {
+    int32_t block = table_row[p / ORACLE_BLOCK];
+    int in_block = p % ORACLE_BLOCK;
+    float qk = 0.0f;
+    for (int i = 0; i < d; ++i)
+      qk += bf16_float(q_row[i]) * bf16_float(k_pool[k_index(block, h, in_block, i, n_kv, d)]);
+    w[p] = scale * qk;
+  }
+
+  float top = w[0];
+  for (int p = 1; p < ctx; ++p)
+    if (w[p] > top) top = w[p];
+
+  float total = 0.0f;
+  for (int p = 0; p < ctx; ++p) {
+    w[p] = expf(w[p] - top); /* w now holds the unnormalised weights */
+    total += w[p];
+  }
+
+  for (int i = 0; i < d; ++i) {
+    float acc = 0.0f;
+    for (int p = 0; p < ctx; ++p) {
+      int32_t block = table_row[p / ORACLE_BLOCK];
+      int in_block = p % ORACLE_BLOCK;
+      acc += w[p] * bf16_float(v_pool[v_index(block, h, in_block, i, n_kv, d)]);
+    }
+    out_row[i] = acc / total;
+  }
+  free(w);
+  return 0;
+}
+
+/* oracle_decode with oracle_decode_row_f32 for every row; out is float
+ * [num_seqs][n_q][d]. Returns as oracle_decode. */
+int oracle_decode_f32(float* out, const uint16_t* q, const uint16_t* k_pool,
+                      const uint16_t* v_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs,
+                      int max_blocks_per_seq, int num_blocks, int n_q, int n_kv,
+                      int d, float scale) {
+  if (n_kv <= 0 || n_q % n_kv != 0) return -3;
+  int group = n_q / n_kv;
+  int status = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    int ctx = context_lens[s];
+    int too_long = ctx > ORACLE_BLOCK * max_blocks_per_seq;
+    for (int j = 0; j < n_q; ++j) {
+      float* row = out + ((size_t)s * n_q + j) * d;
+      if (too_long) {
+        for (int i = 0; i < d; ++i) row[i] = NAN;
+        status = -1;
+        continue;
+      }
+      int kv_head = j / group;
+      const uint16_t* q_row = q + ((size_t)s * n_q + j) * d;
+      const int32_t* table_row = block_tables + (size_t)s * max_blocks_per_seq;
+      int rc = oracle_decode_row_f32(row, q_row, k_pool, v_pool, table_row, ctx, num_blocks,
+                                     n_kv, kv_head, d, scale);
       if (rc == -2) return -2;
       if (rc != 0) status = -1;
     }

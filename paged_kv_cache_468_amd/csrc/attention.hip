@@ -1473,7 +1473,6 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane & 15;
   const int r = lane >> 4;
   const int n_rt = (a.qrows + kPfRows - 1) / kPfRows;   // row tiles per (sequence, KV head)
   const int unit = logical_workgroup(a);

@@ -320,6 +320,145 @@ def check_invalid_inputs(orc):
 
 
 # ---------------------------------------------------------------------------
+# the decode's single-precision twin (the naive fp32 loop)
+
+U32 = 2.0 ** -24   # unit roundoff of binary32
+
+
+def _gamma(n):
+    return n * U32 / (1 - n * U32)
+
+
+def _f32_bound(case, scale):
+    """A bound on |f32 - exact| per (sequence, head) from the operations the
+    fp32 loop performs, in the standard model (each operation's result is the
+    exact one times (1 + e), |e| <= u; a sum of n terms within gamma_n of the
+    sum of magnitudes):
+      score   |dz| <= |scale| gamma_d sum_i |q_i k_i| + u |z|
+      z - top adds both errors and one rounding: D = 2 max|dz| + u max|z - top|
+      expf    within 2 u of its argument's exponential (glibc's expf is
+              correctly rounded in almost all cases, below 1 ulp otherwise)
+      weights relative error E = exp(D) - 1 + 2u
+      sums    gamma_ctx on the total, gamma_(ctx+1) on the weighted values
+    out = A / T errs by at most (|dA| + |out| |dT|) / T + u |out|, with
+    |dA| <= (E + gamma_(ctx+1)) sum w |v| and |dT| <= (E + gamma_ctx) T."""
+    sh = case.shape
+    G = sh.n_q // sh.n_kv
+    B = len(case.tables.context_lens)
+    bound = np.zeros((B, sh.n_q))
+    for s in range(B):
+        kc, vc = w.gather_contiguous(case.k_pool, case.v_pool, case.tables, s)
+        k = w.bf16_to_f32(kc).astype(np.float64)
+        v = w.bf16_to_f32(vc).astype(np.float64)
+        ctx = k.shape[1]
+        for j in range(sh.n_q):
+            q = w.bf16_to_f32(case.q[s, j]).astype(np.float64)
+            kh, vh = k[j // G], v[j // G]
+            z = scale * (kh @ q)
+            dz = abs(scale) * _gamma(sh.d) * (np.abs(kh) @ np.abs(q)) + U32 * np.abs(z)
+            D = 2 * dz.max() + U32 * (z.max() - z.min())
+            E = math.expm1(D) + 2 * U32
+            wgt = np.exp(z - z.max())
+            T = wgt.sum()
+            out = (wgt @ vh) / T
+            dA = (E + _gamma(ctx + 1)) * (wgt @ np.abs(vh))
+            dT = (E + _gamma(ctx)) * T
+            bound[s, j] = ((dA + np.abs(out) * dT) / T + U32 * np.abs(out)).max()
+    return bound
+
+
+F32_CASES = [  # (n_q, n_kv, d, context lengths, scale or None for 1/sqrt(d))
+    (20, 4, 64, [17, 40, 77, 130, 1], None),
+    (32, 8, 128, [300, 64, 1, 1000], None),
+    (8, 1, 64, [5, 48, 49, 2000], 0.37),
+    (64, 8, 128, [33, 700], None),
+]
+
+
+def check_f32_within_bound_of_twin(orc):
+    """The fp32 loop against its float64 twin (itself pinned to torch's
+    scaled_dot_product_attention in float64): every row within the rounding
+    bound of the fp32 operations (_f32_bound; a worst case, 1e-5 to 1e-3 at
+    these inputs, against an observed few 1e-7)."""
+    for i, (n_q, n_kv, d, ctx, scale) in enumerate(F32_CASES):
+        case = w.host_case(_small_shape(n_q, n_kv, d), 700 + i, context_lens=ctx, spare_blocks=2)
+        sc = 1 / math.sqrt(d) if scale is None else scale
+        o64, r64 = _decode(orc, case, sc)
+        o32, r32 = orc.decode_f32(case.q, case.k_pool, case.v_pool, case.tables.block_tables,
+                                  case.tables.context_lens, n_kv, sc)
+        assert r64 == 0 and r32 == 0 and o32.dtype == np.float32
+        err = np.abs(o32.astype(np.float64) - o64).max(axis=2)
+        bound = _f32_bound(case, sc)
+        assert (err <= bound).all(), (i, float(err.max()), float(bound.min()))
+
+
+def check_f32_exact_cases(orc):
+    """Cases the fp32 loop must get exactly: one cached token (its weight is
+    expf(0) = 1, so out is that token's value), values all equal to a power
+    of two c (scaling by c commutes with every rounding, so out = c), and
+    the same bits for an identity and a permuted block table."""
+    case = w.host_case(_small_shape(8, 2, 128), 3, context_lens=[1, 1, 1])
+    out, rc = orc.decode_f32(case.q, case.k_pool, case.v_pool, case.tables.block_tables,
+                             case.tables.context_lens, 2, case.shape.scale)
+    assert rc == 0
+    for s in range(3):
+        _, vc = w.gather_contiguous(case.k_pool, case.v_pool, case.tables, s)
+        assert np.array_equal(out[s], np.repeat(w.bf16_to_f32(vc[:, 0, :]), 4, axis=0))
+    case = w.host_case(_small_shape(5, 1, 64), 4, context_lens=[7, 16, 100, 257])
+    case.v_pool[case.tables.used] = w.bf16_bits(np.array([-0.5], np.float32))[0]
+    out, rc = orc.decode_f32(case.q, case.k_pool, case.v_pool, case.tables.block_tables,
+                             case.tables.context_lens, 1, case.shape.scale)
+    assert rc == 0 and (out == np.float32(-0.5)).all()
+    sh = _small_shape(20, 4, 64)
+    a = w.host_case(sh, 21, context_lens=[17, 40, 77, 130], permute=False)
+    b = w.host_case(sh, 21, context_lens=[17, 40, 77, 130], permute=True)
+    oa, _ = orc.decode_f32(a.q, a.k_pool, a.v_pool, a.tables.block_tables, a.tables.context_lens,
+                           4, sh.scale)
+    ob, _ = orc.decode_f32(b.q, b.k_pool, b.v_pool, b.tables.block_tables, b.tables.context_lens,
+                           4, sh.scale)
+    assert np.array_equal(oa, ob)
+
+
+def check_f32_large_logits(orc):
+    """Scale 100: scores in the thousands, where expf of an unshifted score
+    overflows. Rows whose largest score leads the next by more than 30
+    natural units are, to within e^-30 of the weights, that token's value."""
+    case = w.host_case(_small_shape(4, 2, 64), 9, context_lens=[40, 90])
+    out, rc = orc.decode_f32(case.q, case.k_pool, case.v_pool, case.tables.block_tables,
+                             case.tables.context_lens, 2, 100.0)
+    assert rc == 0 and np.isfinite(out).all()
+    checked = 0
+    for s in range(2):
+        kc, vc = w.gather_contiguous(case.k_pool, case.v_pool, case.tables, s)
+        for j in range(4):
+            q = w.bf16_to_f32(case.q[s, j]).astype(np.float64)
+            z = 100.0 * (w.bf16_to_f32(kc[j // 2]).astype(np.float64) @ q)
+            top2 = np.sort(z)[-2:]
+            if top2[1] - top2[0] > 30:
+                v_top = w.bf16_to_f32(vc[j // 2, int(np.argmax(z))])
+                assert np.abs(out[s, j] - v_top).max() < 1e-6, (s, j)
+                checked += 1
+    assert checked >= 4, checked
+
+
+def check_f32_invalid_inputs(orc):
+    """As the float64 decode: NaN rows and status -1 for a bad block id or a
+    context length below one; the other rows finite."""
+    sh = _small_shape(4, 2, 64)
+    case = w.host_case(sh, 51, context_lens=[20, 30])
+    bt = case.tables.block_tables.copy()
+    bt[1, 1] = case.tables.num_blocks
+    out, rc = orc.decode_f32(case.q, case.k_pool, case.v_pool, bt, case.tables.context_lens, 2,
+                             sh.scale)
+    assert rc == -1 and np.isnan(out[1]).all() and np.isfinite(out[0]).all()
+    cl = case.tables.context_lens.copy()
+    cl[0] = 0
+    out, rc = orc.decode_f32(case.q, case.k_pool, case.v_pool, case.tables.block_tables, cl, 2,
+                             sh.scale)
+    assert rc == -1 and np.isnan(out[0]).all() and np.isfinite(out[1]).all()
+
+
+# ---------------------------------------------------------------------------
 # verification attention (q_len query tokens per sequence, causal among them)
 
 def _verify_case(seed, n_q, n_kv, d, ctx, q_len):
@@ -415,4 +554,5 @@ ALL_CHECKS = [check_kv_sizes, check_kv_linearity, check_append_golden, check_wri
               check_constant_values, check_equal_keys, check_sdpa, check_large_logits,
               check_block_permutation, check_shared_prefix, check_group_equals_repeat,
               check_invalid_inputs, check_verify_one_token_is_decode, check_verify_sdpa,
-              check_verify_causal, check_verify_invalid]
+              check_verify_causal, check_verify_invalid, check_f32_within_bound_of_twin,
+              check_f32_exact_cases, check_f32_large_logits, check_f32_invalid_inputs]

@@ -78,3 +78,42 @@ def test_prefix_call_alg_bytes():
     want = (per_tok * (own_tokens + 64) + 5 * 32 * 128 * 6 + 4 * (tiles + 4) + 4 * 5
             + 2 * 2 * 5 * 8 * 128 * 2)
     assert bench.prefix_call_alg_bytes(S, ctx) == want
+
+
+def test_cpu_baseline_reports_both_oracles():
+    """The CPU baseline's plumbing on a tiny state held in host tensors: the
+    float64 oracle's one-core and threaded runs and its single-precision
+    twin over the same pairs. The state's outputs are the float64 oracle's
+    own rows, so both parity figures of that oracle are 0 and the twin's
+    difference from it is its own rounding (well under 1e-5 here)."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import workload as w
+    sh = w.Shape("tiny", 2, 8, 2, 64, 3, 20, 90)
+    S = types.SimpleNamespace(shape=sh, B=3, k_pool=[], v_pool=[], q=[], out=[])
+    cases = [w.host_case(sh, 40 + l, context_lens=[20, 55, 90], share=False, permute=False)
+             for l in range(2)]
+    S.tables = cases[0].tables.block_tables
+    S.ctx = cases[0].tables.context_lens
+    as_t = lambda a: torch.from_numpy(a.view(np.int16).copy())
+    for c in cases:
+        assert np.array_equal(c.tables.block_tables, S.tables)
+        S.k_pool.append(as_t(c.k_pool))
+        S.v_pool.append(as_t(c.v_pool))
+        S.q.append(as_t(c.q))
+        want, rc = oracle.default().decode(c.q, c.k_pool, c.v_pool, S.tables, S.ctx, sh.n_kv,
+                                           sh.scale)
+        assert rc == 0
+        S.out.append(torch.from_numpy(want.astype(np.float32)))
+    multi, worst, done, worst_p = bench.cpu_baseline(torch, S, 0.05, 0.05)
+    single = multi["single_core"]
+    assert single["cores"] == 1 and single["kind"] == "oracle" and done >= 1
+    assert multi["cores"] >= 1 and multi["full_layers_checked"] >= 1
+    assert worst < 1e-6 and worst_p < 1e-6   # the fp32 copy of the oracle's own rows
+    twin = single["fp32_twin"]
+    assert twin["value"] > 0 and twin["cores"] == 1
+    assert 0 < twin["max_abs_vs_float64_oracle"] < 1e-5

@@ -73,6 +73,24 @@ def test_random_shapes(pkv, orc, case, fused):
     print(f"case {CASES[case]}: max-abs {err:.2e}")
 
 
+@pytest.mark.parametrize("case", [0, 2, 3, 6])
+def test_matches_fp32_oracle(pkv, orc, case):
+    """The same cases against the naive fp32 loop (the oracle's
+    single-precision twin) as well: within 1e-3 of it too, and the two
+    oracles within 1e-5 of each other."""
+    n_q, n_kv, d, ctx, part = CASES[case]
+    hc = w.host_case(_shape(n_q, n_kv, d), 3000 + case, context_lens=ctx, spare_blocks=3)
+    got, _ = _check_case(pkv, orc, hc, partition=part, fused=True)
+    want64, _, k_ref, v_ref = oracle_step(orc, hc)
+    want32, rc = orc.decode_f32(hc.q, k_ref, v_ref, hc.tables.block_tables,
+                                hc.tables.context_lens, n_kv, hc.shape.scale)
+    assert rc == 0
+    want32 = want32.astype(np.float64)
+    e32, twin = max_abs(got, want32), max_abs(want32, want64)
+    print(f"case {case}: max-abs vs fp32 oracle {e32:.2e}, fp32 vs float64 oracle {twin:.2e}")
+    assert e32 <= TOL and twin <= 1e-5
+
+
 def test_partition_merge_agrees(pkv, orc):
     """Different partition sizes only change where the running softmax is
     split; the merged results agree to fp32 rounding."""

@@ -44,6 +44,16 @@ MUTANTS = {
     "verify_short_context_accepted": ("int bad_ctx = ctx < q_len ||", "int bad_ctx ="),
     "kv_bytes_no_two": ("return (uint64_t)2 * (uint64_t)n_layers", "return (uint64_t)n_layers"),
     "kv_bytes_no_precision": (" *\n         (uint64_t)bytes_per_value;", ";"),
+    "f32_dropped_scale": ("w[p] = scale * qk;", "w[p] = qk;"),
+    "f32_exp_sign": ("w[p] = expf(w[p] - top);", "w[p] = expf(top - w[p]);"),
+    "f32_max_not_subtracted": ("w[p] = expf(w[p] - top);", "w[p] = expf(w[p]);"),
+    "f32_no_normalisation": ("out_row[i] = acc / total;", "out_row[i] = acc;"),
+    "f32_kv_head_modulo": ("int kv_head = j / group;", "int kv_head = j % n_kv;"),
+    "f32_v_slot_from_dim": ("      acc += w[p] * bf16_float(v_pool[v_index(block, h, in_block, i, n_kv, d)]);",
+                            "      acc += w[p] * bf16_float(v_pool[v_index(block, h, i % ORACLE_BLOCK, i, n_kv, d)]);"),
+    "f32_context_off_by_one": ("  for (int p = 0; p < ctx; ++p) {\n    int32_t block",
+                               "  for (int p = 0; p < ctx - 1; ++p) {\n    int32_t block"),
+    "f32_last_token_dropped_from_sum": ("    total += w[p];", "    if (p + 1 < ctx) total += w[p];"),
 }
 
 
