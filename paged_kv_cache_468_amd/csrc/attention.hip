@@ -727,7 +727,11 @@ __device__ inline bool process_segment(const DecodeArgs& a, int lane, int s, int
 //   Softmax: base 2, reference maximum with the same slack as the matrix
 //      path; a ballot finds whether any token exceeds it before any
 //      reduction is taken.
-// At most kVecMaxG query rows per KV head.
+// The rows per KV head are a compile-time count VG (1, 2, 4, 5 or 8; a
+// group size in between takes the next, its extra rows computed on zero
+// queries and dropped), so a tile is straight-line code: every row's
+// scores, one ballot over all rows for the rare rescale, then every row's
+// weights and P.V.
 constexpr int kVecMaxG = 8;
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
@@ -764,22 +768,20 @@ __device__ inline float dot8_bf16(const bf16x8_t& k, const bf16x8_t& q, float ac
 // row g: m_run[g] (identical in every lane), l_run[g] (this lane's token's
 // weights: every token is counted by the four lanes of its quad) and
 // acc[g][m] (dim 16m + c over this lane's tokens 4r .. 4r+3).
-template <int D, bool STREAM, int NBUF>
+template <int D, bool STREAM, int NBUF, int VG>
 __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s, int h, int ctx,
                                             int ta, int tb, bool store_new,
-                                            const SegPre<D, 1>& pre,
-                                            float (&acc)[kVecMaxG][D / 16],
-                                            float (&m_run)[kVecMaxG], float (&l_run)[kVecMaxG]) {
+                                            const SegPre<D, 1>& pre, float (&acc)[VG][D / 16],
+                                            float (&m_run)[VG], float (&l_run)[VG]) {
   constexpr int KM = D / 32;
   constexpr int VM = D / 16;
   const int c = lane & 15;
   const int r = lane >> 4;
   const int tok = 4 * r + (c >> 2);   // this lane's token within a tile
   const int quarter = 8 * (c & 3);    // its first dim within each 32
-  const int G = a.group;
 
 #pragma unroll
-  for (int g = 0; g < kVecMaxG; ++g) {
+  for (int g = 0; g < VG; ++g) {
 #pragma unroll
     for (int m = 0; m < VM; ++m) acc[g][m] = 0.f;
     m_run[g] = -__builtin_inff();
@@ -790,9 +792,9 @@ __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s
   // writes of the slice are volatile, so they stay in program order (one
   // wave's LDS operations complete in order) and the per-tile reads are not
   // hoisted into registers.
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kVecMaxG * D];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][VG * D];
   volatile lds_u16_t* qs = (volatile lds_u16_t*)q_lds[threadIdx.x >> 6];
-  if (c < kVecMaxG) {
+  if (c < VG) {
 #pragma unroll
     for (int m = 0; m < KM; ++m)
       *(volatile lds_bf16x8_t*)(qs + c * D + 32 * m + 8 * r) = pre.qv[0][m];
@@ -893,9 +895,10 @@ __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s
         vr[m] = __builtin_bit_cast(bf16x4_t, wv);
       }
     }
+    // every row's score of this lane's token
+    float x[VG];
 #pragma unroll
-    for (int g = 0; g < kVecMaxG; ++g) {
-      if (g >= G) break;
+    for (int g = 0; g < VG; ++g) {
       float sc = 0.f;
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
@@ -904,20 +907,36 @@ __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s
       }
       sc += dpp_f32<kDppQuadXor1>(sc);
       sc += dpp_f32<kDppQuadXor2>(sc);   // the token's whole score, in all four lanes
-      float x = sc * a.scale_log2;
-      if (partly && tok >= last_valid) x = -__builtin_inff();
-      if (__ballot(x > m_run[g] + kRescaleSlack) != 0) {
-        float mx = x;
+      x[g] = (partly && tok >= last_valid) ? -__builtin_inff() : sc * a.scale_log2;
+    }
+    // one ballot for all rows; the reductions and rescales only when some
+    // token exceeds its row's reference maximum (rare after a row's first
+    // tile)
+    bool over = false;
+#pragma unroll
+    for (int g = 0; g < VG; ++g) over = over || x[g] > m_run[g] + kRescaleSlack;
+    if (__ballot(over) != 0) {
+#pragma unroll
+      for (int g = 0; g < VG; ++g) {
+        float mx = x[g];
 #pragma unroll
         for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float m_new = fmaxf(m_run[g], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-        m_run[g] = m_new;
-        l_run[g] *= alpha;
+        if (mx > m_run[g] + kRescaleSlack) {   // the same in every lane
+          const float m_new = fmaxf(m_run[g], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
 #pragma unroll
-        for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+          for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+        }
       }
-      const float p = __builtin_amdgcn_exp2f(x - m_run[g]);
+    }
+    bf16x8_t vv[VM];   // tokens 4r .. 4r+3 twice, the hi and the lo half of the pairs
+#pragma unroll
+    for (int m = 0; m < VM; ++m) vv[m] = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
+#pragma unroll
+    for (int g = 0; g < VG; ++g) {
+      const float p = __builtin_amdgcn_exp2f(x[g] - m_run[g]);
       l_run[g] += p;
       // weights of tokens 4r .. 4r+3, each as bf16 hi (truncated: exact
       // remainder) + lo (rounded), paired for the packed dot products
@@ -933,10 +952,7 @@ __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s
           bf16x8_t, u32x4_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3], lo[0] | (lo[1] << 16),
                             lo[2] | (lo[3] << 16)});
 #pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        const bf16x8_t vv = __builtin_shufflevector(vr[m], vr[m], 0, 1, 2, 3, 0, 1, 2, 3);
-        acc[g][m] = dot8_bf16(vv, pw, acc[g][m]);
-      }
+      for (int m = 0; m < VM; ++m) acc[g][m] = dot8_bf16(vv[m], pw, acc[g][m]);
     }
   };
 
@@ -975,19 +991,17 @@ __device__ inline bool process_segment_valu(const DecodeArgs& a, int lane, int s
 // accumulators over the four lanes r of a dim; then, as finish_rows does,
 // out directly or a partial. Lane (c, r) writes dims 16m + c for
 // m = r, r + 4, ... of every row.
-template <int D>
+template <int D, int VG>
 __device__ inline void finish_rows_valu(const DecodeArgs& a, int lane, bool ok, bool whole,
-                                        int64_t slot, int s, int h,
-                                        float (&acc)[kVecMaxG][D / 16],
-                                        const float (&m_run)[kVecMaxG],
-                                        const float (&l_run)[kVecMaxG]) {
+                                        int64_t slot, int s, int h, float (&acc)[VG][D / 16],
+                                        const float (&m_run)[VG], const float (&l_run)[VG]) {
   constexpr int VM = D / 16;
   const int c = lane & 15;
   const int r = lane >> 4;
   if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
   const float nan = __builtin_nanf("");
 #pragma unroll
-  for (int g = 0; g < kVecMaxG; ++g) {
+  for (int g = 0; g < VG; ++g) {
     if (g >= a.group) break;
     float l = l_run[g];
 #pragma unroll
@@ -1183,9 +1197,9 @@ __device__ inline void prefix_segment(const DecodeArgs& a, int lane, int pu, int
 // together. (With a single wave, one order holds both.) The wave holding
 // a unit's first tile records, for the merge kernel, the unit's first
 // partial slot and its number of partials (1: written here).
-template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX, bool VALU = false>
+template <int D, int NG, bool CAUSAL, int NBUF, bool PREFIX, int VG = 0>
 __device__ inline void balanced_body(const DecodeArgs& a) {
-  static_assert(!VALU || (!PREFIX && !CAUSAL && NG == 1), "vector-ALU path: the plain decode only");
+  static_assert(VG == 0 || (!PREFIX && !CAUSAL && NG == 1), "vector-ALU path: the plain decode only");
   constexpr int VM = D / 16;
   const int lane = threadIdx.x & 63;
   const int w = logical_workgroup(a) * kWaves + (threadIdx.x >> 6);
@@ -1344,16 +1358,16 @@ __device__ inline void balanced_body(const DecodeArgs& a) {
           skip2 + tb2, pre2);
     }
 
-    if constexpr (VALU) {
-      float vacc[kVecMaxG][VM];
-      float vm[kVecMaxG], vl[kVecMaxG];
+    if constexpr (VG > 0) {
+      float vacc[VG][VM];
+      float vm[VG], vl[VG];
       const bool ok =
           scan_shares_first<KEEP>(a, ts, s)
-              ? process_segment_valu<D, false, NBUF>(a, lane, s, h, ctx, pos, tb, qg == 0, pre,
-                                                     vacc, vm, vl)
-              : process_segment_valu<D, true, NBUF>(a, lane, s, h, ctx, pos, tb, qg == 0, pre,
-                                                    vacc, vm, vl);
-      finish_rows_valu<D>(a, lane, ok, whole, (int64_t)w + u, s, h, vacc, vm, vl);
+              ? process_segment_valu<D, false, NBUF, VG>(a, lane, s, h, ctx, pos, tb, qg == 0,
+                                                         pre, vacc, vm, vl)
+              : process_segment_valu<D, true, NBUF, VG>(a, lane, s, h, ctx, pos, tb, qg == 0,
+                                                        pre, vacc, vm, vl);
+      finish_rows_valu<D, VG>(a, lane, ok, whole, (int64_t)w + u, s, h, vacc, vm, vl);
     } else {
       f32x4_t acc[NG][VM];
       float m_run[NG], l_run[NG];
@@ -1402,10 +1416,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
 
 // The decode's partition kernel with its scores and P.V on the vector ALUs
 // (process_segment_valu), for comparison with the matrix-core kernel above:
-// the same split, waves, ring and partials.
-template <int D>
+// the same split, waves, ring and partials; VG rows per KV head. Two waves
+// per SIMD at head_dim 128 (with two register sets) measured slower at one
+// and two rows and spilled at four; at head_dim 64 with eight rows a few
+// values spill.
+template <int D, int VG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void paged_attn_balanced_valu_kernel(DecodeArgs a) {
-  balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing, false, true>(a);
+  balanced_body<D, 1, false, D == 128 ? kDecodeRing128 : kRing, false, VG>(a);
 }
 
 // The verification pass: q_len query tokens per sequence, causal among
@@ -2290,13 +2307,27 @@ extern "C" int pkv_decode_step_partition_valu(PKV_STEP_PARAMS) {
   if (!k_new || !v_new) return PKV_EINVAL;
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
+  const int vg = a.group <= 2 ? a.group : (a.group <= 4 ? 4 : (a.group == 5 ? 5 : 8));
   const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
-  if (d == 128)
-    hipLaunchKernelGGL(paged_attn_balanced_valu_kernel<128>, dim3(grid), dim3(256), 0,
-                       (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL(paged_attn_balanced_valu_kernel<64>, dim3(grid), dim3(256), 0,
-                       (hipStream_t)stream, a);
+  const hipStream_t st = (hipStream_t)stream;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, a); };
+  if (d == 128) {
+    switch (vg) {
+      case 1: go(paged_attn_balanced_valu_kernel<128, 1>); break;
+      case 2: go(paged_attn_balanced_valu_kernel<128, 2>); break;
+      case 4: go(paged_attn_balanced_valu_kernel<128, 4>); break;
+      case 5: go(paged_attn_balanced_valu_kernel<128, 5>); break;
+      default: go(paged_attn_balanced_valu_kernel<128, 8>); break;
+    }
+  } else {
+    switch (vg) {
+      case 1: go(paged_attn_balanced_valu_kernel<64, 1>); break;
+      case 2: go(paged_attn_balanced_valu_kernel<64, 2>); break;
+      case 4: go(paged_attn_balanced_valu_kernel<64, 4>); break;
+      case 5: go(paged_attn_balanced_valu_kernel<64, 5>); break;
+      default: go(paged_attn_balanced_valu_kernel<64, 8>); break;
+    }
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
