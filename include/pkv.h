@@ -331,8 +331,8 @@ int pkv_decode_step_partition(float* out, const void* q, const void* k_new,
  * the scores and the weighted sum of the values (the weights split into
  * bf16 hi + lo, as the matrix path splits them); the same split, loads,
  * append and partials, so pkv_paged_attn_merge with the same arguments
- * finishes the step. The unit's query rows are staged in at most 8 KiB of LDS per
- * workgroup (head_dim 128). Kept to measure what the matrix cores buy on
+ * finishes the step. The unit's query rows are staged in at most 8 KiB of
+ * LDS per workgroup. Kept to measure what the matrix cores buy on
  * this memory-bound path (the pages call the decode a streaming read of the
  * cache: [M23] 23.2; [SLS] "Why decoding is limited by memory"). Results
  * within 1e-3 of the oracle, not bit-identical to the matrix path (another
