@@ -1103,7 +1103,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
               "(no collectives or sharding are implemented).", file=sys.stderr)
         sys.exit(2)
 
