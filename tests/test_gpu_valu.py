@@ -2,8 +2,9 @@
 (pkv_decode_step_partition_valu), kept to measure what the matrix cores
 buy. Its results are held to the same bar as the matrix path: every row
 within 1e-3 of the oracle, the pools bit-exact after the append; bad block
-ids and context lengths caught the same way. Shapes: 1, 4, 5 and 8 query
-heads per KV head, both head sizes, ragged and one-token contexts, more
+ids and context lengths caught the same way. Shapes: 1 to 8 query heads per
+KV head (3, 6 and 7 run on the next compiled row count, the extra rows
+dropped), both head sizes, ragged and one-token contexts, more
 waves than tiles, and the benchmark's LLaMA-3-8B and 80-layer layers at
 full size (rows sampled). The shaped-score cases of the rescale tests
 (late jumps, early peaks, staircases, large scales) drive its running
@@ -49,6 +50,9 @@ CASES = [  # n_q, n_kv, d, contexts
     (64, 8, 128, [8000, 8000, 100]),            # G = 8
     (8, 1, 128, [123, 456, 789]),               # MQA, G = 8
     (6, 3, 64, [2, 33, 64, 65, 129]),           # G = 2
+    (12, 4, 128, [700, 31, 1]),                 # G = 3 (compiled as 4 rows)
+    (24, 4, 64, [500, 17, 2000]),               # G = 6 (as 8)
+    (14, 2, 128, [1500, 64, 9]),                # G = 7 (as 8)
 ]
 
 
