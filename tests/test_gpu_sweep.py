@@ -1,5 +1,6 @@
-"""A seeded random sweep of the decode step, the verification pass, chunked
-prefill and the shared-prefix step against the oracle, beside the
+"""A seeded random sweep of the decode step (and its vector-ALU partition
+kernel), the verification pass, chunked prefill and the shared-prefix step
+against the oracle, beside the
 hand-picked cases of the other tests. Each
 case draws: KV heads (1, 2, 4, 8) and group size (1 .. 20, at most 64 query
 heads), head size 64 or 128, 1 .. 24 sequences whose contexts mix tiny ones,
@@ -68,6 +69,35 @@ def test_decode_sweep(pkv, orc, seed):
     hc, max_ctx = _host(n_q, n_kv, d, ctx, slack, seed)
     dc = DevCase(hc)
     got = gpu_step(pkv, dc, partition=part, max_ctx=max_ctx, fused=fused)
+    want, rc, k_ref, v_ref = oracle_step(orc, hc)
+    assert rc == 0 and int(dc.err.item()) == 0
+    assert np.array_equal(to_host_u16(dc.k_pool), k_ref)
+    assert np.array_equal(to_host_u16(dc.v_pool), v_ref)
+    e = max_abs(got, want)
+    print(f"  max-abs {e:.2e}")
+    assert np.isfinite(got).all() and e <= TOL
+
+
+@pytest.mark.parametrize("seed", range(500, 515))
+def test_valu_sweep(pkv, orc, seed):
+    """The vector-ALU partition kernel and the merge on the same kind of
+    draws (group sizes up to 8, the balanced split)."""
+    import torch
+    g = np.random.default_rng([9500, seed])
+    n_kv = int(g.choice([1, 2, 4, 8]))
+    G = int(g.integers(1, 9))
+    n_q, _, d, ctx, slack, _, _, _ = _draw(seed)
+    n_q = n_kv * G
+    print(f"seed {seed}: {n_q}/{n_kv} heads, d {d}, {len(ctx)} sequences up to {max(ctx)}, "
+          f"slack {slack}", flush=True)
+    hc, max_ctx = _host(n_q, n_kv, d, ctx, slack, seed)
+    dc = DevCase(hc)
+    ws = pkv.pkv_decode_step_partition_valu(dc.out, dc.q, dc.k_new, dc.v_new, dc.k_pool, dc.v_pool,
+                                            dc.bt, dc.cl, hc.shape.scale, max_ctx, err_flag=dc.err)
+    pkv.pkv_paged_attn_merge(dc.out, dc.q, dc.k_pool, dc.v_pool, dc.bt, dc.cl, hc.shape.scale,
+                             max_ctx, workspace=ws, err_flag=dc.err)
+    torch.cuda.synchronize()
+    got = dc.out.cpu().numpy().astype(np.float64)
     want, rc, k_ref, v_ref = oracle_step(orc, hc)
     assert rc == 0 and int(dc.err.item()) == 0
     assert np.array_equal(to_host_u16(dc.k_pool), k_ref)
