@@ -1450,14 +1450,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PREFIX && D
 // wave's LDS read is lane-linear and free of bank conflicts, and the
 // threads that stage a slot write consecutive addresses too (the pool
 // reads that feed them: whole 64-byte runs of a K row, whole 512-byte runs
-// of a V block). A lane's V operands of two consecutive MFMA steps sit
-// together, one 16-byte read for both; the V slots of the sequence's last
-// block past the context are zeroed there, once per workgroup. Per tile and wave: for
-// each 16-token block, scores (K as A, q as B, as in the decode) for both
-// row groups; one running-max decision per tile; P split into bf16 hi + lo
-// for the P.V MFMAs (as in the decode). Causal: rows see positions up to
-// ctx - q_len + their token; tiles past the workgroup's last row are not
-// loaded; blocks of a tile past the limit of all rows are skipped.
+// of a V block). The V slots of the sequence's last block past the context
+// are zeroed there, once per workgroup. Per tile and wave: for each
+// 16-token block, scores (K as A, q as B, as in the decode) for both row
+// groups; one running-max decision per tile; P split into bf16 hi + lo.
+// Unlike the decode, a P.V MFMA's 32-long inner dimension spans two blocks
+// (4 tokens of each per lane) with the hi parts, and a second MFMA on the
+// same V operand takes the lo parts: the V operand is 8 distinct values
+// read straight from LDS, with no copy to repeat it for hi and lo.
+// Causal: rows see positions up to ctx - q_len + their token; tiles past
+// the workgroup's last row are not loaded, and the masking runs only in
+// the tiles that reach its first row's limit.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kPfWaves = 8;                      // waves per workgroup
@@ -1465,13 +1468,16 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 32 * kPfWaves;           // query rows per workgroup
 constexpr int kPfTile = 64;                      // tokens per LDS tile
 constexpr int kPfSub = kPfTile / 16;             // blocks per tile
+static_assert(kPfSub % 2 == 0, "P.V MFMAs take the tile's blocks in pairs");
 
 template <int D>
 struct PfSmem {
-  // MFMA operand order: slot (block, step) holds, for lane i, the 16 bytes
-  // of K (8 bytes of V) that lane i feeds to that MFMA, at i * 16 (i * 8)
+  // MFMA operand order: K slot (block, step) holds, for lane i, the 16
+  // bytes of K that lane i feeds to that score MFMA, at i * 16; V slot
+  // (pair of blocks, step) the 16 bytes of V it feeds to that P.V MFMA
+  // (4 tokens of one dimension from each of the two blocks)
   uint16_t k[2][kPfSub * (D / 32)][64][8];
-  uint16_t v[2][kPfSub * (D / 32)][64][8];   // two MFMA steps' V per lane
+  uint16_t v[2][kPfSub / 2 * (D / 16)][64][8];
 };
 
 template <int D>
@@ -1481,7 +1487,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   constexpr int KM = D / 32;
   constexpr int VM = D / 16;
   constexpr int K_CHUNKS = kPfSub * KM * 64;     // 16-byte operand slots per tile
-  constexpr int V_CHUNKS = kPfSub * VM * 64;     // 8-byte operand slots per tile
+  constexpr int V_CHUNKS = kPfSub / 2 * VM * 64; // 16-byte operand slots per tile
   constexpr int K_PER = K_CHUNKS / kPfThreads;
   constexpr int V_PER = V_CHUNKS / kPfThreads;
   static_assert(K_PER * kPfThreads == K_CHUNKS && V_PER * kPfThreads == V_CHUNKS, "tile split");
@@ -1492,11 +1498,42 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   const int wave = tid >> 6;
   const int r = lane >> 4;
   const int n_rt = (a.qrows + kPfRows - 1) / kPfRows;   // row tiles per (sequence, KV head)
-  const int unit = logical_workgroup(a);
-  if (unit >= a.num_seqs * a.n_kv * n_rt) return;
-  const int rt = unit % n_rt;
-  const int h = (unit / n_rt) % a.n_kv;
-  const int s = unit / (n_rt * a.n_kv);
+  // Workgroup -> (sequence, KV head, row tile). The row tiles of one
+  // (sequence, KV head) pair read the same K/V tiles, so they run on one XCD
+  // (workgroup b runs on XCD b % kXcds) and share its L2. The pairs, ordered
+  // longest context first (ties by sequence index) with a sequence's KV
+  // heads adjacent, are dealt to the XCDs in a snake order (0..7, 7..0, ...):
+  // every XCD gets a like share of short and long sequences, and starts its
+  // longest pairs first. Ranking more sequences than the workgroup has
+  // threads falls back to index order.
+  const int xcd = blockIdx.x % kXcds;
+  const int k_in_xcd = blockIdx.x / kXcds;
+  const int deal = k_in_xcd / n_rt;
+  const int pair = deal * kXcds + ((deal & 1) ? kXcds - 1 - xcd : xcd);
+  if (pair >= a.num_seqs * a.n_kv) return;
+  const int rt = k_in_xcd % n_rt;
+  const int h = pair % a.n_kv;
+  const int rank = pair / a.n_kv;
+  int s = rank;
+  if (a.num_seqs > 1 && a.num_seqs <= kPfThreads) {
+    // rank by work (tiles to read); the K buffer of the second stage holds
+    // the keys until the first tile is stored
+    int* key = reinterpret_cast<int*>(&sm.k[1][0][0][0]);
+    int* found = key + kPfThreads;
+    if (tid < a.num_seqs) key[tid] = seq_tiles(a.context_lens[tid], a.q_len, a.max_ctx);
+    __syncthreads();
+    if (tid < a.num_seqs) {
+      const int mine = key[tid];
+      int above = 0;
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const int other = key[j];
+        above += (other > mine || (other == mine && j < tid)) ? 1 : 0;
+      }
+      if (above == rank) *found = tid;
+    }
+    __syncthreads();
+    s = *found;
+  }
   const int ctx = a.context_lens[s];
   const int qg = rt * kPfWaves + wave;              // this wave's 32-row group
   const Rows<NG> rw = rows_of<NG, true>(a, lane, s, h, qg, ctx);
@@ -1525,17 +1562,28 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   const int64_t block_stride = (int64_t)a.n_kv * tile_elems;
   const int last_block = (ctx - 1) >> 4;
   const int last_valid = ctx - last_block * 16;
-  const int first_masked = ctx - a.q_len + 1;
+  // the first position that one of the workgroup's rows may not see (its
+  // first row's limit + 1; every later row sees more)
+  const int first_masked = ctx - a.q_len + 1 + (rt * kPfRows) / a.group;
 
-  // this wave's q rows, as the B operand of the score MFMA
+  // this wave's q rows, as the B operand of the score MFMA. The scale is
+  // applied inside the exponent (one fused multiply-add per score), which
+  // needs a positive factor: for a negative scale the rows are negated
+  // (exact in bf16; the products and their sum change sign only), and for
+  // a zero scale they are zeroed, which gives every visible score 0.
+  const float sl = a.scale_log2 == 0.f ? 1.f : fabsf(a.scale_log2);
+  const uint32_t q_xor = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const bool q_zero = a.scale_log2 == 0.f;
   bf16x8_t qv[NG][KM];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      const bf16x8_t v = *(const bf16x8_t*)(q_row + 32 * m + 8 * r);
-      qv[g][m] = rw.valid[g] ? v : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      u32x4_t v = *(const u32x4_t*)(q_row + 32 * m + 8 * r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (rw.valid[g] && !q_zero) ? (v[e] ^ q_xor) : 0u;
+      qv[g][m] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -1546,7 +1594,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   // limit, but 0 * NaN would not be 0).
   bool bad = false;
   u32x4_t kst[K_PER];
-  u32x2_t vst[V_PER];
+  u32x2_t vst[V_PER][2];
   auto load_tile = [&](int t) {
     int ids[kPfSub];
 #pragma unroll
@@ -1575,16 +1623,21 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
-      // slot (sb, m, lane'): dim 16m + c, tokens 4r .. 4r+3
+      // slot (bp, m, lane'): dim 16m + c, tokens 4r .. 4r+3 of blocks 2bp
+      // and 2bp + 1
       const int ch = tid + i * kPfThreads;
-      const int sb = ch / (VM * 64);
+      const int bp = ch / (VM * 64);
       const int m = (ch / 64) % VM;
       const int ln = ch % 64;
-      int blk = ids[0];
+      int b0 = ids[0], b1 = ids[1];
 #pragma unroll
-      for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
-      vst[i] = *(const u32x2_t*)(a.v_pool + blk * block_stride + head_off + (16 * m + (ln & 15)) * 16 +
-                                 4 * (ln >> 4));
+      for (int j = 1; j < kPfSub / 2; ++j) {
+        b0 = bp == j ? ids[2 * j] : b0;
+        b1 = bp == j ? ids[2 * j + 1] : b1;
+      }
+      const int64_t in_blk = head_off + (16 * m + (ln & 15)) * 16 + 4 * (ln >> 4);
+      vst[i][0] = *(const u32x2_t*)(a.v_pool + b0 * block_stride + in_blk);
+      vst[i][1] = *(const u32x2_t*)(a.v_pool + b1 * block_stride + in_blk);
     }
   };
   // registers -> LDS for tile t (the zeroing of blocks past n_blocks is
@@ -1599,17 +1652,20 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const int sb = ch / (VM * 64);
-      const int m = (ch / 64) % VM;
+      const int bp = ch / (VM * 64);
       const int ln = ch % 64;
-      const int b = t * kPfSub + sb;
-      u32x2_t val = b < n_blocks ? vst[i] : u32x2_t{0u, 0u};
-      if (b == last_block && last_valid < 16) {   // slots past the context: zero (0 * NaN)
-        const int first = 4 * (ln >> 4);
-        val[0] &= (first < last_valid ? 0xFFFFu : 0u) | (first + 1 < last_valid ? 0xFFFF0000u : 0u);
-        val[1] &= (first + 2 < last_valid ? 0xFFFFu : 0u) | (first + 3 < last_valid ? 0xFFFF0000u : 0u);
+      const int first = 4 * (ln >> 4);
+      u32x2_t val[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int b = t * kPfSub + 2 * bp + half;
+        val[half] = b < n_blocks ? vst[i][half] : u32x2_t{0u, 0u};
+        if (b == last_block && last_valid < 16) {   // slots past the context: zero (0 * NaN)
+          val[half][0] &= (first < last_valid ? 0xFFFFu : 0u) | (first + 1 < last_valid ? 0xFFFF0000u : 0u);
+          val[half][1] &= (first + 2 < last_valid ? 0xFFFFu : 0u) | (first + 3 < last_valid ? 0xFFFF0000u : 0u);
+        }
       }
-      *(u32x2_t*)&sm.v[buf][sb * (VM / 2) + m / 2][ln][(m & 1) * 4] = val;
+      *(u32x4_t*)&sm.v[buf][ch / 64][ln][0] = u32x4_t{val[0][0], val[0][1], val[1][0], val[1][1]};
     }
   };
 
@@ -1623,16 +1679,26 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
     l_run[g] = 0.f;
   }
 
+  // -1 in the low (high) bf16 of a pair: a packed dot product with it
+  // subtracts that half, widened exactly, from a float. The empty asm
+  // statements keep the two words in registers as the bits written here
+  // (no immediate operand whose meaning for a bf16 pair the encoding fixes)
+  uint32_t neg_lo_bits = 0x0000BF80u, neg_hi_bits = 0xBF800000u;
+  asm volatile("" : "+v"(neg_lo_bits));
+  asm volatile("" : "+v"(neg_hi_bits));
+  const bf16x2_t neg_lo = __builtin_bit_cast(bf16x2_t, neg_lo_bits);
+  const bf16x2_t neg_hi = __builtin_bit_cast(bf16x2_t, neg_hi_bits);
   load_tile(0);
   store_tile(0, 0);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    // Scores of all the tile's blocks, both row groups, with no branch
-    // between them. Blocks past those loaded hold zeros and lie past every
-    // valid row's limit; positions past a row's limit or the context are
-    // masked only in the tiles that reach them.
+    // Raw scores (q.k, the scale not yet applied) of all the tile's
+    // blocks, both row groups, with no branch between them. Blocks past
+    // those loaded hold zeros and lie past every valid row's limit;
+    // positions past a row's limit or the context are masked (-inf) only
+    // in the tiles that reach one of the workgroup's limits.
     const bool edge = (t + 1) * kPfTile > first_masked;
     float x[NG][kPfSub][4];
 #pragma unroll
@@ -1648,7 +1714,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
         for (int m = 0; m < KM; ++m)
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e] * a.scale_log2;
+        for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e];
       }
     }
     if (edge) {
@@ -1662,21 +1728,25 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
             if (p0 + e >= ctx || p0 + e > rw.lim[g]) x[g][sb][e] = -__builtin_inff();
       }
     }
-    // running max per row, one decision per tile; P = hi + lo in bf16
-    // (packed round-to-nearest conversions; hi + lo carries ~16 bits of P).
-    // This vector-unit stretch runs at raised wave priority: the wave's
-    // chain to its P.V matrix ops is shortened while the other wave of the
-    // SIMD keeps the matrix pipe busy (628-630 -> 613-615 us per launch of
-    // the 8 x 512-token LLaMA-3-8B chunk, same box, alternating runs).
-    __builtin_amdgcn_s_setprio(1);
-    bf16x8_t pb[NG][kPfSub];
+    // running max per row (scaled, base 2), one decision per tile;
+    // P = 2^(x * scale - m) split into bf16 hi + lo (hi rounded to nearest,
+    // lo = P - hi rounded again: ~16 bits of P). The maximum is NaN-
+    // propagating (a NaN score makes the row NaN, as the oracle's would);
+    // across a row's four lane groups it is taken with the row swaps of
+    // gfx950 (lanes 16, then 32 apart), not through the LDS.
+    u32x4_t p_hi[NG][kPfSub / 2], p_lo[NG][kPfSub / 2];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      float mx = -__builtin_inff();
+      float raw = x[g][0][0];
 #pragma unroll
       for (int sb = 0; sb < kPfSub; ++sb)
-        mx = fmaxf(mx, fmaxf(fmaxf(x[g][sb][0], x[g][sb][1]), fmaxf(x[g][sb][2], x[g][sb][3])));
-      mx = wave_max_across_rows(mx);
+#pragma unroll
+        for (int e = (sb == 0 ? 1 : 0); e < 4; ++e) raw = __builtin_elementwise_maximum(raw, x[g][sb][e]);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
+      raw = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
+      raw = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      const float mx = raw == -__builtin_inff() ? raw : raw * sl;
       if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
         const float m_new = fmaxf(m_run[g], mx);
         float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
@@ -1686,36 +1756,43 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
         for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
       }
-      const float m_use = m_run[g] == -__builtin_inff() ? 0.f : m_run[g];
+      const float neg_m = m_run[g] == -__builtin_inff() ? 0.f : -m_run[g];
 #pragma unroll
       for (int sb = 0; sb < kPfSub; ++sb) {
-        f32x2_t p01 = {__builtin_amdgcn_exp2f(x[g][sb][0] - m_use),
-                       __builtin_amdgcn_exp2f(x[g][sb][1] - m_use)};
-        f32x2_t p23 = {__builtin_amdgcn_exp2f(x[g][sb][2] - m_use),
-                       __builtin_amdgcn_exp2f(x[g][sb][3] - m_use)};
-        l_run[g] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
-        const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
-        const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
-        const bf16x2_t l01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
-        const bf16x2_t l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
-        const u32x4_t pw = u32x4_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
-                                   __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
-        pb[g][sb] = __builtin_bit_cast(bf16x8_t, pw);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][0], sl, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][1], sl, neg_m));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][2], sl, neg_m));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][3], sl, neg_m));
+        l_run[g] += (p0 + p1) + (p2 + p3);
+        const bf16x2_t h01 = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        const bf16x2_t h23 = __builtin_convertvector((f32x2_t){p2, p3}, bf16x2_t);
+        const bf16x2_t l01 = __builtin_convertvector(
+            (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h01, neg_lo, p0, false),
+                      __builtin_amdgcn_fdot2_f32_bf16(h01, neg_hi, p1, false)}, bf16x2_t);
+        const bf16x2_t l23 = __builtin_convertvector(
+            (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h23, neg_lo, p2, false),
+                      __builtin_amdgcn_fdot2_f32_bf16(h23, neg_hi, p3, false)}, bf16x2_t);
+        const int half = 2 * (sb & 1);
+        p_hi[g][sb / 2][half] = __builtin_bit_cast(uint32_t, h01);
+        p_hi[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, h23);
+        p_lo[g][sb / 2][half] = __builtin_bit_cast(uint32_t, l01);
+        p_lo[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, l23);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
-    // P.V per block (the V slots past the context were zeroed when stored)
+    // P.V per pair of blocks: one LDS read gives a lane's V operand for
+    // both blocks (the V slots past the context were zeroed when stored),
+    // used by the hi and the lo MFMA of both row groups
 #pragma unroll
-    for (int sb = 0; sb < kPfSub; ++sb) {
+    for (int bp = 0; bp < kPfSub / 2; ++bp) {
 #pragma unroll
-      for (int m = 0; m < VM; m += 2) {
-        const bf16x8_t w = *(const bf16x8_t*)&sm.v[buf][sb * (VM / 2) + m / 2][lane][0];
-        const bf16x8_t v0 = __builtin_shufflevector(w, w, 0, 1, 2, 3, 0, 1, 2, 3);
-        const bf16x8_t v1 = __builtin_shufflevector(w, w, 4, 5, 6, 7, 4, 5, 6, 7);
+      for (int m = 0; m < VM; ++m) {
+        const bf16x8_t vv = *(const bf16x8_t*)&sm.v[buf][bp * VM + m][lane][0];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[g][sb], acc[g][m], 0, 0, 0);
-          acc[g][m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb[g][sb], acc[g][m + 1], 0, 0, 0);
+          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_hi[g][bp]),
+                                                              acc[g][m], 0, 0, 0);
+          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_lo[g][bp]),
+                                                              acc[g][m], 0, 0, 0);
         }
       }
     }
@@ -2503,10 +2580,14 @@ extern "C" int pkv_paged_prefill(float* out, const void* q, const void* k_pool, 
                          num_blocks, head_dim, scale, max_context_len, 0, nullptr, 0, err_flag,
                          false);
   if (rc != PKV_OK || num_seqs == 0) return rc;
-  // one workgroup per (sequence, KV head, kPfRows rows)
-  const int64_t wgs = (int64_t)num_seqs * n_kv_heads * ((a.qrows + kPfRows - 1) / kPfRows);
-  a.wg_per_xcd = (int)((wgs + kXcds - 1) / kXcds);
-  const unsigned grid = (unsigned)a.wg_per_xcd * kXcds;
+  // one workgroup per (sequence, KV head, kPfRows rows); the (sequence, KV
+  // head) pairs are dealt to the XCDs, kXcds at a time, each with all its
+  // row tiles (the kernel's mapping), so the grid is rounded up to whole deals
+  const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
+  const int64_t deals = (pairs + kXcds - 1) / kXcds;
+  const int64_t grid64 = deals * kXcds * ((a.qrows + kPfRows - 1) / kPfRows);
+  if (grid64 > INT32_MAX) return PKV_EINVAL;
+  const unsigned grid = (unsigned)grid64;
   if (d == 128)
     hipLaunchKernelGGL(paged_prefill_lds_kernel<128>, dim3(grid), dim3(kPfThreads), 0,
                        (hipStream_t)stream, a);

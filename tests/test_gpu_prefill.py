@@ -161,3 +161,31 @@ def test_largest_chunk_sampled(pkv, orc):
         e = max(e, float(np.abs(got[0, i, j] - want).max()))
     print(f"16,384-token chunk, {len(picks)} sampled rows: max-abs {e:.2e}")
     assert e <= TOL
+
+
+ORDER_CASES = [  # n_q, n_kv, d, contexts, chunk
+    # equal contexts: the ranking by work breaks ties by sequence index
+    (8, 2, 64, [40, 40, 100, 17, 100, 40, 17, 17, 250, 40, 100, 17, 33, 33, 250, 40], 9),
+    # more sequences than a workgroup has threads: index order
+    (4, 2, 64, [int(5 + (i * 37) % 60) for i in range(600)], 3),
+    # KV heads not a multiple of the XCD count, pairs dealt over several rounds
+    (12, 3, 128, [300, 20, 150, 150, 700, 64, 65, 500, 21, 300, 90], 20),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ORDER_CASES)))
+def test_work_order_covers_every_row(pkv, orc, case):
+    """The workgroups take the (sequence, KV head) pairs longest context
+    first; every row of every sequence is still written once (the output
+    starts as NaN) and matches the oracle."""
+    n_q, n_kv, d, ctx, C = ORDER_CASES[case]
+    hc = w.host_case(_shape(n_q, n_kv, d), 460 + case, context_lens=ctx)
+    qv = w.normal_bf16(w.rng(460 + case, 15), (len(ctx), C, n_q, d))
+    got, err = _run(pkv, hc, qv)
+    want, rc = orc.verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables, hc.tables.context_lens,
+                          n_kv, hc.shape.scale)
+    assert rc == 0 and err == 0
+    assert np.isfinite(got).all()
+    e = max_abs(got, want)
+    print(f"order case {case}: {len(ctx)} sequences, chunk {C}: max-abs {e:.2e}")
+    assert e <= TOL, e
