@@ -1518,16 +1518,23 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   if (a.num_seqs > 1 && a.num_seqs <= kPfThreads) {
     // rank by work (tiles to read); the K buffer of the second stage holds
     // the keys until the first tile is stored
+    // (padded to a multiple of 4 with INT32_MIN, below every key, and read
+    // four at a time)
     int* key = reinterpret_cast<int*>(&sm.k[1][0][0][0]);
     int* found = key + kPfThreads;
-    if (tid < a.num_seqs) key[tid] = seq_tiles(a.context_lens[tid], a.q_len, a.max_ctx);
+    const int n4 = (a.num_seqs + 3) & ~3;
+    if (tid < n4)
+      key[tid] = tid < a.num_seqs ? seq_tiles(a.context_lens[tid], a.q_len, a.max_ctx) : INT32_MIN;
     __syncthreads();
     if (tid < a.num_seqs) {
       const int mine = key[tid];
       int above = 0;
-      for (int j = 0; j < a.num_seqs; ++j) {
-        const int other = key[j];
-        above += (other > mine || (other == mine && j < tid)) ? 1 : 0;
+      for (int j = 0; j < n4; j += 4) {
+        const int4 o = *reinterpret_cast<const int4*>(key + j);
+        above += (o.x > mine || (o.x == mine && j < tid)) ? 1 : 0;
+        above += (o.y > mine || (o.y == mine && j + 1 < tid)) ? 1 : 0;
+        above += (o.z > mine || (o.z == mine && j + 2 < tid)) ? 1 : 0;
+        above += (o.w > mine || (o.w == mine && j + 3 < tid)) ? 1 : 0;
       }
       if (above == rank) *found = tid;
     }

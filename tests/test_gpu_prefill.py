@@ -170,6 +170,9 @@ ORDER_CASES = [  # n_q, n_kv, d, contexts, chunk
     (4, 2, 64, [int(5 + (i * 37) % 60) for i in range(600)], 3),
     # KV heads not a multiple of the XCD count, pairs dealt over several rounds
     (12, 3, 128, [300, 20, 150, 150, 700, 64, 65, 500, 21, 300, 90], 20),
+    # a count that is not a multiple of 4 (the ranking reads its keys four
+    # at a time), many ties
+    (4, 2, 64, [int(5 + (i * 53) % 40) for i in range(301)], 2),
 ]
 
 
