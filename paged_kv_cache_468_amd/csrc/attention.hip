@@ -1698,108 +1698,114 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   load_tile(0);
   store_tile(0, 0);
   __syncthreads();
+  // A wave whose 32 rows all lie past the chunk's (a short chunk leaves
+  // most of the workgroup's rows empty) only stages tiles and keeps the
+  // barriers; it computes nothing.
+  const bool computes = qg * 32 < a.qrows;
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    // Raw scores (q.k, the scale not yet applied) of all the tile's
-    // blocks, both row groups, with no branch between them. Blocks past
-    // those loaded hold zeros and lie past every valid row's limit;
-    // positions past a row's limit or the context are masked (-inf) only
-    // in the tiles that reach one of the workgroup's limits.
-    const bool edge = (t + 1) * kPfTile > first_masked;
-    float x[NG][kPfSub][4];
+    if (computes) {
+      // Raw scores (q.k, the scale not yet applied) of all the tile's
+      // blocks, both row groups, with no branch between them. Blocks past
+      // those loaded hold zeros and lie past every valid row's limit;
+      // positions past a row's limit or the context are masked (-inf) only
+      // in the tiles that reach one of the workgroup's limits.
+      const bool edge = (t + 1) * kPfTile > first_masked;
+      float x[NG][kPfSub][4];
 #pragma unroll
-    for (int sb = 0; sb < kPfSub; ++sb) {
-      bf16x8_t kr[KM];
-#pragma unroll
-      for (int m = 0; m < KM; ++m)
-        kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * KM + m][lane][0];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < kPfSub; ++sb) {
+        bf16x8_t kr[KM];
 #pragma unroll
         for (int m = 0; m < KM; ++m)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e];
-      }
-    }
-    if (edge) {
-#pragma unroll
-      for (int sb = 0; sb < kPfSub; ++sb) {
-        const int p0 = (t * kPfSub + sb) * 16 + 4 * r;        // this lane's first position
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (p0 + e >= ctx || p0 + e > rw.lim[g]) x[g][sb][e] = -__builtin_inff();
-      }
-    }
-    // running max per row (scaled, base 2), one decision per tile;
-    // P = 2^(x * scale - m) split into bf16 hi + lo (hi rounded to nearest,
-    // lo = P - hi rounded again: ~16 bits of P). The maximum is NaN-
-    // propagating (a NaN score makes the row NaN, as the oracle's would);
-    // across a row's four lane groups it is taken with the row swaps of
-    // gfx950 (lanes 16, then 32 apart), not through the LDS.
-    u32x4_t p_hi[NG][kPfSub / 2], p_lo[NG][kPfSub / 2];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float raw = x[g][0][0];
-#pragma unroll
-      for (int sb = 0; sb < kPfSub; ++sb)
-#pragma unroll
-        for (int e = (sb == 0 ? 1 : 0); e < 4; ++e) raw = __builtin_elementwise_maximum(raw, x[g][sb][e]);
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
-      raw = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
-      raw = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-      const float mx = raw == -__builtin_inff() ? raw : raw * sl;
-      if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run[g], mx);
-        float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-        if (m_new == -__builtin_inff()) alpha = 1.f;
-        m_run[g] = m_new;
-        l_run[g] *= alpha;
-#pragma unroll
-        for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
-      }
-      const float neg_m = m_run[g] == -__builtin_inff() ? 0.f : -m_run[g];
-#pragma unroll
-      for (int sb = 0; sb < kPfSub; ++sb) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][0], sl, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][1], sl, neg_m));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][2], sl, neg_m));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][3], sl, neg_m));
-        l_run[g] += (p0 + p1) + (p2 + p3);
-        const bf16x2_t h01 = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
-        const bf16x2_t h23 = __builtin_convertvector((f32x2_t){p2, p3}, bf16x2_t);
-        const bf16x2_t l01 = __builtin_convertvector(
-            (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h01, neg_lo, p0, false),
-                      __builtin_amdgcn_fdot2_f32_bf16(h01, neg_hi, p1, false)}, bf16x2_t);
-        const bf16x2_t l23 = __builtin_convertvector(
-            (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h23, neg_lo, p2, false),
-                      __builtin_amdgcn_fdot2_f32_bf16(h23, neg_hi, p3, false)}, bf16x2_t);
-        const int half = 2 * (sb & 1);
-        p_hi[g][sb / 2][half] = __builtin_bit_cast(uint32_t, h01);
-        p_hi[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, h23);
-        p_lo[g][sb / 2][half] = __builtin_bit_cast(uint32_t, l01);
-        p_lo[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, l23);
-      }
-    }
-    // P.V per pair of blocks: one LDS read gives a lane's V operand for
-    // both blocks (the V slots past the context were zeroed when stored),
-    // used by the hi and the lo MFMA of both row groups
-#pragma unroll
-    for (int bp = 0; bp < kPfSub / 2; ++bp) {
-#pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        const bf16x8_t vv = *(const bf16x8_t*)&sm.v[buf][bp * VM + m][lane][0];
+          kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * KM + m][lane][0];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_hi[g][bp]),
-                                                              acc[g][m], 0, 0, 0);
-          acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_lo[g][bp]),
-                                                              acc[g][m], 0, 0, 0);
+          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < KM; ++m)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e];
+        }
+      }
+      if (edge) {
+#pragma unroll
+        for (int sb = 0; sb < kPfSub; ++sb) {
+          const int p0 = (t * kPfSub + sb) * 16 + 4 * r;        // this lane's first position
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (p0 + e >= ctx || p0 + e > rw.lim[g]) x[g][sb][e] = -__builtin_inff();
+        }
+      }
+      // running max per row (scaled, base 2), one decision per tile;
+      // P = 2^(x * scale - m) split into bf16 hi + lo (hi rounded to nearest,
+      // lo = P - hi rounded again: ~16 bits of P). The maximum is NaN-
+      // propagating (a NaN score makes the row NaN, as the oracle's would);
+      // across a row's four lane groups it is taken with the row swaps of
+      // gfx950 (lanes 16, then 32 apart), not through the LDS.
+      u32x4_t p_hi[NG][kPfSub / 2], p_lo[NG][kPfSub / 2];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float raw = x[g][0][0];
+#pragma unroll
+        for (int sb = 0; sb < kPfSub; ++sb)
+#pragma unroll
+          for (int e = (sb == 0 ? 1 : 0); e < 4; ++e) raw = __builtin_elementwise_maximum(raw, x[g][sb][e]);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
+        raw = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
+        raw = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+        const float mx = raw == -__builtin_inff() ? raw : raw * sl;
+        if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_run[g], mx);
+          float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+          if (m_new == -__builtin_inff()) alpha = 1.f;
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
+        }
+        const float neg_m = m_run[g] == -__builtin_inff() ? 0.f : -m_run[g];
+#pragma unroll
+        for (int sb = 0; sb < kPfSub; ++sb) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][0], sl, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][1], sl, neg_m));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][2], sl, neg_m));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][3], sl, neg_m));
+          l_run[g] += (p0 + p1) + (p2 + p3);
+          const bf16x2_t h01 = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+          const bf16x2_t h23 = __builtin_convertvector((f32x2_t){p2, p3}, bf16x2_t);
+          const bf16x2_t l01 = __builtin_convertvector(
+              (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h01, neg_lo, p0, false),
+                        __builtin_amdgcn_fdot2_f32_bf16(h01, neg_hi, p1, false)}, bf16x2_t);
+          const bf16x2_t l23 = __builtin_convertvector(
+              (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h23, neg_lo, p2, false),
+                        __builtin_amdgcn_fdot2_f32_bf16(h23, neg_hi, p3, false)}, bf16x2_t);
+          const int half = 2 * (sb & 1);
+          p_hi[g][sb / 2][half] = __builtin_bit_cast(uint32_t, h01);
+          p_hi[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, h23);
+          p_lo[g][sb / 2][half] = __builtin_bit_cast(uint32_t, l01);
+          p_lo[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, l23);
+        }
+      }
+      // P.V per pair of blocks: one LDS read gives a lane's V operand for
+      // both blocks (the V slots past the context were zeroed when stored),
+      // used by the hi and the lo MFMA of both row groups
+#pragma unroll
+      for (int bp = 0; bp < kPfSub / 2; ++bp) {
+#pragma unroll
+        for (int m = 0; m < VM; ++m) {
+          const bf16x8_t vv = *(const bf16x8_t*)&sm.v[buf][bp * VM + m][lane][0];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_hi[g][bp]),
+                                                                acc[g][m], 0, 0, 0);
+            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_lo[g][bp]),
+                                                                acc[g][m], 0, 0, 0);
+          }
         }
       }
     }
