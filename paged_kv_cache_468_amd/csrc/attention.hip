@@ -1441,62 +1441,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PREFIX && D
 // Chunked prefill with the K/V tiles staged in LDS. A workgroup of
 // kPfWaves waves takes 32 * kPfWaves query rows of one (sequence, KV head)
 // (rows ordered (chunk token, head within the group), as everywhere); each
-// wave serves 32 of them as two 16-row MFMA groups. The workgroup walks the
-// cached context in tiles of kPfTile tokens (kPfTile / 16 blocks): all its
-// threads load the next tile's K and V from the pool into registers while
-// the waves compute the current tile from LDS, then store them into the
-// other LDS buffer. LDS holds the tiles in MFMA operand order: for each
-// (block, MFMA step) the 64 lanes' operands one after another, so every
-// wave's LDS read is lane-linear and free of bank conflicts, and the
-// threads that stage a slot write consecutive addresses too (the pool
-// reads that feed them: whole 64-byte runs of a K row, whole 512-byte runs
-// of a V block). The V slots of the sequence's last block past the context
-// are zeroed there, once per workgroup. Per tile and wave: for each
-// 16-token block, scores (K as A, q as B, as in the decode) for both row
-// groups; one running-max decision per tile; P split into bf16 hi + lo.
-// Unlike the decode, a P.V MFMA's 32-long inner dimension spans two blocks
-// (4 tokens of each per lane) with the hi parts, and a second MFMA on the
-// same V operand takes the lo parts: the V operand is 8 distinct values
-// read straight from LDS, with no copy to repeat it for hi and lo.
-// Causal: rows see positions up to ctx - q_len + their token; tiles past
-// the workgroup's last row are not loaded, and the masking runs only in
-// the tiles that reach its first row's limit.
+// wave serves 32 of them with 32x32x16 MFMAs (lane i: row i % 32; the two
+// halves of the wave split every MFMA's inner dimension and every output
+// column). The workgroup walks the cached context in tiles of kPfTile
+// tokens (kPfTile / 16 blocks): all its threads load the next tile's K and
+// V from the pool into registers while the waves compute the current tile
+// from LDS, then store them into the other LDS buffer. LDS holds the tiles
+// in MFMA operand order: for each (32-token group, 16-dim step) of K and
+// each (block, 32-dim group) of V the 64 lanes' operands one after
+// another, so every wave's LDS read is lane-linear and free of bank
+// conflicts. The V slots of the sequence's last block past the context are
+// zeroed there, once per workgroup. Per tile and wave: for each 32-token
+// group, scores (K as A, q as B) accumulated over the head dimension; one
+// running-max decision per tile (each row's 32 scores of a group sit in
+// two lanes, 16 each); P split into bf16 hi + lo. A P.V MFMA's 16-long
+// inner dimension is 8 tokens of one block per half-wave (4 and 4, 8
+// apart) with the hi parts, and a second MFMA on the same V operand takes
+// the lo parts: the V operand is 8 distinct values read straight from LDS.
+// The 32x32x16 shape keeps the matrix pipe fed with few independent
+// accumulators, where the 16x16x32 one needs many. Causal: rows see
+// positions up to ctx - q_len + their token; tiles past the workgroup's
+// last row are not loaded, and the masking runs only in the tiles that
+// reach its first row's limit.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kPfWaves = 8;                      // waves per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 32 * kPfWaves;           // query rows per workgroup
 constexpr int kPfTile = 64;                      // tokens per LDS tile
 constexpr int kPfSub = kPfTile / 16;             // blocks per tile
-static_assert(kPfSub % 2 == 0, "P.V MFMAs take the tile's blocks in pairs");
+constexpr int kPfGroups = kPfTile / 32;          // 32-token score groups per tile
 
 template <int D>
 struct PfSmem {
-  // MFMA operand order: K slot (block, step) holds, for lane i, the 16
-  // bytes of K that lane i feeds to that score MFMA, at i * 16; V slot
-  // (pair of blocks, step) the 16 bytes of V it feeds to that P.V MFMA
-  // (4 tokens of one dimension from each of the two blocks)
-  uint16_t k[2][kPfSub * (D / 32)][64][8];
-  uint16_t v[2][kPfSub / 2 * (D / 16)][64][8];
+  // K slot (group, step): lane i's 16 bytes of the score MFMA's A operand,
+  // token 32 * group + i % 32 of the tile, dims 16 * step + 8 * (i / 32) ..
+  // + 7. V slot (block, dim group): lane i's 16 bytes of the P.V MFMA's A
+  // operand, dim 32 * group + i % 32, tokens 4 * (i / 32) .. + 3 and then
+  // 8 + 4 * (i / 32) .. + 3 of the block.
+  uint16_t k[2][kPfGroups * (D / 16)][64][8];
+  uint16_t v[2][kPfSub * (D / 32)][64][8];
 };
 
 template <int D>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_prefill_lds_kernel(DecodeArgs a) {
-  constexpr int NG = 2;
-  constexpr int KM = D / 32;
-  constexpr int VM = D / 16;
-  constexpr int K_CHUNKS = kPfSub * KM * 64;     // 16-byte operand slots per tile
-  constexpr int V_CHUNKS = kPfSub / 2 * VM * 64; // 16-byte operand slots per tile
-  constexpr int K_PER = K_CHUNKS / kPfThreads;
-  constexpr int V_PER = V_CHUNKS / kPfThreads;
-  static_assert(K_PER * kPfThreads == K_CHUNKS && V_PER * kPfThreads == V_CHUNKS, "tile split");
+  constexpr int KS = D / 16;                      // score MFMA steps
+  constexpr int DG = D / 32;                      // P.V dim groups
+  constexpr int K_SLOTS = kPfGroups * KS;
+  constexpr int V_SLOTS = kPfSub * DG;
+  constexpr int K_PER = K_SLOTS * 64 / kPfThreads;
+  constexpr int V_PER = V_SLOTS * 64 / kPfThreads;
+  static_assert(K_PER * kPfThreads == K_SLOTS * 64 && V_PER * kPfThreads == V_SLOTS * 64, "tile split");
   __shared__ PfSmem<D> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int r = lane >> 4;
+  const int hf = lane >> 5;                       // half of the wave
   const int n_rt = (a.qrows + kPfRows - 1) / kPfRows;   // row tiles per (sequence, KV head)
   // Workgroup -> (sequence, KV head, row tile). The row tiles of one
   // (sequence, KV head) pair read the same K/V tiles, so they run on one XCD
@@ -1543,17 +1546,33 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   }
   const int ctx = a.context_lens[s];
   const int qg = rt * kPfWaves + wave;              // this wave's 32-row group
-  const Rows<NG> rw = rows_of<NG, true>(a, lane, s, h, qg, ctx);
+  // this lane's query row
+  const int gr = qg * 32 + (lane & 31);
+  const bool row_valid = gr < a.qrows;
+  const int tok = row_valid ? gr / a.group : 0;
+  const int64_t row_index =
+      row_valid ? ((int64_t)s * a.q_len + tok) * a.n_q + h * a.group + (gr - tok * a.group) : 0;
+  const int lim = row_valid ? ctx - a.q_len + tok : 0x7fffffff;
+  // this lane's share of its row's output: dims 32 dg + 8 g + 4 hf .. + 3
+  auto write_row = [&](const f32x16_t (&v)[DG], float mul) __attribute__((always_inline)) {
+    float* o = a.out + row_index * D + 4 * hf;
+#pragma unroll
+    for (int dg = 0; dg < DG; ++dg)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4_t*)(o + 32 * dg + 8 * g) =
+            f32x4_t{v[dg][4 * g], v[dg][4 * g + 1], v[dg][4 * g + 2], v[dg][4 * g + 3]} * mul;
+  };
 
   if (seq_tiles(ctx, a.q_len, a.max_ctx) == 0) {
     if (h == 0 && rt == 0 && tid == 0) flag_error(a.err_flag, PKV_DEVERR_CONTEXT);
-    const float nan = __builtin_nanf("");
+    if (row_valid) {
+      f32x16_t z[DG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (!rw.valid[g]) continue;
-      float* o = a.out + rw.index[g] * D + 4 * r;
+      for (int dg = 0; dg < DG; ++dg)
 #pragma unroll
-      for (int m = 0; m < VM; ++m) *(f32x4_t*)(o + 16 * m) = f32x4_t{nan, nan, nan, nan};
+        for (int e = 0; e < 16; ++e) z[dg][e] = 1.f;
+      write_row(z, __builtin_nanf(""));
     }
     return;
   }
@@ -1573,24 +1592,24 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   // first row's limit + 1; every later row sees more)
   const int first_masked = ctx - a.q_len + 1 + (rt * kPfRows) / a.group;
 
-  // this wave's q rows, as the B operand of the score MFMA. The scale is
-  // applied inside the exponent (one fused multiply-add per score), which
-  // needs a positive factor: for a negative scale the rows are negated
-  // (exact in bf16; the products and their sum change sign only), and for
-  // a zero scale they are zeroed, which gives every visible score 0.
+  // this lane's q row, as the B operand of the score MFMA (dims
+  // 16 step + 8 hf .. + 7). The scale is applied inside the exponent (one
+  // fused multiply-add per score), which needs a positive factor: for a
+  // negative scale the rows are negated (exact in bf16; the products and
+  // their sum change sign only), and for a zero scale they are zeroed,
+  // which gives every visible score 0.
   const float sl = a.scale_log2 == 0.f ? 1.f : fabsf(a.scale_log2);
   const uint32_t q_xor = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const bool q_zero = a.scale_log2 == 0.f;
-  bf16x8_t qv[NG][KM];
+  const bool q_keep = row_valid && a.scale_log2 != 0.f;
+  bf16x8_t qv[KS];
+  {
+    const uint16_t* q_row = a.q + row_index * D + 8 * hf;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const uint16_t* q_row = a.q + (rw.valid[g] ? rw.index[g] : 0) * D;
+    for (int st = 0; st < KS; ++st) {
+      u32x4_t v = *(const u32x4_t*)(q_row + 16 * st);
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      u32x4_t v = *(const u32x4_t*)(q_row + 32 * m + 8 * r);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (rw.valid[g] && !q_zero) ? (v[e] ^ q_xor) : 0u;
-      qv[g][m] = __builtin_bit_cast(bf16x8_t, v);
+      for (int e = 0; e < 4; ++e) v[e] = q_keep ? (v[e] ^ q_xor) : 0u;
+      qv[st] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -1602,7 +1621,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   bool bad = false;
   u32x4_t kst[K_PER];
   u32x2_t vst[V_PER][2];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
     int ids[kPfSub];
 #pragma unroll
     for (int j = 0; j < kPfSub; ++j) {
@@ -1617,74 +1636,74 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
-      // slot (sb, m, lane'): token sb*16 + c, dims 32m + 8r .. +7
+      // slot (group, step), lane': token 32 group + c (c = lane' % 32: block
+      // 2 group + c / 16, row c % 16), dims 16 step + 8 (lane' / 32) .. + 7
       const int ch = tid + i * kPfThreads;
-      const int sb = ch / (KM * 64);
-      const int m = (ch / 64) % KM;
+      const int slot = ch / 64;
       const int ln = ch % 64;
+      const int grp = slot / KS;
+      const int st = slot % KS;
+      const int jb = 2 * grp + ((ln >> 4) & 1);
       int blk = ids[0];
 #pragma unroll
-      for (int j = 1; j < kPfSub; ++j) blk = sb == j ? ids[j] : blk;
-      kst[i] = *(const u32x4_t*)(a.k_pool + blk * block_stride + head_off + (ln & 15) * D +
-                                 32 * m + 8 * (ln >> 4));
+      for (int j = 1; j < kPfSub; ++j) blk = jb == j ? ids[j] : blk;
+      kst[i] = *(const u32x4_t*)(a.k_pool + blk * block_stride + head_off + (ln & 15) * D + 16 * st +
+                                 8 * (ln >> 5));
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
-      // slot (bp, m, lane'): dim 16m + c, tokens 4r .. 4r+3 of blocks 2bp
-      // and 2bp + 1
+      // slot (block, dim group), lane': dim 32 group + lane' % 32, tokens
+      // 4 (lane' / 32) .. + 3 and 8 + 4 (lane' / 32) .. + 3
       const int ch = tid + i * kPfThreads;
-      const int bp = ch / (VM * 64);
-      const int m = (ch / 64) % VM;
+      const int slot = ch / 64;
       const int ln = ch % 64;
-      int b0 = ids[0], b1 = ids[1];
+      const int jb = slot / DG;
+      const int dg = slot % DG;
+      int blk = ids[0];
 #pragma unroll
-      for (int j = 1; j < kPfSub / 2; ++j) {
-        b0 = bp == j ? ids[2 * j] : b0;
-        b1 = bp == j ? ids[2 * j + 1] : b1;
-      }
-      const int64_t in_blk = head_off + (16 * m + (ln & 15)) * 16 + 4 * (ln >> 4);
-      vst[i][0] = *(const u32x2_t*)(a.v_pool + b0 * block_stride + in_blk);
-      vst[i][1] = *(const u32x2_t*)(a.v_pool + b1 * block_stride + in_blk);
+      for (int j = 1; j < kPfSub; ++j) blk = jb == j ? ids[j] : blk;
+      const uint16_t* row = a.v_pool + blk * block_stride + head_off + (32 * dg + (ln & 31)) * 16 + 4 * (ln >> 5);
+      vst[i][0] = *(const u32x2_t*)row;
+      vst[i][1] = *(const u32x2_t*)(row + 8);
     }
   };
   // registers -> LDS for tile t (the zeroing of blocks past n_blocks is
   // done here, after the tile's compute, so the loads stay in flight)
-  auto store_tile = [&](int buf, int t) {
+  auto store_tile = [&](int buf, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const bool in = t * kPfSub + ch / (KM * 64) < n_blocks;
-      *(u32x4_t*)&sm.k[buf][ch / 64][ch % 64][0] = in ? kst[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const int slot = ch / 64;
+      const int ln = ch % 64;
+      const bool in = t * kPfSub + 2 * (slot / KS) + ((ln >> 4) & 1) < n_blocks;
+      *(u32x4_t*)&sm.k[buf][slot][ln][0] = in ? kst[i] : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int ch = tid + i * kPfThreads;
-      const int bp = ch / (VM * 64);
+      const int slot = ch / 64;
       const int ln = ch % 64;
-      const int first = 4 * (ln >> 4);
+      const int b = t * kPfSub + slot / DG;
       u32x2_t val[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int b = t * kPfSub + 2 * bp + half;
         val[half] = b < n_blocks ? vst[i][half] : u32x2_t{0u, 0u};
         if (b == last_block && last_valid < 16) {   // slots past the context: zero (0 * NaN)
+          const int first = 8 * half + 4 * (ln >> 5);
           val[half][0] &= (first < last_valid ? 0xFFFFu : 0u) | (first + 1 < last_valid ? 0xFFFF0000u : 0u);
           val[half][1] &= (first + 2 < last_valid ? 0xFFFFu : 0u) | (first + 3 < last_valid ? 0xFFFF0000u : 0u);
         }
       }
-      *(u32x4_t*)&sm.v[buf][ch / 64][ln][0] = u32x4_t{val[0][0], val[0][1], val[1][0], val[1][1]};
+      *(u32x4_t*)&sm.v[buf][slot][ln][0] = u32x4_t{val[0][0], val[0][1], val[1][0], val[1][1]};
     }
   };
 
-  f32x4_t acc[NG][VM];
-  float m_run[NG], l_run[NG];
+  f32x16_t acc[DG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
+  for (int dg = 0; dg < DG; ++dg)
 #pragma unroll
-    for (int m = 0; m < VM; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run[g] = -__builtin_inff();
-    l_run[g] = 0.f;
-  }
+    for (int e = 0; e < 16; ++e) acc[dg][e] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;   // l_run: this half-wave's tokens
 
   // -1 in the low (high) bf16 of a pair: a packed dot product with it
   // subtracts that half, widened exactly, from a float. The empty asm
@@ -1695,6 +1714,7 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   asm volatile("" : "+v"(neg_hi_bits));
   const bf16x2_t neg_lo = __builtin_bit_cast(bf16x2_t, neg_lo_bits);
   const bf16x2_t neg_hi = __builtin_bit_cast(bf16x2_t, neg_hi_bits);
+
   load_tile(0);
   store_tile(0, 0);
   __syncthreads();
@@ -1706,76 +1726,73 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
     if (computes) {
-      // Raw scores (q.k, the scale not yet applied) of all the tile's
-      // blocks, both row groups, with no branch between them. Blocks past
-      // those loaded hold zeros and lie past every valid row's limit;
+      // Raw scores (q.k, the scale not yet applied) of the tile's 32-token
+      // groups: lane i, register 4 g + e holds token 32 group + 8 g + 4 hf
+      // + e of row i % 32. The two groups' chains are interleaved. Blocks
+      // past those loaded hold zeros and lie past every valid row's limit;
       // positions past a row's limit or the context are masked (-inf) only
       // in the tiles that reach one of the workgroup's limits.
-      const bool edge = (t + 1) * kPfTile > first_masked;
-      float x[NG][kPfSub][4];
+      f32x16_t x[kPfGroups];
 #pragma unroll
-      for (int sb = 0; sb < kPfSub; ++sb) {
-        bf16x8_t kr[KM];
+      for (int grp = 0; grp < kPfGroups; ++grp)
 #pragma unroll
-        for (int m = 0; m < KM; ++m)
-          kr[m] = *(const bf16x8_t*)&sm.k[buf][sb * KM + m][lane][0];
+        for (int e = 0; e < 16; ++e) x[grp][e] = 0.f;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < KS; ++st)
 #pragma unroll
-          for (int m = 0; m < KM; ++m)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m], qv[g][m], sc, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[g][sb][e] = sc[e];
+        for (int grp = 0; grp < kPfGroups; ++grp) {
+          const bf16x8_t kr = *(const bf16x8_t*)&sm.k[buf][grp * KS + st][lane][0];
+          x[grp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qv[st], x[grp], 0, 0, 0);
         }
-      }
-      if (edge) {
+      if ((t + 1) * kPfTile > first_masked) {
 #pragma unroll
-        for (int sb = 0; sb < kPfSub; ++sb) {
-          const int p0 = (t * kPfSub + sb) * 16 + 4 * r;        // this lane's first position
+        for (int grp = 0; grp < kPfGroups; ++grp)
 #pragma unroll
-          for (int g = 0; g < NG; ++g)
+          for (int g = 0; g < 4; ++g) {
+            const int p0 = t * kPfTile + 32 * grp + 8 * g + 4 * hf;   // this lane's first position
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (p0 + e >= ctx || p0 + e > rw.lim[g]) x[g][sb][e] = -__builtin_inff();
-        }
+              if (p0 + e >= ctx || p0 + e > lim) x[grp][4 * g + e] = -__builtin_inff();
+          }
       }
-      // running max per row (scaled, base 2), one decision per tile;
-      // P = 2^(x * scale - m) split into bf16 hi + lo (hi rounded to nearest,
+      // running max per row (scaled, base 2), one decision per tile; P =
+      // 2^(x * scale - m) split into bf16 hi + lo (hi rounded to nearest,
       // lo = P - hi rounded again: ~16 bits of P). The maximum is NaN-
-      // propagating (a NaN score makes the row NaN, as the oracle's would);
-      // across a row's four lane groups it is taken with the row swaps of
-      // gfx950 (lanes 16, then 32 apart), not through the LDS.
-      u32x4_t p_hi[NG][kPfSub / 2], p_lo[NG][kPfSub / 2];
+      // propagating (a NaN score makes the row NaN, as the oracle's
+      // would); the row's other half is in the lane 32 away, swapped in
+      // with the gfx950 row swap.
+      float raw = x[0][0];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        float raw = x[g][0][0];
+      for (int grp = 0; grp < kPfGroups; ++grp)
 #pragma unroll
-        for (int sb = 0; sb < kPfSub; ++sb)
-#pragma unroll
-          for (int e = (sb == 0 ? 1 : 0); e < 4; ++e) raw = __builtin_elementwise_maximum(raw, x[g][sb][e]);
-        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
-        raw = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+        for (int e = (grp == 0 ? 1 : 0); e < 16; ++e) raw = __builtin_elementwise_maximum(raw, x[grp][e]);
+      {
         const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(raw), __float_as_uint(raw), false, false);
         raw = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-        const float mx = raw == -__builtin_inff() ? raw : raw * sl;
-        if (__ballot(mx > m_run[g] + kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run[g], mx);
-          float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-          if (m_new == -__builtin_inff()) alpha = 1.f;
-          m_run[g] = m_new;
-          l_run[g] *= alpha;
+      }
+      const float mx = raw == -__builtin_inff() ? raw : raw * sl;
+      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (m_new == -__builtin_inff()) alpha = 1.f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-          for (int m = 0; m < VM; ++m) acc[g][m] *= alpha;
-        }
-        const float neg_m = m_run[g] == -__builtin_inff() ? 0.f : -m_run[g];
+        for (int dg = 0; dg < DG; ++dg) acc[dg] *= alpha;
+      }
+      const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+      // P operands, per (group, block): the lane's tokens 4 hf .. + 3 (g =
+      // 2 block) then 8 + 4 hf .. + 3 (g = 2 block + 1) of the block
+      u32x4_t p_hi[kPfGroups][2], p_lo[kPfGroups][2];
 #pragma unroll
-        for (int sb = 0; sb < kPfSub; ++sb) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][0], sl, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][1], sl, neg_m));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][2], sl, neg_m));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[g][sb][3], sl, neg_m));
-          l_run[g] += (p0 + p1) + (p2 + p3);
+      for (int grp = 0; grp < kPfGroups; ++grp)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[grp][4 * g], sl, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[grp][4 * g + 1], sl, neg_m));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[grp][4 * g + 2], sl, neg_m));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[grp][4 * g + 3], sl, neg_m));
+          l_run += (p0 + p1) + (p2 + p3);
           const bf16x2_t h01 = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
           const bf16x2_t h23 = __builtin_convertvector((f32x2_t){p2, p3}, bf16x2_t);
           const bf16x2_t l01 = __builtin_convertvector(
@@ -1784,30 +1801,32 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
           const bf16x2_t l23 = __builtin_convertvector(
               (f32x2_t){__builtin_amdgcn_fdot2_f32_bf16(h23, neg_lo, p2, false),
                         __builtin_amdgcn_fdot2_f32_bf16(h23, neg_hi, p3, false)}, bf16x2_t);
-          const int half = 2 * (sb & 1);
-          p_hi[g][sb / 2][half] = __builtin_bit_cast(uint32_t, h01);
-          p_hi[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, h23);
-          p_lo[g][sb / 2][half] = __builtin_bit_cast(uint32_t, l01);
-          p_lo[g][sb / 2][half + 1] = __builtin_bit_cast(uint32_t, l23);
+          const int half = 2 * (g & 1);
+          p_hi[grp][g / 2][half] = __builtin_bit_cast(uint32_t, h01);
+          p_hi[grp][g / 2][half + 1] = __builtin_bit_cast(uint32_t, h23);
+          p_lo[grp][g / 2][half] = __builtin_bit_cast(uint32_t, l01);
+          p_lo[grp][g / 2][half + 1] = __builtin_bit_cast(uint32_t, l23);
         }
-      }
-      // P.V per pair of blocks: one LDS read gives a lane's V operand for
-      // both blocks (the V slots past the context were zeroed when stored),
-      // used by the hi and the lo MFMA of both row groups
+      // P.V per block: one LDS read per dim group gives the lane's V
+      // operand (the V slots past the context were zeroed when stored),
+      // used by the hi and the lo MFMA; the dim groups' chains interleave
 #pragma unroll
-      for (int bp = 0; bp < kPfSub / 2; ++bp) {
+      for (int grp = 0; grp < kPfGroups; ++grp)
 #pragma unroll
-        for (int m = 0; m < VM; ++m) {
-          const bf16x8_t vv = *(const bf16x8_t*)&sm.v[buf][bp * VM + m][lane][0];
+        for (int bl = 0; bl < 2; ++bl) {
+          bf16x8_t vv[DG];
 #pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_hi[g][bp]),
-                                                                acc[g][m], 0, 0, 0);
-            acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, p_lo[g][bp]),
-                                                                acc[g][m], 0, 0, 0);
-          }
+          for (int dg = 0; dg < DG; ++dg)
+            vv[dg] = *(const bf16x8_t*)&sm.v[buf][(2 * grp + bl) * DG + dg][lane][0];
+#pragma unroll
+          for (int dg = 0; dg < DG; ++dg)
+            acc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dg], __builtin_bit_cast(bf16x8_t, p_hi[grp][bl]),
+                                                              acc[dg], 0, 0, 0);
+#pragma unroll
+          for (int dg = 0; dg < DG; ++dg)
+            acc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dg], __builtin_bit_cast(bf16x8_t, p_lo[grp][bl]),
+                                                              acc[dg], 0, 0, 0);
         }
-      }
     }
     if (t + 1 < n_tiles) {
       // the other buffer was last read in the previous tile, before the
@@ -1816,7 +1835,16 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
       __syncthreads();
     }
   }
-  finish_rows<D, NG>(a, lane, !bad, true, 0, rw, acc, m_run, l_run);
+  // out = acc / l, l summed over the row's two halves; a bad block id
+  // makes the rows NaN and sets the error bit
+  const bool ok = !bad;
+  if (!ok && lane == 0) flag_error(a.err_flag, PKV_DEVERR_BLOCK_ID);
+  float l_tot;
+  {
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_tot = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  }
+  if (row_valid) write_row(acc, ok ? 1.0f / l_tot : __builtin_nanf(""));
 }
 
 // Merge kernel: one wave per (unit, query row). With reference maxima m_p,
