@@ -6,7 +6,8 @@ values and new context lengths are copied into the device buffers the graph
 reads, and the stream is synchronised. After every replay the graph's output
 must equal, bit for bit, an eager decode of the same state, and the pools
 must hold the appended tokens. Nothing in the graph clears memory, and
-nothing is allocated during capture.
+nothing is allocated during capture. The same for chunked prefill, whose
+work order follows the context lengths the graph reads at each replay.
 """
 import numpy as np
 import pytest
@@ -80,3 +81,43 @@ def test_graph_replays_match_eager(pkv, part):
         p = int(ctx[0]) - 1
         blk = hc.tables.block_tables[0, p // 16]
         assert np.array_equal(k_host[blk, :, p % 16, :], to_host_u16(dc.k_new)[0])
+
+
+def test_prefill_graph_replays_match_eager(pkv):
+    """pkv_paged_prefill captured once and replayed with new queries and new
+    context lengths between replays: the workgroups rank the sequences by
+    context length on the device, so a replay must follow the new lengths;
+    every replay equals an eager launch of the same state bit for bit."""
+    import torch
+    sh = _shape(32, 8, 128)
+    C = 64
+    ctx0 = np.array([900, 300, 1500, 64, 700], np.int32)
+    hc = w.host_case(sh, 73, context_lens=ctx0, max_blocks=100)
+    kp, vp = to_dev_bf16(hc.k_pool), to_dev_bf16(hc.v_pool)
+    bt, cl = to_dev_i32(hc.tables.block_tables), to_dev_i32(ctx0)
+    q = torch.empty((len(ctx0), C, sh.n_q, sh.d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    out_ref = torch.empty_like(out)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    max_ctx = int(ctx0.max())
+    rng = w.rng(74, 0)
+    q.copy_(to_dev_bf16(w.normal_bf16(rng, tuple(q.shape))))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.pkv_paged_prefill(out, q, kp, vp, bt, cl, sh.scale, max_ctx, err_flag=err)
+    for rep in range(4):
+        # shorter contexts (never below the chunk) reorder the sequences' ranks
+        ctx = np.maximum(ctx0 - rng.integers(0, 700, size=len(ctx0)).astype(np.int32), C)
+        cl.copy_(to_dev_i32(ctx))
+        q.copy_(to_dev_bf16(w.normal_bf16(rng, tuple(q.shape))))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        pkv.pkv_paged_prefill(out_ref, q, kp, vp, bt, cl, sh.scale, max_ctx, err_flag=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert np.isfinite(got).all(), f"replay {rep}"
+        assert np.array_equal(got, out_ref.cpu().numpy()), f"replay {rep} differs from eager"
