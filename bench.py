@@ -758,7 +758,7 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True, prefix_kernel=
                             if use_prefix else "pkv_paged_attn_verify")}
 
 
-def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=True):
+def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=True, cpu_seconds=0.0):
     """Chunked prefill at a model shape: batch sequences each take a chunk
     of `chunk` prompt tokens on top of 1,024..6,144 tokens already cached
     (uniform), all layers. Per layer: pkv_kv_write of the chunk's keys and
@@ -840,6 +840,8 @@ def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=Tr
     traffic, why = (stored_traffic(f"llama3-8b-prefill{chunk}x{batch}", "paged_prefill",
                                    kernel_file="paged_prefill")
                     if shape.name == w.CONFIGS[4].name and seed == 0 else (None, "other workload"))
+    cpu = prefill_cpu_baseline(torch, kp[L - 1], vp[L - 1], q[L - 1], out[L - 1], t.block_tables, ctx,
+                               chunk, n_kv, shape.scale, seed, cpu_seconds) if cpu_seconds > 0 else None
     return {
         "metric": "chunked prefill against the paged cache: TFLOP/s of the attention",
         "value": flops_layer * L / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
@@ -855,7 +857,45 @@ def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=Tr
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                      "traffic_gbs": measured_gbs(traffic, prefill_us),
                      "traffic_note": why, "alg_flops_per_launch": flops_layer},
+        "cpu_baseline": cpu,
     }
+
+
+def prefill_cpu_baseline(torch, kp, vp, q, out, tables, ctx, chunk, n_kv, scale, seed, budget_s):
+    """The oracle beside the prefill, on a bounded sample of the last
+    layer's final state: rows (sequence, chunk token, query head) drawn at
+    random, the first and last chunk token of every sequence first, each
+    recomputed by the single-threaded C oracle in float64 (the row's
+    attention over positions 0 .. ctx - chunk + token) until budget_s
+    seconds; its rate in the prefill's own flop count, and the largest
+    difference from the GPU's rows."""
+    import oracle
+    orc = oracle.default()
+    k_h = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    v_h = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    q_h = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    got = out.cpu().numpy()
+    B, C, n_q, d = q_h.shape
+    G = n_q // n_kv
+    rnd = np.random.default_rng(seed + 77)
+    picks = [(s, 0, 0) for s in range(B)] + [(s, C - 1, n_q - 1) for s in range(B)]
+    rows, flops, err, spent = 0, 0.0, 0.0, 0.0
+    while spent < budget_s:
+        s, i, j = picks[rows] if rows < len(picks) else \
+            (int(rnd.integers(B)), int(rnd.integers(C)), int(rnd.integers(n_q)))
+        seen = int(ctx[s]) - chunk + i + 1
+        t0 = time.perf_counter()
+        want, rc = orc.decode_row(q_h[s, i, j], k_h, v_h, tables[s], seen, n_kv, j // G, scale)
+        spent += time.perf_counter() - t0
+        if rc != 0:
+            raise RuntimeError(f"oracle status {rc}")
+        err = max(err, float(np.abs(got[s, i, j] - want).max()))
+        flops += 4.0 * d * seen
+        rows += 1
+    return {"value": flops / spent / 1e9, "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} (sequence, chunk token, query head) rows of the last layer, "
+                      f"{spent:.1f} s of single-threaded C oracle time in float64",
+            "parity_max_abs": err, "parity_rows": rows}
 
 
 def prefix_cache_bench(pkv, seed, n_req=2000):
@@ -1129,7 +1169,14 @@ def main():
     if args.prefill_chunk > 0:
         log(f"[bench] chunked prefill, {args.prefill_chunk}-token chunks x {args.prefill_batch}")
         line = prefill_bench(pkv, torch, shape, args.seed, args.prefill_chunk, args.prefill_batch,
-                             args.steps, args.warmup, graph=not args.no_graph)
+                             args.steps, args.warmup, graph=not args.no_graph,
+                             cpu_seconds=min(args.cpu_seconds, 10.0))
+        if line["cpu_baseline"] is not None:
+            cb = line["cpu_baseline"]
+            log(f"[bench] oracle {cb['value']:.2f} GFLOP/s on 1 thread, parity max-abs "
+                f"{cb['parity_max_abs']:.2e} over {cb['parity_rows']} rows")
+            if not cb["parity_max_abs"] <= 1e-3:
+                raise RuntimeError(f"prefill parity {cb['parity_max_abs']:.3e} > 1e-3")
         copy_calibration(torch, args.copy_calibration_mib)
         print(json.dumps(line), flush=True)
         return

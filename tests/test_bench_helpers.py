@@ -2,8 +2,8 @@
 keys the stored counter records ignores comments and whitespace but not
 code, a record is used only while that hash matches, the counted-bytes
 rate is bytes over duration, the batch order puts the shared prefix's
-members first, and the shared-prefix call's byte count takes the prefix
-once."""
+members first, the shared-prefix call's byte count takes the prefix
+once, and the prefill bench's oracle leg finds a planted row error."""
 import json
 import os
 import sys
@@ -13,6 +13,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
+import numpy as np  # noqa: E402
+import workload as w  # noqa: E402
 
 
 def test_source_hash_ignores_comments_not_code(tmp_path):
@@ -117,3 +119,31 @@ def test_cpu_baseline_reports_both_oracles():
     twin = single["fp32_twin"]
     assert twin["value"] > 0 and twin["cores"] == 1
     assert 0 < twin["max_abs_vs_float64_oracle"] < 1e-5
+
+
+def test_prefill_cpu_baseline_checks_rows_against_the_oracle():
+    """The prefill bench's oracle leg recomputes sampled rows one by one:
+    against the verification oracle's own rows it finds no difference
+    beyond fp32 rounding, and it reports its rate, core count and sample."""
+    import torch
+    import oracle
+    sh = w.Shape("x", 1, 8, 2, 64, 1, 1, 1)
+    ctx = np.array([40, 90], np.int32)
+    C = 8
+    hc = w.host_case(sh, 5, context_lens=ctx)
+    qv = w.normal_bf16(w.rng(5, 15), (2, C, 8, 64))
+    want, rc = oracle.default().verify(qv, hc.k_pool, hc.v_pool, hc.tables.block_tables, ctx, 2,
+                                       sh.scale)
+    assert rc == 0
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    res = bench.prefill_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv),
+                                     torch.from_numpy(want.astype(np.float32)),
+                                     hc.tables.block_tables, ctx, C, 2, sh.scale, 0, 0.05)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
+    assert res["parity_rows"] >= 4 and res["parity_max_abs"] <= 1e-6
+    # a planted error in one row is found when that row is sampled
+    bad = want.astype(np.float32).copy()
+    bad[0, 0, 0, 3] += 0.01
+    res = bench.prefill_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv), torch.from_numpy(bad),
+                                     hc.tables.block_tables, ctx, C, 2, sh.scale, 0, 0.05)
+    assert res["parity_max_abs"] >= 0.009
