@@ -630,7 +630,8 @@ def stored_traffic(workload, kernel, kernel_file="paged_attn_balanced"):
     return per[kernel], None
 
 
-def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True, prefix_kernel=True):
+def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True, prefix_kernel=True,
+                 cpu_seconds=0.0):
     """The verification pass of speculative decoding on the decode bench's
     state: per layer, pkv_kv_write of the q_len new tokens of every sequence
     (at positions ctx - q_len .. ctx - 1) and the verification attention;
@@ -745,7 +746,10 @@ def verify_bench(pkv, torch, S, q_len, steps, warmup, graph=True, prefix_kernel=
     extra = B * (q_len - 1) * sh.n_q * sh.d * (2 + 4)
     alg = attn_alg_bytes(S, S.ctx) + extra              # logical: the prefix once per reader
     alg_u = alg - kv_layer + unique_kv_bytes(S, S.ctx)  # the bytes HBM must deliver
-    return {"ms_per_step": ms, "step_mode": mode, "eager_ms_per_step": eager_ms,
+    cpu = rows_cpu_baseline(torch, S.k_pool[L - 1], S.v_pool[L - 1], q[L - 1], out[L - 1],
+                            S.bt.cpu().numpy(), S.ctx, q_len, sh.n_kv, sh.scale, 0,
+                            cpu_seconds) if cpu_seconds > 0 else None
+    return {"cpu_baseline": cpu, "ms_per_step": ms, "step_mode": mode, "eager_ms_per_step": eager_ms,
             "kv_gbs": kv_layer * L / (ms * 1e-3) / 1e9,
             "kv_gbs_unique": unique_kv_bytes(S, S.ctx) * L / (ms * 1e-3) / 1e9,
             "write_us": write_us,
@@ -840,7 +844,7 @@ def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=Tr
     traffic, why = (stored_traffic(f"llama3-8b-prefill{chunk}x{batch}", "paged_prefill",
                                    kernel_file="paged_prefill")
                     if shape.name == w.CONFIGS[4].name and seed == 0 else (None, "other workload"))
-    cpu = prefill_cpu_baseline(torch, kp[L - 1], vp[L - 1], q[L - 1], out[L - 1], t.block_tables, ctx,
+    cpu = rows_cpu_baseline(torch, kp[L - 1], vp[L - 1], q[L - 1], out[L - 1], t.block_tables, ctx,
                                chunk, n_kv, shape.scale, seed, cpu_seconds) if cpu_seconds > 0 else None
     return {
         "metric": "chunked prefill against the paged cache: TFLOP/s of the attention",
@@ -861,14 +865,15 @@ def prefill_bench(pkv, torch, shape, seed, chunk, batch, steps, warmup, graph=Tr
     }
 
 
-def prefill_cpu_baseline(torch, kp, vp, q, out, tables, ctx, chunk, n_kv, scale, seed, budget_s):
-    """The oracle beside the prefill, on a bounded sample of the last
-    layer's final state: rows (sequence, chunk token, query head) drawn at
-    random, the first and last chunk token of every sequence first, each
-    recomputed by the single-threaded C oracle in float64 (the row's
-    attention over positions 0 .. ctx - chunk + token) until budget_s
-    seconds; its rate in the prefill's own flop count, and the largest
-    difference from the GPU's rows."""
+def rows_cpu_baseline(torch, kp, vp, q, out, tables, ctx, chunk, n_kv, scale, seed, budget_s):
+    """The oracle beside a multi-token pass (a prefill chunk, or the
+    verification pass's query tokens: `chunk` tokens per sequence, the last
+    of its context), on a bounded sample of the last layer's final state:
+    rows (sequence, token, query head) drawn at random, the first and last
+    token of every sequence first, each recomputed by the single-threaded
+    C oracle in float64 (the row's attention over positions 0 .. ctx -
+    chunk + token) until budget_s seconds; its rate in the pass's own flop
+    count, and the largest difference from the GPU's rows."""
     import oracle
     orc = oracle.default()
     k_h = kp.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -893,7 +898,7 @@ def prefill_cpu_baseline(torch, kp, vp, q, out, tables, ctx, chunk, n_kv, scale,
         flops += 4.0 * d * seen
         rows += 1
     return {"value": flops / spent / 1e9, "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} (sequence, chunk token, query head) rows of the last layer, "
+            "sample": f"{rows} (sequence, token, query head) rows of the last layer, "
                       f"{spent:.1f} s of single-threaded C oracle time in float64",
             "parity_max_abs": err, "parity_rows": rows}
 
@@ -1189,7 +1194,14 @@ def main():
         dec = run(pkv, torch, S, args.steps, args.warmup, graph=not args.no_graph)
         log(f"[bench] decode on the same state: {dec['ms_per_step']:.3f} ms/step")
         vr = verify_bench(pkv, torch, S, args.verify_tokens, args.steps, args.warmup,
-                          graph=not args.no_graph, prefix_kernel=args.verify_prefix_kernel)
+                          graph=not args.no_graph, prefix_kernel=args.verify_prefix_kernel,
+                          cpu_seconds=min(args.cpu_seconds, 10.0))
+        if vr["cpu_baseline"] is not None:
+            cb = vr["cpu_baseline"]
+            log(f"[bench] oracle {cb['value']:.2f} GFLOP/s on 1 thread, parity max-abs "
+                f"{cb['parity_max_abs']:.2e} over {cb['parity_rows']} rows")
+            if not cb["parity_max_abs"] <= 1e-3:
+                raise RuntimeError(f"verification parity {cb['parity_max_abs']:.3e} > 1e-3")
         log(f"[bench] verify: {vr['ms_per_step']:.3f} ms/step, write {vr['write_us']:.1f} us, "
             f"verify {vr['verify_us']:.1f} us per layer")
         vtraffic, vwhy = (stored_traffic(f"llama3-8b-verify{args.verify_tokens}", "paged_attn_verify",
@@ -1212,7 +1224,7 @@ def main():
             "query_tokens_per_s": vr["query_tokens_per_s"],
             "kernels_us": {"kv_write": vr["write_us"], "paged_attn_verify": vr["verify_us"],
                            "spec_accept": vr["accept_us"]},
-            "vocab": VOCAB,
+            "vocab": VOCAB, "cpu_baseline": vr["cpu_baseline"],
             "roofline": {"kernel": "paged_attn_verify", "bound": "hbm", "achieved": vr["verify_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": vr["verify_gbs"] / HBM_PEAK_GBS, "traffic": vtraffic,

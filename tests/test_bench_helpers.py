@@ -136,7 +136,7 @@ def test_prefill_cpu_baseline_checks_rows_against_the_oracle():
                                        sh.scale)
     assert rc == 0
     tt = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
-    res = bench.prefill_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv),
+    res = bench.rows_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv),
                                      torch.from_numpy(want.astype(np.float32)),
                                      hc.tables.block_tables, ctx, C, 2, sh.scale, 0, 0.05)
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
@@ -144,6 +144,6 @@ def test_prefill_cpu_baseline_checks_rows_against_the_oracle():
     # a planted error in one row is found when that row is sampled
     bad = want.astype(np.float32).copy()
     bad[0, 0, 0, 3] += 0.01
-    res = bench.prefill_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv), torch.from_numpy(bad),
+    res = bench.rows_cpu_baseline(torch, tt(hc.k_pool), tt(hc.v_pool), tt(qv), torch.from_numpy(bad),
                                      hc.tables.block_tables, ctx, C, 2, sh.scale, 0, 0.05)
     assert res["parity_max_abs"] >= 0.009
