@@ -498,7 +498,11 @@ int pkv_paged_attn_verify_prefix(float* out, const void* q, const void* k_pool,
  * pkv_paged_attn_verify with q_len = chunk_len, organised for long chunks:
  * a workgroup of 8 wavefronts per (sequence, KV head, 256 query rows)
  * stages 64-token K/V tiles in LDS for all its rows; scores and values on
- * MFMA; no workspace.
+ * 32x32x16 MFMAs; no workspace. The workgroups take the (sequence, KV head)
+ * pairs longest context first (the ranking reads context_lens on the
+ * device, so a captured launch follows the lengths at each replay). For
+ * chunks of a few tokens, whose rows fill a small part of a workgroup,
+ * pkv_paged_attn_verify is the faster call.
  *   q:   device bf16 [num_seqs][chunk_len][n_q_heads][head_dim]
  *   out: device fp32 [num_seqs][chunk_len][n_q_heads][head_dim]
  * chunk_len in [1, 16384]. Other arguments as for pkv_paged_attn_decode.
