@@ -1509,12 +1509,22 @@ void paged_prefill_lds_kernel(DecodeArgs a) {
   // every XCD gets a like share of short and long sequences, and starts its
   // longest pairs first. Ranking more sequences than the workgroup has
   // threads falls back to index order.
-  const int xcd = blockIdx.x % kXcds;
-  const int k_in_xcd = blockIdx.x / kXcds;
-  const int deal = k_in_xcd / n_rt;
-  const int pair = deal * kXcds + ((deal & 1) ? kXcds - 1 - xcd : xcd);
-  if (pair >= a.num_seqs * a.n_kv) return;
-  const int rt = k_in_xcd % n_rt;
+  const int n_pairs = a.num_seqs * a.n_kv;
+  int pair, rt;
+  if (n_pairs >= kXcds) {
+    const int xcd = blockIdx.x % kXcds;
+    const int k_in_xcd = blockIdx.x / kXcds;
+    const int deal = k_in_xcd / n_rt;
+    pair = deal * kXcds + ((deal & 1) ? kXcds - 1 - xcd : xcd);
+    rt = k_in_xcd % n_rt;
+  } else {
+    // fewer pairs than XCDs: a pair's row tiles go round the XCDs (each
+    // XCD then reads the pair's K/V into its own L2), so that every XCD
+    // has work
+    pair = blockIdx.x / n_rt;
+    rt = blockIdx.x % n_rt;
+  }
+  if (pair >= n_pairs) return;
   const int h = pair % a.n_kv;
   const int rank = pair / a.n_kv;
   int s = rank;
@@ -2624,9 +2634,11 @@ extern "C" int pkv_paged_prefill(float* out, const void* q, const void* k_pool, 
   // one workgroup per (sequence, KV head, kPfRows rows); the (sequence, KV
   // head) pairs are dealt to the XCDs, kXcds at a time, each with all its
   // row tiles (the kernel's mapping), so the grid is rounded up to whole deals
+  // (fewer pairs than XCDs: one workgroup per row tile, in order)
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
   const int64_t deals = (pairs + kXcds - 1) / kXcds;
-  const int64_t grid64 = deals * kXcds * ((a.qrows + kPfRows - 1) / kPfRows);
+  const int64_t n_rt = (a.qrows + kPfRows - 1) / kPfRows;
+  const int64_t grid64 = pairs >= kXcds ? deals * kXcds * n_rt : pairs * n_rt;
   if (grid64 > INT32_MAX) return PKV_EINVAL;
   const unsigned grid = (unsigned)grid64;
   if (d == 128)

@@ -173,6 +173,9 @@ ORDER_CASES = [  # n_q, n_kv, d, contexts, chunk
     # a count that is not a multiple of 4 (the ranking reads its keys four
     # at a time), many ties
     (4, 2, 64, [int(5 + (i * 53) % 40) for i in range(301)], 2),
+    # one (sequence, KV head) pair, fewer than the XCDs: its five row tiles
+    # go round the XCDs
+    (8, 1, 128, [700], 160),
 ]
 
 
