@@ -176,6 +176,8 @@ ORDER_CASES = [  # n_q, n_kv, d, contexts, chunk
     # one (sequence, KV head) pair, fewer than the XCDs: its five row tiles
     # go round the XCDs
     (8, 1, 128, [700], 160),
+    # 15 pairs, not a whole number of deals: row tiles round the XCDs
+    (12, 3, 64, [130, 70, 400, 255, 90], 40),
 ]
 
 
